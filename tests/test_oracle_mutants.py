@@ -1,0 +1,107 @@
+"""Planted mistakes in the oracle must be caught by its pins.
+
+Each mutant is a copy of ``oracle/kkt_oracle.c`` with one plausible mistake
+(a dropped term, a wrong sign or index, a transposed operand, the sequence
+boundary bug the pages describe), compiled into a temporary library.  The
+test runs every pin on it and requires at least one to fail.  CPU only; the
+real oracle source is never modified.
+"""
+import ctypes
+import os
+import subprocess
+import tempfile
+
+import numpy as np
+import pytest
+
+from tests import oracle_pins
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "kkt_oracle.c")
+
+# (name, text in the source, replacement)
+MUTANTS = [
+    ("gate_sign", "double d = g[ti] - g[tj];", "double d = g[tj] - g[ti];"),
+    ("beta_on_column", "(beta != NULL) ? beta[ti] : 1.0", "(beta != NULL) ? beta[tj] : 1.0"),
+    ("dot_drops_first_term", "for (int64_t c = 0; c < K; ++c) {\n                dot",
+     "for (int64_t c = 1; c < K; ++c) {\n                dot"),
+    ("diagonal_in_A", "for (int64_t j = 0; j < i; ++j) {\n            const int64_t tj",
+     "for (int64_t j = 0; j <= i; ++j) {\n            const int64_t tj"),
+    ("minus_A", "((i == j) ? 1.0 : 0.0) + A[i * L + j]", "((i == j) ? 1.0 : 0.0) - A[i * L + j]"),
+    ("transposed_output", "row[j] = (j < L) ? X[i * L + j] : 0.0;", "row[j] = (j < L) ? X[j * L + i] : 0.0;"),
+    ("elimination_sign", "W[r * w + x] -= f * W[c * w + x];", "W[r * w + x] += f * W[c * w + x];"),
+    ("clamp_bound_5", "static const double GATE_CLAMP = 50.0;", "static const double GATE_CLAMP = 5.0;"),
+    ("no_clamp", "if (clamp_gate) {\n                    if (d > GATE_CLAMP)",
+     "if (0) {\n                    if (d > GATE_CLAMP)"),
+    ("gate_of_wrong_token", "double d = g[ti] - g[tj];", "double d = g[ti] - g[tj + (j > 0 ? -H : 0)];"),
+    # chunk length taken from the full T instead of the sequence end
+    ("sequence_end_uses_T", "chunk_len[n] = (eos - t0 < chunk_size) ? (eos - t0) : chunk_size;",
+     "chunk_len[n] = (T - t0 < chunk_size) ? (T - t0) : chunk_size;"),
+    # chunk starts snapped to the global 64-token grid instead of the sequence start
+    ("chunks_ignore_sequence_start", "chunk_t0[n] = t0;", "chunk_t0[n] = t0 - bos % chunk_size;"),
+    ("key_of_previous_token", "const double* kj = k + tj * K;", "const double* kj = k + (tj >= H ? tj - H : tj) * K;"),
+]
+
+
+def _build(src_text, tmpdir, name):
+    c = os.path.join(tmpdir, name + ".c")
+    so = os.path.join(tmpdir, name + ".so")
+    with open(c, "w") as f:
+        f.write(src_text)
+    subprocess.run(["gcc", "-std=c11", "-O2", "-fopenmp", "-fPIC", "-shared", "-w", "-o", so, c, "-lm"],
+                   check=True, capture_output=True)
+    lib = ctypes.CDLL(so)
+    dp = ctypes.POINTER(ctypes.c_double)
+    ip = ctypes.POINTER(ctypes.c_int32)
+    lib.kkt_oracle_solve.argtypes = [dp, dp, dp, ip, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                     ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, dp]
+    lib.kkt_oracle_solve.restype = ctypes.c_int
+    return lib
+
+
+def _solver(lib):
+    def ptr(a, t):
+        return None if a is None else a.ctypes.data_as(ctypes.POINTER(t))
+
+    def solve(k, g=None, beta=None, cu=None, chunk_size=64, clamp_gate=True):
+        k = np.ascontiguousarray(k, dtype=np.float64)
+        B, T, H, K = k.shape
+        g = None if g is None else np.ascontiguousarray(g, dtype=np.float64)
+        beta = None if beta is None else np.ascontiguousarray(beta, dtype=np.float64)
+        cu = None if cu is None else np.ascontiguousarray(cu, dtype=np.int32)
+        out = np.empty((B, T, H, chunk_size))
+        rc = lib.kkt_oracle_solve(ptr(k, ctypes.c_double), ptr(g, ctypes.c_double), ptr(beta, ctypes.c_double),
+                                  ptr(cu, ctypes.c_int32), 0 if cu is None else len(cu) - 1,
+                                  B, T, H, K, chunk_size, int(clamp_gate), ptr(out, ctypes.c_double))
+        if rc != 0:
+            raise ValueError(rc)
+        return out
+    return solve
+
+
+@pytest.fixture(scope="module")
+def tmpdir():
+    with tempfile.TemporaryDirectory() as d:
+        yield d
+
+
+def test_unmutated_copy_passes(tmpdir):
+    with open(SRC) as f:
+        solve = _solver(_build(f.read(), tmpdir, "clean"))
+    for pin in oracle_pins.ALL_PINS:
+        pin(solve)
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmpdir, name, old, new):
+    with open(SRC) as f:
+        text = f.read()
+    assert text.count(old) == 1, f"mutation site for {name} not found exactly once"
+    solve = _solver(_build(text.replace(old, new), tmpdir, name))
+    caught = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(solve)
+        except (AssertionError, ValueError, IndexError, FloatingPointError):
+            caught.append(pin.__name__)
+    assert caught, f"mutant {name} passed every pin"
