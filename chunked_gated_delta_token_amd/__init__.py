@@ -1,0 +1,11 @@
+"""Fused chunk-local KKT + triangular solve of the chunked Gated DeltaNet
+forward pass, for AMD Instinct MI355X (gfx950).
+
+    from chunked_gated_delta_token_amd import kkt_solve
+    X = kkt_solve(k, g, beta)          # [B, T, H, 64] rows of (I + A)^{-1}
+
+The computation is the HIP library ``libkkt_solve.so`` (C ABI in
+``include/kkt_solve.h``); this package only marshals arguments.
+"""
+from .kkt import (KKTError, chunk_gated_delta_rule_fwd_kkt_solve, kkt_solve, last_error,  # noqa: F401
+                  load_library, version)

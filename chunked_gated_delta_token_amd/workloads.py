@@ -72,12 +72,40 @@ BENCH_WORKLOAD = "T8192_H8_bf16_f32"
 def f64_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round fp64 to bfloat16 (round-to-nearest-even, straight from fp64) and
     return uint16 bit patterns.  Used to cast generated keys."""
-    x = np.asarray(x, dtype=np.float64)
-    m, e = np.frexp(x)                    # x = m * 2^e, 0.5 <= |m| < 1
-    # bf16 keeps 8 significant bits: quantum 2^(e-8), never below 2^-133
-    q_exp = np.maximum(e - 8, -133)
-    r = np.ldexp(np.rint(np.ldexp(x, -q_exp)), q_exp)
-    return (r.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    flat = x.reshape(-1)
+    out = np.empty(flat.shape, dtype=np.uint16)
+    step = 1 << 22
+    for a in range(0, flat.size, step):
+        out[a:a + step] = _f64_to_bf16_bits_block(flat[a:a + step])
+    return out.reshape(x.shape)
+
+
+def _f64_to_bf16_bits_block(x: np.ndarray) -> np.ndarray:
+    """
+
+    Fast path on the fp64 bit pattern: drop the low 45 of the 52 mantissa
+    bits with round-half-even (a carry may bump the exponent), then re-bias
+    the exponent.  Results outside bf16's normal range take a slow exact path.
+    """
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    u = x.view(np.uint64)
+    sign = (u >> np.uint64(63)).astype(np.uint16) << np.uint16(15)
+    mag = u & np.uint64(0x7FFFFFFFFFFFFFFF)
+    lsb = (mag >> np.uint64(45)) & np.uint64(1)
+    r = (mag + np.uint64((1 << 44) - 1) + lsb) >> np.uint64(45)       # 11-bit exponent | 7-bit mantissa
+    e = (r >> np.uint64(7)).astype(np.int64) - 1023 + 127
+    out = sign | (np.clip(e, 0, 255).astype(np.uint16) << np.uint16(7)) | (r & np.uint64(0x7F)).astype(np.uint16)
+    out = np.where(mag == 0, sign, out)
+    slow = (mag != 0) & ((e < 1) | (e > 254))
+    if np.any(slow):
+        xs = x[slow]
+        m_, e_ = np.frexp(xs)                  # xs = m_ * 2^e_, 0.5 <= |m_| < 1
+        q = np.maximum(e_ - 8, -133)           # bf16 keeps 8 significant bits, quantum >= 2^-133
+        rs = np.ldexp(np.rint(np.ldexp(xs, -q)), q)
+        with np.errstate(over="ignore"):
+            out[slow] = (rs.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    return out
 
 
 def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:

@@ -1,0 +1,107 @@
+/*
+ * kkt_solve.h: C ABI of the fused chunk-local KKT + triangular solve for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Operation (MindSpeed-Ops pull request #135, "feat(triton): add
+ * chunk_gated_delta_rule_fwd_kkt_solve"; PR description, user-facing-change
+ * section and bot change summary):
+ *
+ *   One call does what the two-step path solve_tril(chunk_scaled_dot_kkt_fwd)
+ *   does.  The tokens of every (batch row or sequence, head) are cut into
+ *   chunks of 64, restarting at every sequence start; the last chunk of a
+ *   sequence may be shorter (L < 64).  For a chunk starting at token t0 with
+ *   local rows i, j in [0, L):
+ *
+ *     A[i][j] = beta_i * (k_i . k_j) * exp(clamp(g_i - g_j, -50, 50))  for i > j
+ *     A[i][j] = 0                                                        otherwise
+ *
+ *     out[b][t0 + i][h][j] = ((I + A)^{-1})[i][j]   for j < L
+ *     out[b][t0 + i][h][j] = 0                      for L <= j < 64
+ *
+ *   so every output row holds its chunk's row of the unit lower-triangular
+ *   inverse: 1.0 on the diagonal, +0.0 above it, written in full by the call
+ *   (no pre-zeroed output is needed).
+ *
+ * Threading: every entry point is thread-safe; the library keeps no state
+ * besides a per-thread error string and a per-device architecture cache.
+ */
+#ifndef KKT_SOLVE_H
+#define KKT_SOLVE_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types.  fp32 is IEEE binary32, bf16 is bfloat16, f16 is IEEE binary16. */
+typedef enum {
+    KKT_DTYPE_F32 = 0,
+    KKT_DTYPE_BF16 = 1,
+    KKT_DTYPE_F16 = 2
+} kkt_dtype_t;
+
+typedef enum {
+    KKT_OK = 0,
+    KKT_ERR_INVALID_ARGUMENT = 1, /* a pointer, size or dtype is invalid; nothing was launched */
+    KKT_ERR_UNSUPPORTED = 2,      /* valid request this build does not serve (chunk_size, K, device) */
+    KKT_ERR_HIP = 3               /* the HIP runtime reported an error while querying or launching */
+} kkt_status_t;
+
+/*
+ * kkt_solve: the fused op (PR #135 page: the fused API takes k, g, beta,
+ * cu_seqlens, chunk_size and an output dtype and returns (I+A)^{-1} of shape
+ * [B,T,H,64]; only chunk_size 64 is served, other values are an error).
+ *
+ *   k          device, [B,T,H,K] of in_dtype, contiguous (H*K elements per token).
+ *   g          device, [B,T,H] fp32 chunk-local cumulative log-decay, or NULL
+ *              (no gate: every exp factor is 1).  The caller provides g already
+ *              summed within each chunk; only differences g_i - g_j inside a
+ *              chunk are used.
+ *   beta       device, [B,T,H] fp32 row scale, or NULL (beta = 1).
+ *   cu_seqlens device, int32 [num_seqs + 1] start offsets of packed sequences,
+ *              or NULL for fixed-length rows.  With cu_seqlens, B must be 1;
+ *              offsets are expected to start at 0, not decrease and end at T.
+ *              The kernel clamps every offset into [0, T], so malformed
+ *              offsets cannot make it access memory outside the tensors; rows
+ *              not covered by any sequence are then left unwritten.  With the
+ *              environment variable KKT_VALIDATE=1 the offsets are copied to the
+ *              host (synchronously) and checked first.
+ *   num_seqs   number of sequences; ignored when cu_seqlens is NULL.
+ *   B, T, H, K sizes.  T may be 0 (nothing is launched).
+ *              K must be 64, 128 or 256.
+ *   chunk_size must be 64.
+ *   in_dtype   element type of k.
+ *   out_dtype  element type of out.  bf16 / f16 results are rounded to nearest
+ *              even from the fp32 value.
+ *   out        device, [B,T,H,64] of out_dtype, contiguous; every element is
+ *              written (for varlen: every element of the rows covered by the
+ *              sequences).  Must not overlap any input.
+ *   stream     HIP stream the kernel is enqueued on (NULL: the null stream).
+ *
+ * All pointers are owned by the caller; the library allocates nothing and
+ * keeps no pointer after the call returns.  The call is asynchronous: it
+ * returns once the kernel is enqueued, and faults during execution surface at
+ * the caller's next synchronisation.  Argument errors are detected before
+ * any HIP call, return KKT_ERR_INVALID_ARGUMENT / KKT_ERR_UNSUPPORTED and
+ * launch nothing; kkt_last_error() then describes the problem.
+ */
+kkt_status_t kkt_solve(const void* k, const float* g, const float* beta,
+                       const int32_t* cu_seqlens, int64_t num_seqs,
+                       int64_t B, int64_t T, int64_t H, int64_t K,
+                       int64_t chunk_size, kkt_dtype_t in_dtype, kkt_dtype_t out_dtype,
+                       void* out, hipStream_t stream);
+
+/* Text of the last non-OK status returned on the calling thread ("" if none).
+ * The pointer stays valid until the next kkt_* call on the same thread. */
+const char* kkt_last_error(void);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int kkt_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KKT_SOLVE_H */

@@ -1,0 +1,86 @@
+"""Comparison of a GPU result with the fp64 oracle (test infrastructure).
+
+Acceptance criteria, element by element over the whole [B,T,H,64] output:
+  * structure, bit-exact: no NaN anywhere (outputs are pre-filled with NaN, so
+    this also proves every element was written); 1.0 on each row's diagonal;
+    +0.0 (bit pattern 0) above the diagonal and in columns >= L;
+  * fp32 output: max |gpu - ref| <= 2e-4 over all elements, and the mean
+    relative error sum|gpu - ref| / sum|ref| over the strictly lower elements
+    <= 1e-5;
+  * bf16 / f16 output: each element within one unit in the last place of the
+    format, measured as the distance in representable values between the GPU
+    bits and the oracle's exact value rounded to nearest even, or
+    |gpu - ref| <= 2^-23 (fp32 rounding of values near zero, where one bf16
+    step is smaller than the fp32 arithmetic error).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+from chunked_gated_delta_token_amd import workloads
+
+MAX_ABS_F32 = 2e-4
+MRE_F32 = 1e-5
+FLOOR_16 = 2.0 ** -23
+ONE_BITS = {"bf16": 0x3F80, "f16": 0x3C00}
+
+
+def ordinal16(bits: np.ndarray) -> np.ndarray:
+    """Map 16-bit float patterns to integers ordered like their values (+0 and -0 -> 0)."""
+    b = bits.astype(np.int64)
+    mag = b & 0x7FFF
+    return np.where(b & 0x8000, -mag, mag)
+
+
+def decode(got: np.ndarray, out_dtype: str) -> np.ndarray:
+    if out_dtype == "f32":
+        return got.astype(np.float64)
+    if out_dtype == "bf16":
+        return workloads.bf16_bits_to_f64(got)
+    return got.view(np.float16).astype(np.float64)
+
+
+def structural_masks(T: int, cu_seqlens=None):
+    """[T, 64] masks: diagonal, strictly upper (incl. columns >= L), strictly lower."""
+    local, _length = workloads.chunk_geometry(T, cu_seqlens)
+    j = np.arange(64)[None, :]
+    i = local[:, None]
+    return (j == i), (j > i), (j < i)
+
+
+def compare(got: np.ndarray, ref: np.ndarray, out_dtype: str, cu_seqlens=None, label: str = "") -> dict:
+    """Assert the criteria above; return the measured figures."""
+    B, T, H, C = ref.shape
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    diag, upper, lower = (m[None, :, None, :] for m in structural_masks(T, cu_seqlens))
+    diag = np.broadcast_to(diag, ref.shape)
+    upper = np.broadcast_to(upper, ref.shape)
+    lower = np.broadcast_to(lower, ref.shape)
+    val = decode(got, out_dtype)
+    stats = {"label": label, "elements": int(ref.size)}
+    assert not np.any(np.isnan(val)), f"{label}: NaN in output (unwritten elements?)"
+    if out_dtype == "f32":
+        bits = got.view(np.uint32)
+        assert np.all(val[diag] == 1.0), f"{label}: diagonal is not exactly 1.0"
+        assert np.all(bits[upper] == 0), f"{label}: upper triangle is not +0.0"
+        err = np.abs(val - ref)
+        max_abs = float(err.max())
+        mre = float(err[lower].sum() / max(np.abs(ref[lower]).sum(), 1e-300))
+        stats.update(max_abs=max_abs, mre=mre)
+        assert max_abs <= MAX_ABS_F32, f"{label}: max abs error {max_abs:.3e} > {MAX_ABS_F32}"
+        assert mre <= MRE_F32, f"{label}: mean relative error {mre:.3e} > {MRE_F32}"
+    else:
+        assert np.all(got[diag] == ONE_BITS[out_dtype]), f"{label}: diagonal is not exactly 1.0"
+        assert np.all(got[upper] == 0), f"{label}: upper triangle is not +0.0"
+        exp_bits = oracle.round_to_bf16_bits(ref) if out_dtype == "bf16" else oracle.round_to_f16_bits(ref)
+        dist = np.abs(ordinal16(got) - ordinal16(exp_bits))
+        err = np.abs(val - ref)
+        ok_ulp = dist <= 1
+        ok_floor = err <= FLOOR_16
+        bad = ~(ok_ulp | ok_floor)
+        stats.update(max_ulp=int(dist.max()), n_floor=int(np.sum(~ok_ulp & ok_floor)),
+                     max_abs=float(err.max()), exact_frac=float(np.mean(dist == 0)))
+        assert not np.any(bad), (f"{label}: {int(bad.sum())} elements beyond 1 ulp "
+                                 f"(max {int(dist.max())} ulp, first at {np.argwhere(bad)[0].tolist()})")
+    return stats

@@ -1,0 +1,111 @@
+"""The C-ABI library on the CPU: it loads, exports every function the header
+declares, and rejects invalid arguments before making any HIP call (so these
+tests run without a GPU; nothing here launches a kernel)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kkt_solve.h")
+LIB = os.path.join(ROOT, "chunked_gated_delta_token_amd", "libkkt_solve.so")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        from chunked_gated_delta_token_amd import build
+        build.build()
+    from chunked_gated_delta_token_amd import kkt
+    return kkt.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(kkt_[a-z_]+)\s*\(",
+                                 text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == ["kkt_last_error", "kkt_solve", "kkt_version"]
+
+
+def test_every_declared_symbol_is_exported(lib):
+    from chunked_gated_delta_token_amd import kkt
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert name in kkt.SIGNATURES, name
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\s[TW]\s(kkt_\w+)$", out, flags=re.M))
+    assert exported == set(declared_functions()), exported
+
+
+def test_version(lib):
+    assert lib.kkt_version() == 100
+
+
+def _call(lib, **over):
+    args = dict(k=1, g=None, beta=None, cu=None, num_seqs=0, B=1, T=64, H=1, K=128, chunk_size=64,
+                in_dtype=1, out_dtype=0, out=1, stream=None)
+    args.update(over)
+    return lib.kkt_solve(args["k"], args["g"], args["beta"], args["cu"], args["num_seqs"], args["B"],
+                         args["T"], args["H"], args["K"], args["chunk_size"], args["in_dtype"],
+                         args["out_dtype"], args["out"], args["stream"])
+
+
+@pytest.mark.parametrize("over,status,msg", [
+    (dict(chunk_size=32), 2, "chunk_size"),
+    (dict(chunk_size=128), 2, "chunk_size"),
+    (dict(in_dtype=3), 1, "dtype"),
+    (dict(out_dtype=-1), 1, "dtype"),
+    (dict(B=0), 1, ">= 1"),
+    (dict(H=0), 1, ">= 1"),
+    (dict(T=-1), 1, ">= 1"),
+    (dict(K=100), 2, "K must be"),
+    (dict(K=512), 2, "K must be"),
+    (dict(cu=1, num_seqs=2, B=2), 1, "cu_seqlens"),
+    (dict(cu=1, num_seqs=0), 1, "cu_seqlens"),
+    (dict(k=None), 1, "NULL"),
+    (dict(out=None), 1, "NULL"),
+])
+def test_invalid_arguments_rejected_on_host(lib, over, status, msg):
+    from chunked_gated_delta_token_amd import kkt
+    assert _call(lib, **over) == status
+    assert msg in kkt.last_error()
+
+
+def test_empty_sequence_is_a_no_op(lib):
+    from chunked_gated_delta_token_amd import kkt
+    assert _call(lib, T=0, k=None, out=None) == 0
+    assert kkt.last_error() == ""
+
+
+def test_python_binding_rejects_chunk_size():
+    import torch
+    from chunked_gated_delta_token_amd import kkt
+    with pytest.raises(ValueError):
+        kkt.kkt_solve(torch.zeros(1, 4, 1, 128), chunk_size=32)
+
+
+def test_header_compiles_as_c_and_links(tmp_path, lib):
+    """A plain C program includes the header, links the library and makes a
+    host-only call (argument rejection)."""
+    src = tmp_path / "t.c"
+    src.write_text('#include "kkt_solve.h"\n#include <stdio.h>\n'
+                   'int main(void){ kkt_status_t s = kkt_solve(0,0,0,0,0,1,64,1,128,32,KKT_DTYPE_BF16,'
+                   'KKT_DTYPE_F32,0,0); printf("%d %d %s\\n", (int)s, kkt_version(), kkt_last_error());'
+                   ' return s == KKT_ERR_UNSUPPORTED ? 0 : 1; }\n')
+    exe = tmp_path / "t"
+    libdir = os.path.dirname(LIB)
+    subprocess.run(["gcc", "-std=c11", "-Wall", "-Werror", "-D__HIP_PLATFORM_AMD__", f"-I{ROOT}/include",
+                    f"-I{ROCM}/include", str(src), "-o", str(exe), f"-L{libdir}", "-lkkt_solve",
+                    f"-Wl,-rpath,{libdir}"], check=True, capture_output=True)
+    res = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert res.returncode == 0, res.stdout + res.stderr
+    assert "chunk_size must be 64" in res.stdout

@@ -1,0 +1,310 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 oracle,
+element by element on the same seeded inputs.
+
+Every test needs a gfx950 GPU and the built library; none falls back to
+anything.  Each case prints what it runs (and flushes) before touching the
+GPU, so a log names the case if a run ends early.
+"""
+from __future__ import annotations
+
+import json
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from chunked_gated_delta_token_amd import workloads as W
+from tests._compare import compare
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def kkt():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from chunked_gated_delta_token_amd import kkt as mod
+    mod.load_library()  # raises if the library is not built: no fallback
+    name = torch.cuda.get_device_properties(0).gcnArchName
+    assert name.startswith("gfx950"), name
+    return mod
+
+
+def to_device(inp: W.Inputs, dev="cuda:0"):
+    dt = inp.workload.in_dtype
+    if dt == "f32":
+        k = torch.from_numpy(inp.k_store).to(dev)
+    else:
+        k = torch.from_numpy(inp.k_store.view(np.int16)).to(dev).view(TORCH_DT[dt])
+    g = None if inp.g is None else torch.from_numpy(inp.g).to(dev)
+    b = None if inp.beta is None else torch.from_numpy(inp.beta).to(dev)
+    cu = None if inp.cu_seqlens is None else torch.from_numpy(inp.cu_seqlens).to(dev)
+    return k, g, b, cu
+
+
+def from_device(out: torch.Tensor, out_dtype: str) -> np.ndarray:
+    if out_dtype == "f32":
+        return out.cpu().numpy()
+    return out.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def run_gpu(kkt, inp: W.Inputs, out_dtype: str, stream=None, tensors=None) -> np.ndarray:
+    k, g, b, cu = tensors if tensors is not None else to_device(inp)
+    B, T, H, _ = k.shape
+    out = torch.full((B, T, H, 64), float("nan"), dtype=TORCH_DT[out_dtype], device=k.device)
+    kkt.kkt_solve(k, g, b, cu, output_dtype=TORCH_DT[out_dtype], out=out, stream=stream)
+    torch.cuda.synchronize()
+    return from_device(out, out_dtype)
+
+
+def reference(inp: W.Inputs) -> np.ndarray:
+    return oracle.kkt_solve_ref(inp.k64(), inp.g, inp.beta, inp.cu_seqlens)
+
+
+def check(kkt, inp: W.Inputs, out_dtype: str, label: str) -> dict:
+    w = inp.workload
+    say(f"[case] {label}: B={w.B} T={w.T} H={w.H} K={w.K} in={w.in_dtype} out={out_dtype} "
+        f"g={inp.g is not None} beta={inp.beta is not None} "
+        f"seqs={0 if inp.cu_seqlens is None else len(inp.cu_seqlens) - 1}")
+    got = run_gpu(kkt, inp, out_dtype)
+    stats = compare(got, reference(inp), out_dtype, inp.cu_seqlens, label)
+    say("[ok] " + json.dumps(stats))
+    return stats
+
+
+# ---------------------------------------------------------------- full workloads
+@pytest.mark.parametrize("name", list(W.WORKLOADS))
+def test_workload_full_parity(kkt, name):
+    """Each workload at its full size, every output element compared."""
+    inp = W.generate(name)
+    check(kkt, inp, inp.workload.out_dtype, name)
+
+
+# ---------------------------------------------------------------- dtype matrix
+@pytest.mark.parametrize("in_dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16", "f16"])
+def test_dtype_matrix(kkt, in_dtype, out_dtype):
+    inp = W.generate("T256_H8_bf16_f32", B=2, T=200, H=3, in_dtype=in_dtype, seed=101)
+    check(kkt, inp, out_dtype, f"dtype {in_dtype}->{out_dtype}")
+
+
+# ---------------------------------------------------------------- shapes
+@pytest.mark.parametrize("T", [1, 2, 3, 15, 16, 17, 63, 64, 65, 127, 128, 2000])
+def test_lengths(kkt, T):
+    gate, beta = bool(T % 2), bool((T // 2) % 2)
+    inp = W.generate("T256_H8_bf16_f32", B=2, T=T, H=3, seed=200 + T, gate=gate, beta=beta)
+    check(kkt, inp, "f32", f"T={T}")
+
+
+@pytest.mark.parametrize("gate", [False, True])
+@pytest.mark.parametrize("beta", [False, True])
+def test_gate_beta_variants(kkt, gate, beta):
+    inp = W.generate("T256_H8_bf16_f32", T=300, H=5, seed=300, gate=gate, beta=beta)
+    check(kkt, inp, "f32", f"gate={gate} beta={beta}")
+    check(kkt, inp, "bf16", f"gate={gate} beta={beta} bf16 out")
+
+
+@pytest.mark.parametrize("K", [64, 256])
+@pytest.mark.parametrize("in_dtype", ["bf16", "f32"])
+def test_other_head_dims(kkt, K, in_dtype):
+    inp = W.generate("T256_H8_bf16_f32", T=130, H=2, K=K, in_dtype=in_dtype, seed=400 + K)
+    check(kkt, inp, "f32", f"K={K} {in_dtype}")
+
+
+def test_large_gate_spread(kkt):
+    """Within-chunk gate differences beyond +-50 take the clamp."""
+    inp = W.generate("T256_H8_bf16_f32", T=128, H=2, seed=450)
+    rng = np.random.default_rng(451)
+    inc = -rng.uniform(0.0, 3.0, inp.g.shape)
+    g = np.empty_like(inc)
+    for t0 in range(0, 128, 64):
+        g[:, t0:t0 + 64] = np.cumsum(inc[:, t0:t0 + 64], axis=1)
+    inp.g = g.astype(np.float32)
+    check(kkt, inp, "f32", "gate spread ~ -96")
+
+
+# ---------------------------------------------------------------- varlen
+VARLEN_CASES = {
+    "tiny_and_empty": [1, 2, 3, 0, 64, 65, 0, 130, 5],
+    "single": [777],
+    "all_empty_but_one": [0, 0, 40, 0],
+    "many_short": [1, 3] * 70,  # 140 sequences: more than one 64-wide scan pass
+}
+
+
+@pytest.mark.parametrize("case", list(VARLEN_CASES))
+def test_varlen(kkt, case):
+    lens = VARLEN_CASES[case]
+    inp = W.generate("T256_H8_bf16_f32", lengths=lens, H=3, seed=500)
+    check(kkt, inp, "f32", f"varlen {case}")
+    # the pages' split cross-check: the packed call equals one fixed-length
+    # call per sequence, bit for bit
+    packed = run_gpu(kkt, inp, "f32")
+    cu = inp.cu_seqlens
+    for s in range(len(lens)):
+        a, b = int(cu[s]), int(cu[s + 1])
+        if b == a:
+            continue
+        sub = W.Inputs(W.Workload(**{**inp.workload.__dict__, "T": b - a, "n_seqs": 0}),
+                       np.ascontiguousarray(inp.k_store[:, a:b]),
+                       None if inp.g is None else np.ascontiguousarray(inp.g[:, a:b]),
+                       None if inp.beta is None else np.ascontiguousarray(inp.beta[:, a:b]), None)
+        single = run_gpu(kkt, sub, "f32")
+        assert np.array_equal(single.view(np.uint32), packed[:, a:b].view(np.uint32)), f"sequence {s}"
+
+
+def test_varlen_validate_env_rejects_bad_offsets(kkt, monkeypatch):
+    """KKT_VALIDATE=1 copies cu_seqlens to the host and rejects malformed
+    offsets before launching anything."""
+    monkeypatch.setenv("KKT_VALIDATE", "1")
+    inp = W.generate("T256_H8_bf16_f32", lengths=[10, 20], H=2, seed=501)
+    k, g, b, _ = to_device(inp)
+    bad = torch.tensor([0, 25, 20], dtype=torch.int32, device=k.device)  # decreasing, ends != T
+    with pytest.raises(kkt.KKTError) as e:
+        kkt.kkt_solve(k, g, b, bad)
+    assert e.value.status == kkt.KKT_ERR_INVALID_ARGUMENT
+
+
+def test_varlen_offsets_are_clamped(kkt):
+    """Offsets beyond T are clamped in the kernel: rows inside [0, T) that a
+    sequence covers are still correct and nothing outside the tensors is
+    touched (the output's guard rows stay NaN)."""
+    inp = W.generate("T256_H8_bf16_f32", lengths=[50, 30], H=2, seed=502)
+    k, g, b, _ = to_device(inp)
+    cu = torch.tensor([0, 50, 1000], dtype=torch.int32, device=k.device)  # last end beyond T=80
+    guard = torch.full((1, 100, 2, 64), float("nan"), device=k.device)
+    out = guard[:, :80]
+    kkt.kkt_solve(k, g, b, cu, output_dtype=torch.float32, out=out)
+    torch.cuda.synchronize()
+    assert torch.isnan(guard[:, 80:]).all()
+    ref = reference(inp)
+    compare(out.cpu().numpy(), ref, "f32", inp.cu_seqlens, "clamped offsets")
+
+
+# ---------------------------------------------------------------- bit-exact pins
+def test_orthogonal_keys_give_identity(kkt):
+    T, H, K = 192, 2, 64
+    inp = W.generate("T256_H8_bf16_f32", T=T, H=H, K=K, seed=600)
+    k = np.zeros((1, T, H, K))
+    k[0, np.arange(T), :, np.arange(T) % 64] = 1.0
+    inp.k_store = W.f64_to_bf16_bits(k)
+    got = run_gpu(kkt, inp, "f32")
+    eye = np.tile(np.eye(64, dtype=np.float32), (T // 64, 1))
+    for h in range(H):
+        assert np.array_equal(got[0, :, h].view(np.uint32), eye.view(np.uint32))
+
+
+def test_beta_zero_gives_identity(kkt):
+    inp = W.generate("T256_H8_bf16_f32", T=150, H=3, seed=601)
+    inp.beta = np.zeros_like(inp.beta)
+    got = run_gpu(kkt, inp, "bf16")
+    local = np.arange(150) % 64
+    exp = np.zeros((150, 64), dtype=np.uint16)
+    exp[np.arange(150), local] = 0x3F80
+    for h in range(3):
+        assert np.array_equal(got[0, :, h], exp)
+
+
+def test_single_token(kkt):
+    inp = W.generate("T256_H8_bf16_f32", B=3, T=1, H=5, seed=602)
+    got = run_gpu(kkt, inp, "f32")
+    exp = np.zeros(64, dtype=np.float32)
+    exp[0] = 1.0
+    assert np.array_equal(got.reshape(-1, 64).view(np.uint32), np.tile(exp, (15, 1)).view(np.uint32))
+
+
+def test_neutral_gate_beta_equal_null(kkt):
+    inp = W.generate("T256_H8_bf16_f32", T=256, H=4, seed=603, gate=False, beta=False)
+    a = run_gpu(kkt, inp, "f32")
+    inp.g = np.zeros((1, 256, 4), dtype=np.float32)
+    inp.beta = np.ones((1, 256, 4), dtype=np.float32)
+    b = run_gpu(kkt, inp, "f32")
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_head_and_batch_permutation(kkt):
+    inp = W.generate("T256_H8_bf16_f32", B=2, T=200, H=4, seed=604)
+    base = run_gpu(kkt, inp, "f32")
+    p = np.array([3, 1, 0, 2])
+    perm = W.Inputs(inp.workload, np.ascontiguousarray(inp.k_store[::-1][:, :, p]),
+                    np.ascontiguousarray(inp.g[::-1][:, :, p]), np.ascontiguousarray(inp.beta[::-1][:, :, p]), None)
+    got = run_gpu(kkt, perm, "f32")
+    assert np.array_equal(got.view(np.uint32), base[::-1][:, :, p].view(np.uint32))
+
+
+def test_prefix_partial_chunk_bitexact(kkt):
+    """T=2000 against a T=2048 run sharing the first 2000 tokens: every row of
+    the shorter run is bit-identical (a partial chunk is the leading block)."""
+    full = W.generate("T256_H8_bf16_f32", T=2048, H=8, seed=605)
+    part = W.Inputs(W.Workload(**{**full.workload.__dict__, "T": 2000}),
+                    np.ascontiguousarray(full.k_store[:, :2000]), np.ascontiguousarray(full.g[:, :2000]),
+                    np.ascontiguousarray(full.beta[:, :2000]), None)
+    a = run_gpu(kkt, full, "f32")
+    b = run_gpu(kkt, part, "f32")
+    # columns >= 16 of the partial chunk are zero in the short run only
+    assert np.array_equal(b[:, :1984].view(np.uint32), a[:, :1984].view(np.uint32))
+    assert np.array_equal(b[:, 1984:, :, :16].view(np.uint32), a[:, 1984:2000, :, :16].view(np.uint32))
+    assert np.all(b[:, 1984:, :, 16:].view(np.uint32) == 0)
+
+
+def test_repeatable_and_stream(kkt):
+    inp = W.generate("T8192_H8_bf16_f32")
+    t = to_device(inp)
+    a = run_gpu(kkt, inp, "f32", tensors=t)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        b = run_gpu(kkt, inp, "f32", stream=s, tensors=t)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+# ---------------------------------------------------------------- golden file on the GPU
+def test_hand_worked_golden_on_gpu(kkt):
+    path = os.path.join(os.path.dirname(__file__), "golden", "hand_worked_chunks.json")
+    with open(path) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        kk = np.array(c["k"], dtype=np.float64)
+        T, Kc = kk.shape
+        k = np.zeros((1, T, 1, 64))
+        k[0, :, 0, :Kc] = kk           # zero padding keeps every dot product
+        wl = W.Workload("golden", 1, T, 1, 64, "f32", "f32", c["g"] is not None, c["beta"] is not None, 0)
+        inp = W.Inputs(wl, k.astype(np.float32),
+                       None if c["g"] is None else np.array(c["g"], dtype=np.float32).reshape(1, T, 1),
+                       None if c["beta"] is None else np.array(c["beta"], dtype=np.float32).reshape(1, T, 1),
+                       None if c["cu_seqlens"] is None else np.array(c["cu_seqlens"], dtype=np.int32))
+        got = run_gpu(kkt, inp, "f32")
+        for t, row in enumerate(c["expected_rows"]):
+            exp = np.zeros(64)
+            exp[:len(row)] = row
+            tol = 1e-6 * np.maximum(np.abs(exp), 1.0)
+            assert np.all(np.abs(got[0, t, 0] - exp) <= tol), (c["name"], t, got[0, t, 0, :4])
+
+
+# ---------------------------------------------------------------- error paths
+def test_error_paths(kkt):
+    inp = W.generate("T256_H8_bf16_f32", T=64, H=1, seed=700)
+    k, g, b, _ = to_device(inp)
+    with pytest.raises(ValueError):
+        kkt.kkt_solve(k, g, b, chunk_size=128)
+    out = torch.empty((1, 64, 1, 64), device=k.device)
+    for kwargs, status in (
+        (dict(chunk_size=32), kkt.KKT_ERR_UNSUPPORTED),
+        (dict(K=100), kkt.KKT_ERR_UNSUPPORTED),
+        (dict(in_dtype=7), kkt.KKT_ERR_INVALID_ARGUMENT),
+        (dict(B=0), kkt.KKT_ERR_INVALID_ARGUMENT),
+    ):
+        args = dict(chunk_size=64, K=128, in_dtype=1, B=1)
+        args.update(kwargs)
+        st = kkt.kkt_solve_raw(k.data_ptr(), g.data_ptr(), b.data_ptr(), None, 0, args["B"], 64, 1, args["K"],
+                               args["chunk_size"], args["in_dtype"], 0, out.data_ptr(), None)
+        assert st == status, (kwargs, st, kkt.last_error())
+        assert kkt.last_error()
