@@ -171,18 +171,20 @@ def main():
         with torch.cuda.graph(graph, stream=stream, capture_error_mode="thread_local"):
             for i in range(K):
                 launch(i)
-        graph.replay()  # first replay uploads the graph; not timed
+        with torch.cuda.stream(stream):
+            graph.replay()  # first replay uploads the graph; not timed
         torch.cuda.synchronize()
 
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ev0.record(stream)
-    if graph is not None:
-        graph.replay()
-    else:
-        for i in range(K):
-            launch(i)
-    ev1.record(stream)
+    with torch.cuda.stream(stream):  # a graph replays on the current stream
+        ev0.record(stream)
+        if graph is not None:
+            graph.replay()
+        else:
+            for i in range(K):
+                launch(i)
+        ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ev_ms = ev0.elapsed_time(ev1) / K

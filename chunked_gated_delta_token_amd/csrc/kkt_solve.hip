@@ -138,11 +138,14 @@ template <> __device__ __forceinline__ f32x4 gram_step<Elt::F16>(u32x4 a, u32x4 
 }
 template <> __device__ __forceinline__ f32x4 gram_step<Elt::F32>(u32x4 a, u32x4 b, f32x4 c)
 {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        c = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, a[e]),
-                                                 __builtin_bit_cast(float, b[e]), c, 0, 0, 0);
-    }
+    // reinterpret whole vectors: a bit-cast of a single vector element would
+    // read the vector's first element instead
+    const f32x4 af = __builtin_bit_cast(f32x4, a);
+    const f32x4 bf = __builtin_bit_cast(f32x4, b);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(af[0], bf[0], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(af[1], bf[1], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(af[2], bf[2], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(af[3], bf[3], c, 0, 0, 0);
     return c;
 }
 

@@ -285,7 +285,10 @@ def test_hand_worked_golden_on_gpu(kkt):
         for t, row in enumerate(c["expected_rows"]):
             exp = np.zeros(64)
             exp[:len(row)] = row
-            tol = 1e-6 * np.maximum(np.abs(exp), 1.0)
+            # fp32 exp of an argument x carries a relative error of about
+            # |x| log2(e) 2^-24 (the clamp case has x = 50: ~4.3e-6), so the
+            # fp32 kernel is held to the 1e-5 relative bar of the criteria
+            tol = 1e-5 * np.maximum(np.abs(exp), 1.0)
             assert np.all(np.abs(got[0, t, 0] - exp) <= tol), (c["name"], t, got[0, t, 0, :4])
 
 
