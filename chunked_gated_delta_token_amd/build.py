@@ -28,6 +28,8 @@ def build(verbose: bool = False, extra_flags=()) -> str:
            # packed fp32 VALU ops stay off (see the kernel notes); hipcc's host
            # pass warns that it does not know the feature, which is harmless
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           # MFMA results in ordinary VGPRs: no accumulator-register copies
+           "-mllvm", "-amdgpu-mfma-vgpr-form=1",
            "-Wall", "-I", INCLUDE, "-o", LIB + ".tmp", SRC, *extra_flags]
     if verbose:
         print(" ".join(cmd), flush=True)

@@ -10,16 +10,24 @@
 // One wave64 owns one (chunk, head) tile from load to store; nothing goes
 // back to HBM between the steps.
 //   a1  tile -> (b, t0, L, h); for packed sequences a wave-wide prefix scan
-//       over cu_seqlens (no host sync, no index tensor).
+//       over cu_seqlens (no host sync, no index tensor).  Every tensor of the
+//       tile is then addressed through a buffer resource whose base is the
+//       tile's first row and whose size ends after row L-1: loads of rows
+//       >= L return 0 and stores to them are dropped by the hardware range
+//       check, so no lane needs a bounds test or 64-bit address arithmetic.
 //   a2  K tile [64 x K] straight from HBM into VGPRs: lane (q, m) of the wave
 //       holds row 16*bi + m of each 16-row block bi, 16 contiguous bytes per
 //       MFMA k-step.  S = K K^T uses the same fragments as both operands, so
 //       any fixed assignment of k indices to (lane group, slot) gives S.
-//   a3  g and beta: one value per lane, shared through LDS.
+//   a3  g and beta: one row per lane.
 //   a4  Gram on MFMA (bf16/f16: 16x16x32, fp32: 16x16x4), fp32 accumulate,
 //       only the 10 lower 16x16 blocks.
-//   a5  epilogue on the accumulators: beta row scale, clamped gate, strict
-//       lower mask, all as selects so no inf*0 can appear.
+//   a5  epilogue on the accumulators.  When the chunk's gate values span at
+//       most 50 the clamp cannot bind, and exp(g_i - g_j) factors into
+//       exp(g_i - g_ref) exp(g_ref - g_j) with g_ref = g_0: each lane
+//       computes one row factor r = beta exp(g - g_ref) and one column factor
+//       c = exp(g_ref - g) for its own row, and every element is (r_i S) c_j.
+//       Otherwise every element takes the clamped exp of its own difference.
 //   a6  the four 16x16 unit-lower diagonal blocks inverted side by side by
 //       forward substitution: lane (block, column) keeps one column in
 //       VGPRs, row r needs rows < r only, all 15 steps unrolled (the pages'
@@ -43,7 +51,7 @@
 
 #include "kkt_solve.h"
 
-#define KKT_VERSION_NUMBER 100  // 0.1.0
+#define KKT_VERSION_NUMBER 200  // 0.2.0
 
 namespace {
 
@@ -53,22 +61,25 @@ constexpr int kWavesPerGroup = 4;
 constexpr int kBlockLd = 20;   // padded row stride (floats) of a 16x16 LDS block
 constexpr int kStageLd = 68;   // padded row stride (floats) of the 16x64 store stage
 constexpr float kGateClamp = 50.0f;
+// buffer resource word 3 for raw (untyped) buffer access on gfx9-family GPUs
+constexpr int kRawBufferFlags = 0x00020000;
+constexpr int kNonTemporal = 2;  // cache-policy bit "nt" of a buffer access
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
-// Per-wave LDS.  The store stage reuses the diagonal-A area once the
-// diagonal solve has read it.
+// Per-wave LDS.  One 16x16x4 area holds, in turn, the diagonal blocks of A,
+// the diagonal inverses, and the store stage of each block row.
 struct WaveLds {
-    float g[kChunk];
-    float beta[kChunk];
+    float row_scale[kChunk];  // r (factored gate) or beta (clamped gate)
+    float col_scale[kChunk];  // c (factored gate)
+    float gate[kChunk];       // g (clamped gate)
     union {
-        float adiag[4][16][kBlockLd];
+        float blk[4][16][kBlockLd];
         float stage[16][kStageLd];
     };
-    float xdiag[4][16][kBlockLd];
 };
 static_assert(sizeof(float) * 4 * 16 * kBlockLd >= sizeof(float) * 16 * kStageLd, "stage fits");
 
@@ -79,6 +90,11 @@ __device__ __forceinline__ void wave_lds_sync()
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRawBufferFlags);
 }
 
 // ---------------------------------------------------------------- element types
@@ -149,45 +165,73 @@ template <> __device__ __forceinline__ f32x4 gram_step<Elt::F32>(u32x4 a, u32x4 
     return c;
 }
 
+__device__ __forceinline__ float wave_max(float v)
+{
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) v = fmaxf(v, __shfl_xor(v, d, kWave));
+    return v;
+}
+
+__device__ __forceinline__ float wave_min(float v)
+{
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) v = fminf(v, __shfl_xor(v, d, kWave));
+    return v;
+}
+
+// ---------------------------------------------------------------- launch arguments
+struct KernelArgs {
+    const void* k;
+    const float* g;
+    const float* beta;
+    const int32_t* cu_seqlens;  // nullptr: fixed-length rows
+    void* out;
+    int64_t T;                  // tokens per batch row (total packed tokens for varlen)
+    int32_t num_seqs;
+    int32_t H;
+    int32_t chunks_per_row;
+    int32_t n_tiles;            // tiles in the grid (an upper bound for varlen)
+    uint32_t k_row_bytes;       // bytes between consecutive tokens of one head in k
+    uint32_t o_row_bytes;       // bytes between consecutive tokens of one head in out
+    int32_t xcd_remap;          // 1: give each XCD one contiguous range of tiles
+};
+
 // ---------------------------------------------------------------- tile map (a1)
 struct Tile {
     int64_t row0;  // flat token index (b * T + t0) of the chunk's first row
     int len;       // valid rows L in [1, 64]; 0: no tile
-    int h;
 };
 
 // Packed sequences: the chunk with global index c (chunks numbered sequence
 // by sequence) is found with a wave-wide inclusive scan of per-sequence chunk
 // counts, 64 sequences per pass.  Offsets are clamped into [0, T].
-__device__ Tile varlen_tile(const int32_t* __restrict__ cu, int64_t num_seqs, int64_t T,
-                            int64_t c, int h, int lane)
+__device__ Tile varlen_tile(const int32_t* __restrict__ cu, int32_t num_seqs, int64_t T, int32_t c, int lane)
 {
-    Tile t{0, 0, h};
-    int64_t before = 0;  // chunks in the sequences already passed
-    for (int64_t base = 0; base < num_seqs; base += kWave) {
-        const int64_t s = base + lane;
+    Tile t{0, 0};
+    int32_t before = 0;  // chunks in the sequences already passed
+    for (int32_t base = 0; base < num_seqs; base += kWave) {
+        const int32_t s = base + lane;
         int64_t bos = 0, eos = 0;
         if (s < num_seqs) {
-            int64_t a = cu[s], e = cu[s + 1];
+            const int64_t a = cu[s], e = cu[s + 1];
             bos = a < 0 ? 0 : (a > T ? T : a);
             eos = e < bos ? bos : (e > T ? T : e);
         }
-        const int64_t n = (eos - bos + kChunk - 1) / kChunk;
-        int64_t incl = n;
+        const int32_t n = (int32_t)((eos - bos + kChunk - 1) / kChunk);
+        int32_t incl = n;
 #pragma unroll
         for (int d = 1; d < kWave; d <<= 1) {
-            const int64_t up = __shfl_up(incl, d, kWave);
+            const int32_t up = __shfl_up(incl, d, kWave);
             if (lane >= d) incl += up;
         }
         const bool hit = (s < num_seqs) && (before + incl > c);
         const uint64_t mask = __ballot(hit);
         if (mask != 0) {
             const int src = __builtin_ctzll(mask);
-            const int64_t excl = incl - n;
-            const int64_t sel_excl = __shfl(excl, src, kWave);
+            const int32_t sel_excl = __shfl(incl - n, src, kWave);
             const int64_t sel_bos = __shfl(bos, src, kWave);
             const int64_t sel_eos = __shfl(eos, src, kWave);
-            const int64_t t0 = sel_bos + (c - before - sel_excl) * kChunk;
+            const int64_t t0 = sel_bos + (int64_t)(c - before - sel_excl) * kChunk;
             const int64_t rem = sel_eos - t0;
             t.row0 = t0;
             t.len = (int)(rem < kChunk ? rem : kChunk);
@@ -201,132 +245,182 @@ __device__ Tile varlen_tile(const int32_t* __restrict__ cu, int64_t num_seqs, in
 // ---------------------------------------------------------------- the kernel
 template <Elt IN, Elt OUT, int K>
 __global__ __launch_bounds__(kWave * kWavesPerGroup)
-void kkt_solve_kernel(const typename EltInfo<IN>::storage* __restrict__ k,
-                      const float* __restrict__ g, const float* __restrict__ beta,
-                      const int32_t* __restrict__ cu_seqlens, int64_t num_seqs,
-                      int64_t T, int H, int64_t chunks_per_row, int64_t n_tiles,
-                      typename EltInfo<OUT>::storage* __restrict__ out)
+void kkt_solve_kernel(const KernelArgs args)
 {
-    using in_t = typename EltInfo<IN>::storage;
-    constexpr int kElemsPer16B = 16 / EltInfo<IN>::bytes;  // 8 (16-bit) or 4 (fp32)
+    constexpr int kInBytes = EltInfo<IN>::bytes;
+    constexpr int kOutBytes = EltInfo<OUT>::bytes;
+    constexpr int kElemsPer16B = 16 / kInBytes;            // 8 (16-bit) or 4 (fp32)
     constexpr int kSteps = K / (4 * kElemsPer16B);          // 16-byte fragments per row per lane
     static_assert(K % (4 * kElemsPer16B) == 0, "K must fill whole fragments");
 
     __shared__ WaveLds lds_all[kWavesPerGroup];
 
     const int lane = threadIdx.x % kWave;
-    const int wave = threadIdx.x / kWave;
+    // wave-uniform values are pinned to scalar registers so that the buffer
+    // resources built from them are scalar too
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int q = lane / 16;   // lane group (k-slot group of an MFMA operand)
     const int m = lane % 16;   // row inside a 16-row block (A operand) / column (D layout)
     WaveLds& lds = lds_all[wave];
 
-    // XCD-aware order: workgroups are dispatched round-robin over the 8 XCDs;
-    // give each XCD one contiguous range of tiles so that the heads of one
-    // chunk (adjacent in memory) and their shared g/beta lines meet in one L2.
-    const int64_t n_groups = gridDim.x;
-    const int64_t hw = blockIdx.x;
-    const int64_t xcd = hw % 8, slot = hw / 8;
-    const int64_t per = n_groups / 8, extra = n_groups % 8;
-    const int64_t group = (xcd < extra) ? xcd * (per + 1) + slot
-                                        : extra * (per + 1) + (xcd - extra) * per + slot;
-    const int64_t tile_id = group * kWavesPerGroup + wave;
-    if (tile_id >= n_tiles) return;
+    // Workgroup order.  Workgroups are dispatched round-robin over the 8 XCDs;
+    // with xcd_remap each XCD gets one contiguous range of tiles instead.
+    const uint32_t n_groups = gridDim.x;
+    const uint32_t hw = blockIdx.x;
+    uint32_t group = hw;
+    if (args.xcd_remap) {
+        const uint32_t xcd = hw % 8, slot = hw / 8;
+        const uint32_t per = n_groups / 8, extra = n_groups % 8;
+        group = (xcd < extra) ? xcd * (per + 1) + slot : extra * (per + 1) + (xcd - extra) * per + slot;
+    }
+    const uint32_t tile_id = group * kWavesPerGroup + wave;
+    if (tile_id >= (uint32_t)args.n_tiles) return;  // wave-uniform
 
     // ---- a1: tile map
-    const int h = (int)(tile_id % H);
-    const int64_t chunk = tile_id / H;
+    const int H = args.H;
+    const int h = (int)(tile_id % (uint32_t)H);
+    const uint32_t chunk = tile_id / (uint32_t)H;
     Tile tile;
-    if (cu_seqlens == nullptr) {
-        const int64_t b = chunk / chunks_per_row;
-        const int64_t c = chunk % chunks_per_row;
-        const int64_t t0 = c * kChunk;
-        tile.row0 = b * T + t0;
-        tile.len = (int)((T - t0) < kChunk ? (T - t0) : kChunk);
-        tile.h = h;
+    if (args.cu_seqlens == nullptr) {
+        const uint32_t b = chunk / (uint32_t)args.chunks_per_row;
+        const uint32_t c = chunk % (uint32_t)args.chunks_per_row;
+        const int64_t t0 = (int64_t)c * kChunk;
+        tile.row0 = (int64_t)b * args.T + t0;
+        tile.len = (int)((args.T - t0) < kChunk ? (args.T - t0) : kChunk);
     } else {
-        tile = varlen_tile(cu_seqlens, num_seqs, T, chunk, h, lane);
+        tile = varlen_tile(args.cu_seqlens, args.num_seqs, args.T, (int32_t)chunk, lane);
     }
-    const int L = tile.len;
+    const int L = __builtin_amdgcn_readfirstlane(tile.len);
     if (L <= 0) return;  // wave-uniform
+    const int64_t row0 = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(tile.row0 >> 32)) << 32) |
+                                   (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)tile.row0));
 
-    // ---- a2: K fragments, all loads issued up front
+    // Buffer resources spanning exactly rows 0 .. L-1 of this tile.
+    const int64_t tok = row0 * H + h;  // flat (token, head) index of row 0
+    const __amdgpu_buffer_rsrc_t k_rsrc = make_rsrc(
+        static_cast<const char*>(args.k) + tok * (int64_t)(K * kInBytes),
+        (uint32_t)(L - 1) * args.k_row_bytes + K * kInBytes);
+    const __amdgpu_buffer_rsrc_t o_rsrc = make_rsrc(
+        static_cast<char*>(args.out) + tok * (int64_t)(kChunk * kOutBytes),
+        (uint32_t)(L - 1) * args.o_row_bytes + kChunk * kOutBytes);
+
+    // ---- a3: g and beta, one row per lane (rows >= L read as 0).  Issued
+    // before the K tile: loads complete in order, so waiting for these two
+    // does not wait for the whole tile.
+    const bool has_g = args.g != nullptr;
+    const bool valid = lane < L;
+    float gv = 0.0f, bv = 1.0f;
+    {
+        const uint32_t voff = (uint32_t)lane * (uint32_t)H * 4u;
+        const uint32_t span = (uint32_t)(L - 1) * (uint32_t)H * 4u + 4u;
+        // the loads return raw 32-bit words: reinterpret, do not convert
+        if (has_g) {
+            gv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(args.g + tok, span), voff, 0, 0));
+        }
+        if (args.beta != nullptr) {
+            bv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(args.beta + tok, span), voff, 0, 0));
+        }
+    }
+
+    // ---- a2: K fragments, all loads issued up front (rows >= L read as 0).
+    // Each load instruction reads 64 bytes of 16 rows; the next k-step reads
+    // the other half of the same 128-byte lines, so these loads are not
+    // marked streaming (the lines must survive in L2 until then).  The
+    // scheduling barrier keeps every load ahead of the first MFMA, so the
+    // whole tile is in flight at once.
     u32x4 frag[4][kSteps];
 #pragma unroll
     for (int bi = 0; bi < 4; ++bi) {
-        const int r = 16 * bi + m;
-        const in_t* src = k + ((tile.row0 + r) * H + h) * (int64_t)K + q * kElemsPer16B;
+        const uint32_t voff = (uint32_t)(16 * bi + m) * args.k_row_bytes + q * 16;
 #pragma unroll
         for (int s = 0; s < kSteps; ++s) {
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (r < L) {
-                v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + s * 4 * kElemsPer16B));
-            }
-            frag[bi][s] = v;
+            frag[bi][s] = __builtin_amdgcn_raw_buffer_load_b128(k_rsrc, voff + s * 64, 0, 0);
         }
     }
+    __builtin_amdgcn_sched_barrier(0);
 
-    // ---- a3: g and beta, one row per lane (rows >= L: gate 0, beta 0)
-    {
-        float gv = 0.0f, bv = 0.0f;
-        if (lane < L) {
-            const int64_t idx = (tile.row0 + lane) * H + h;
-            gv = (g != nullptr) ? g[idx] : 0.0f;
-            bv = (beta != nullptr) ? beta[idx] : 1.0f;
-        }
-        lds.g[lane] = gv;
-        lds.beta[lane] = bv;
-    }
-    wave_lds_sync();
-    const bool has_g = (g != nullptr);
-    f32x4 g_row[4], b_row[4];
-    float g_col[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        g_row[i] = *reinterpret_cast<const f32x4*>(&lds.g[16 * i + 4 * q]);
-        b_row[i] = *reinterpret_cast<const f32x4*>(&lds.beta[16 * i + 4 * q]);
-        g_col[i] = lds.g[16 * i + m];
-    }
-
-    // ---- a4 + a5: Gram blocks and epilogue.  Block (i, j): lane (q, n=m)
-    // holds rows 16i + 4q + r, column 16j + n.
-    auto epilogue = [&](f32x4 s, int i, int j) -> f32x4 {
-        f32x4 a;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int row = 16 * i + 4 * q + r;
-            const int col = 16 * j + m;
-            float gate = 1.0f;
-            if (has_g) {
-                float d = g_row[i][r] - g_col[j];
-                d = fminf(fmaxf(d, -kGateClamp), kGateClamp);
-                gate = __expf(d);
-            }
-            const float v = b_row[i][r] * (s[r] * gate);
-            a[r] = (row > col && row < L) ? v : 0.0f;
-        }
-        return a;
-    };
+    // ---- a4: Gram blocks.  Block (i, j): lane (q, n=m) holds rows 16i + 4q + r, column 16j + n.
     auto gram = [&](int i, int j) -> f32x4 {
         f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int s = 0; s < kSteps; ++s) acc = gram_step<IN>(frag[i][s], frag[j][s], acc);
         return acc;
     };
-
-    // diagonal blocks go to LDS for the solve
+    f32x4 S[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const f32x4 a = epilogue(gram(i, i), i, i);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) lds.adiag[i][4 * q + r][m] = a[r];
+        for (int j = 0; j <= i; ++j) S[i][j] = gram(i, j);
     }
-    // off-diagonal blocks stay in VGPRs (layout: lane (q, n) = A_ij[4q + r][n])
-    const f32x4 a10 = epilogue(gram(1, 0), 1, 0);
-    const f32x4 a20 = epilogue(gram(2, 0), 2, 0);
-    const f32x4 a21 = epilogue(gram(2, 1), 2, 1);
-    const f32x4 a30 = epilogue(gram(3, 0), 3, 0);
-    const f32x4 a31 = epilogue(gram(3, 1), 3, 1);
-    const f32x4 a32 = epilogue(gram(3, 2), 3, 2);
+
+    // ---- a5: epilogue
+    bool factored = true;
+    if (has_g) {
+        const float gmax = wave_max(valid ? gv : -__builtin_inff());
+        const float gmin = wave_min(valid ? gv : __builtin_inff());
+        factored = (gmax - gmin) <= kGateClamp;
+        // reference: row 0's gate (always a valid row), so the factors of
+        // rows < L do not depend on L; with the spread <= 50 every factor
+        // lies in [e^-50, e^50]
+        const float gref = __shfl(gv, 0, kWave);
+        if (factored) {
+            const float d = gv - gref;
+            lds.row_scale[lane] = valid ? bv * __expf(d) : 0.0f;
+            lds.col_scale[lane] = valid ? __expf(-d) : 0.0f;
+        } else {
+            lds.row_scale[lane] = valid ? bv : 0.0f;
+            lds.gate[lane] = valid ? gv : 0.0f;
+        }
+    } else {
+        lds.row_scale[lane] = valid ? bv : 0.0f;
+    }
+    wave_lds_sync();
+    f32x4 A[4][4];
+    if (!has_g) {
+        // A = beta_i S (rows >= L have beta 0 and zero keys)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const f32x4 rr = *reinterpret_cast<const f32x4*>(&lds.row_scale[16 * i + 4 * q]);
+#pragma unroll
+            for (int j = 0; j <= i; ++j) A[i][j] = rr * S[i][j];
+        }
+    } else if (factored) {
+        // A = (r_i S) c_j: both factors are zero outside the chunk's L rows
+        float cc[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) cc[j] = lds.col_scale[16 * j + m];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const f32x4 rr = *reinterpret_cast<const f32x4*>(&lds.row_scale[16 * i + 4 * q]);
+#pragma unroll
+            for (int j = 0; j <= i; ++j) A[i][j] = (rr * S[i][j]) * cc[j];
+        }
+    } else {
+        // A = beta_i S exp(clamp(g_i - g_j)); the clamp bounds the gate, so
+        // zero keys and zero beta outside the chunk still give 0
+        float gc[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) gc[j] = lds.gate[16 * j + m];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const f32x4 rr = *reinterpret_cast<const f32x4*>(&lds.row_scale[16 * i + 4 * q]);
+            const f32x4 gr = *reinterpret_cast<const f32x4*>(&lds.gate[16 * i + 4 * q]);
+#pragma unroll
+            for (int j = 0; j <= i; ++j) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float d = fminf(fmaxf(gr[r] - gc[j], -kGateClamp), kGateClamp);
+                    A[i][j][r] = rr[r] * (S[i][j][r] * __expf(d));
+                }
+            }
+        }
+    }
+    // strict lower triangle inside the diagonal blocks, then to LDS for the solve
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) lds.blk[i][4 * q + r][m] = (4 * q + r > m) ? A[i][i][r] : 0.0f;
+    }
     wave_lds_sync();
 
     // ---- a6: X_dd = (I + A_dd)^{-1}; lane (d = lane / 16, c = lane % 16)
@@ -341,7 +435,7 @@ void kkt_solve_kernel(const typename EltInfo<IN>::storage* __restrict__ k,
             float arow[16];
 #pragma unroll
             for (int u = 0; u < (r + 3) / 4; ++u) {
-                const f32x4 v = *reinterpret_cast<const f32x4*>(&lds.adiag[d][r][4 * u]);
+                const f32x4 v = *reinterpret_cast<const f32x4*>(&lds.blk[d][r][4 * u]);
                 arow[4 * u + 0] = v[0];
                 arow[4 * u + 1] = v[1];
                 arow[4 * u + 2] = v[2];
@@ -352,8 +446,9 @@ void kkt_solve_kernel(const typename EltInfo<IN>::storage* __restrict__ k,
             for (int p = 0; p < r; ++p) acc = __builtin_fmaf(-arow[p], x[p], acc);
             x[r] = acc;
         }
+        wave_lds_sync();  // every read of A_dd precedes the overwrite with X_dd
 #pragma unroll
-        for (int r = 0; r < 16; ++r) lds.xdiag[d][r][c] = x[r];
+        for (int r = 0; r < 16; ++r) lds.blk[d][r][c] = x[r];
     }
     wave_lds_sync();
 
@@ -363,16 +458,16 @@ void kkt_solve_kernel(const typename EltInfo<IN>::storage* __restrict__ k,
     f32x4 xa[4], xd[4];
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-        xa[d] = *reinterpret_cast<const f32x4*>(&lds.xdiag[d][m][4 * q]);
+        xa[d] = *reinterpret_cast<const f32x4*>(&lds.blk[d][m][4 * q]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) xd[d][r] = lds.xdiag[d][4 * q + r][m];
+        for (int r = 0; r < 4; ++r) xd[d][r] = lds.blk[d][4 * q + r][m];
     }
 
     // ---- a8 helper: stage one 16-row block row and write full output rows
-    using out_t = typename EltInfo<OUT>::storage;
+    // (rows >= L fall outside o_rsrc and are dropped)
     const f32x4 zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
     auto store_block_row = [&](int i, f32x4 b0, f32x4 b1, f32x4 b2, f32x4 b3) {
-        wave_lds_sync();  // earlier stage reads (and the solve's adiag reads) are done
+        wave_lds_sync();  // earlier reads of the area are done
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             lds.stage[4 * q + r][0 + m] = b0[r];
@@ -387,12 +482,9 @@ void kkt_solve_kernel(const typename EltInfo<IN>::storage* __restrict__ k,
 #pragma unroll
             for (int it = 0; it < 4; ++it) {
                 const int rr = 4 * it + rsub;
-                const int row = 16 * i + rr;
                 const f32x4 v = *reinterpret_cast<const f32x4*>(&lds.stage[rr][c4]);
-                if (row < L) {
-                    float* dst = reinterpret_cast<float*>(out) + ((tile.row0 + row) * H + h) * (int64_t)kChunk + c4;
-                    __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(dst));
-                }
+                const uint32_t voff = (uint32_t)(16 * i + rr) * args.o_row_bytes + c4 * 4;
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), o_rsrc, voff, 0, kNonTemporal);
             }
         } else {
             // 8 lanes per 128-byte row, 8 rows per pass
@@ -400,7 +492,6 @@ void kkt_solve_kernel(const typename EltInfo<IN>::storage* __restrict__ k,
 #pragma unroll
             for (int it = 0; it < 2; ++it) {
                 const int rr = 8 * it + rsub;
-                const int row = 16 * i + rr;
                 const f32x4 v0 = *reinterpret_cast<const f32x4*>(&lds.stage[rr][c8]);
                 const f32x4 v1 = *reinterpret_cast<const f32x4*>(&lds.stage[rr][c8 + 4]);
                 u32x4 p;
@@ -408,10 +499,8 @@ void kkt_solve_kernel(const typename EltInfo<IN>::storage* __restrict__ k,
                 p[1] = pack2<OUT>(v0[2], v0[3]);
                 p[2] = pack2<OUT>(v1[0], v1[1]);
                 p[3] = pack2<OUT>(v1[2], v1[3]);
-                if (row < L) {
-                    out_t* dst = out + ((tile.row0 + row) * H + h) * (int64_t)kChunk + c8;
-                    __builtin_nontemporal_store(p, reinterpret_cast<u32x4*>(dst));
-                }
+                const uint32_t voff = (uint32_t)(16 * i + rr) * args.o_row_bytes + c8 * 2;
+                __builtin_amdgcn_raw_buffer_store_b128(p, o_rsrc, voff, 0, kNonTemporal);
             }
         }
     };
@@ -421,12 +510,12 @@ void kkt_solve_kernel(const typename EltInfo<IN>::storage* __restrict__ k,
 
     // ---- a7: merge.  wt_ik = (X_ii A_ik)^T; its result layout is the left
     // operand layout of W_ik.
-    const f32x4 wt10 = mm16(a10, xa[1], zero4);
-    const f32x4 wt20 = mm16(a20, xa[2], zero4);
-    const f32x4 wt21 = mm16(a21, xa[2], zero4);
-    const f32x4 wt30 = mm16(a30, xa[3], zero4);
-    const f32x4 wt31 = mm16(a31, xa[3], zero4);
-    const f32x4 wt32 = mm16(a32, xa[3], zero4);
+    const f32x4 wt10 = mm16(A[1][0], xa[1], zero4);
+    const f32x4 wt20 = mm16(A[2][0], xa[2], zero4);
+    const f32x4 wt21 = mm16(A[2][1], xa[2], zero4);
+    const f32x4 wt30 = mm16(A[3][0], xa[3], zero4);
+    const f32x4 wt31 = mm16(A[3][1], xa[3], zero4);
+    const f32x4 wt32 = mm16(A[3][2], xa[3], zero4);
 
     // X_ij = 0 - sum(...): exact negation that turns an all-zero sum into +0.0
     const f32x4 x10 = zero4 - mm16(wt10, xd[0], zero4);
@@ -456,7 +545,7 @@ constexpr int kMaxDevices = 64;
 int g_arch_ok[kMaxDevices];
 std::mutex g_arch_mutex;
 
-kkt_status_t check_device(int* dev_out)
+kkt_status_t check_device()
 {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -470,7 +559,6 @@ kkt_status_t check_device(int* dev_out)
         g_arch_ok[dev] = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
     }
     if (g_arch_ok[dev] != 1) return fail(KKT_ERR_UNSUPPORTED, "device is not gfx950 (MI355X); this library is built for gfx950 only");
-    *dev_out = dev;
     return KKT_OK;
 }
 
@@ -490,42 +578,41 @@ kkt_status_t validate_cu_seqlens(const int32_t* cu, int64_t num_seqs, int64_t T,
 }
 
 template <Elt IN, Elt OUT, int K>
-hipError_t launch(const void* k, const float* g, const float* beta, const int32_t* cu, int64_t num_seqs,
-                  int64_t T, int64_t H, int64_t chunks_per_row, int64_t n_tiles, void* out,
-                  hipStream_t stream)
+hipError_t launch(const KernelArgs& a, hipStream_t stream)
 {
-    const int64_t groups = (n_tiles + kWavesPerGroup - 1) / kWavesPerGroup;
+    const int64_t groups = ((int64_t)a.n_tiles + kWavesPerGroup - 1) / kWavesPerGroup;
     hipLaunchKernelGGL((kkt_solve_kernel<IN, OUT, K>), dim3((unsigned)groups), dim3(kWave * kWavesPerGroup), 0,
-                       stream, static_cast<const typename EltInfo<IN>::storage*>(k), g, beta, cu, num_seqs, T,
-                       (int)H, chunks_per_row, n_tiles, static_cast<typename EltInfo<OUT>::storage*>(out));
+                       stream, a);
     return hipGetLastError();
 }
 
 template <Elt IN, Elt OUT>
-hipError_t launch_k(int64_t K, const void* k, const float* g, const float* beta, const int32_t* cu,
-                    int64_t num_seqs, int64_t T, int64_t H, int64_t cpr, int64_t n_tiles, void* out,
-                    hipStream_t stream)
+hipError_t launch_k(int64_t K, const KernelArgs& a, hipStream_t stream)
 {
     switch (K) {
-    case 64: return launch<IN, OUT, 64>(k, g, beta, cu, num_seqs, T, H, cpr, n_tiles, out, stream);
-    case 128: return launch<IN, OUT, 128>(k, g, beta, cu, num_seqs, T, H, cpr, n_tiles, out, stream);
-    default: return launch<IN, OUT, 256>(k, g, beta, cu, num_seqs, T, H, cpr, n_tiles, out, stream);
+    case 64: return launch<IN, OUT, 64>(a, stream);
+    case 128: return launch<IN, OUT, 128>(a, stream);
+    default: return launch<IN, OUT, 256>(a, stream);
     }
 }
 
 template <Elt IN>
-hipError_t launch_out(kkt_dtype_t od, int64_t K, const void* k, const float* g, const float* beta,
-                      const int32_t* cu, int64_t num_seqs, int64_t T, int64_t H, int64_t cpr, int64_t n_tiles,
-                      void* out, hipStream_t stream)
+hipError_t launch_out(kkt_dtype_t od, int64_t K, const KernelArgs& a, hipStream_t stream)
 {
     switch (od) {
-    case KKT_DTYPE_F32: return launch_k<IN, Elt::F32>(K, k, g, beta, cu, num_seqs, T, H, cpr, n_tiles, out, stream);
-    case KKT_DTYPE_BF16: return launch_k<IN, Elt::BF16>(K, k, g, beta, cu, num_seqs, T, H, cpr, n_tiles, out, stream);
-    default: return launch_k<IN, Elt::F16>(K, k, g, beta, cu, num_seqs, T, H, cpr, n_tiles, out, stream);
+    case KKT_DTYPE_F32: return launch_k<IN, Elt::F32>(K, a, stream);
+    case KKT_DTYPE_BF16: return launch_k<IN, Elt::BF16>(K, a, stream);
+    default: return launch_k<IN, Elt::F16>(K, a, stream);
     }
 }
 
 bool valid_dtype(int d) { return d == KKT_DTYPE_F32 || d == KKT_DTYPE_BF16 || d == KKT_DTYPE_F16; }
+int64_t dtype_bytes(kkt_dtype_t d) { return d == KKT_DTYPE_F32 ? 4 : 2; }
+
+// Grids up to this many workgroups use the XCD-contiguous tile order; larger
+// ones keep the hardware's round-robin order, which spreads each XCD's
+// concurrent accesses over the whole tensor.
+constexpr int64_t kRemapMaxGroups = 1024;
 
 }  // namespace
 
@@ -541,22 +628,27 @@ extern "C" kkt_status_t kkt_solve(const void* k, const float* g, const float* be
     if (!valid_dtype((int)in_dtype) || !valid_dtype((int)out_dtype)) return fail(KKT_ERR_INVALID_ARGUMENT, "unknown dtype");
     if (B < 1 || H < 1 || K < 1 || T < 0) return fail(KKT_ERR_INVALID_ARGUMENT, "B, H, K must be >= 1 and T >= 0");
     if (K != 64 && K != 128 && K != 256) return fail(KKT_ERR_UNSUPPORTED, "K must be 64, 128 or 256");
-    if (H > (int64_t)0x7FFFFFFF) return fail(KKT_ERR_INVALID_ARGUMENT, "H too large");
     if (cu_seqlens != nullptr && (B != 1 || num_seqs < 1)) {
         return fail(KKT_ERR_INVALID_ARGUMENT, "cu_seqlens needs B == 1 and num_seqs >= 1");
     }
     if (T == 0) return KKT_OK;
     if (k == nullptr || out == nullptr) return fail(KKT_ERR_INVALID_ARGUMENT, "k and out must not be NULL");
 
+    // 32-bit in-tile offsets: 64 rows of one head must span < 2 GiB
+    const int64_t k_row_bytes = H * K * dtype_bytes(in_dtype);
+    const int64_t o_row_bytes = H * kChunk * dtype_bytes(out_dtype);
+    if (kChunk * k_row_bytes >= (1LL << 31) || kChunk * o_row_bytes >= (1LL << 31)) {
+        return fail(KKT_ERR_UNSUPPORTED, "H * K too large for one launch");
+    }
     const int64_t chunks_per_row = (T + kChunk - 1) / kChunk;
     // Packed sequences: at most floor(T/64) + num_seqs chunks; surplus waves exit.
     const int64_t n_chunks = (cu_seqlens == nullptr) ? B * chunks_per_row : T / kChunk + num_seqs;
     const int64_t n_tiles = n_chunks * H;
-    const int64_t groups = (n_tiles + kWavesPerGroup - 1) / kWavesPerGroup;
-    if (groups > 0x7FFFFFFFLL) return fail(KKT_ERR_INVALID_ARGUMENT, "problem too large for one launch");
+    if (n_tiles >= (1LL << 31) - kWavesPerGroup || num_seqs >= (1LL << 31) - 1) {
+        return fail(KKT_ERR_UNSUPPORTED, "problem too large for one launch");
+    }
 
-    int dev = 0;
-    kkt_status_t st = check_device(&dev);
+    kkt_status_t st = check_device();
     if (st != KKT_OK) return st;
     if (cu_seqlens != nullptr) {
         const char* v = getenv("KKT_VALIDATE");
@@ -566,17 +658,27 @@ extern "C" kkt_status_t kkt_solve(const void* k, const float* g, const float* be
         }
     }
 
+    KernelArgs a;
+    a.k = k;
+    a.g = g;
+    a.beta = beta;
+    a.cu_seqlens = cu_seqlens;
+    a.out = out;
+    a.T = T;
+    a.num_seqs = (int32_t)num_seqs;
+    a.H = (int32_t)H;
+    a.chunks_per_row = (int32_t)chunks_per_row;
+    a.n_tiles = (int32_t)n_tiles;
+    a.k_row_bytes = (uint32_t)k_row_bytes;
+    a.o_row_bytes = (uint32_t)o_row_bytes;
+    const int64_t groups = (n_tiles + kWavesPerGroup - 1) / kWavesPerGroup;
+    a.xcd_remap = groups <= kRemapMaxGroups ? 1 : 0;
+
     hipError_t e;
     switch (in_dtype) {
-    case KKT_DTYPE_F32:
-        e = launch_out<Elt::F32>(out_dtype, K, k, g, beta, cu_seqlens, num_seqs, T, H, chunks_per_row, n_tiles, out, stream);
-        break;
-    case KKT_DTYPE_BF16:
-        e = launch_out<Elt::BF16>(out_dtype, K, k, g, beta, cu_seqlens, num_seqs, T, H, chunks_per_row, n_tiles, out, stream);
-        break;
-    default:
-        e = launch_out<Elt::F16>(out_dtype, K, k, g, beta, cu_seqlens, num_seqs, T, H, chunks_per_row, n_tiles, out, stream);
-        break;
+    case KKT_DTYPE_F32: e = launch_out<Elt::F32>(out_dtype, K, a, stream); break;
+    case KKT_DTYPE_BF16: e = launch_out<Elt::BF16>(out_dtype, K, a, stream); break;
+    default: e = launch_out<Elt::F16>(out_dtype, K, a, stream); break;
     }
     if (e != hipSuccess) return fail(KKT_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(e));
     return KKT_OK;

@@ -47,7 +47,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version(lib):
-    assert lib.kkt_version() == 100
+    assert lib.kkt_version() == 200
 
 
 def _call(lib, **over):
