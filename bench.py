@@ -89,6 +89,76 @@ def cpu_baseline(inp, nbytes: int, budget_s: float):
             "sample": f"the whole workload, {reps} calls in {el:.1f} s (fp64, OpenMP over chunk-head tiles)"}
 
 
+def copy_calibration(nbytes: int, steps: int):
+    """Plain device-to-device copies of a known size, over buffers rotated
+    past the Infinity Cache: under rocprofv3 --pmc they give the counter
+    reading per byte actually read / written."""
+    import torch
+    n = nbytes // 4
+    R = max(2, -(-2 * MALL_BYTES // (2 * nbytes)))
+    src = [torch.ones(n, device="cuda") for _ in range(R)]
+    dst = [torch.empty(n, device="cuda") for _ in range(R)]
+    for i in range(steps):
+        dst[i % R].copy_(src[i % R])
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n * 4, "steps": steps, "buffer_sets": R}), flush=True)
+
+
+def _counter_values(directory: str, counter: str, kernel_substr: str):
+    """Per-dispatch values of one counter for kernels whose name contains
+    kernel_substr, from a rocprofv3 --pmc CSV output directory."""
+    import csv
+    import glob
+    vals = []
+    for path in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+        with open(path, newline="") as f:
+            for row in csv.DictReader(f):
+                if row.get("Counter_Name") == counter and kernel_substr in row.get("Kernel_Name", ""):
+                    vals.append(float(row["Counter_Value"]))
+    if not vals:
+        raise SystemExit(f"no {counter} values for '{kernel_substr}' under {directory}")
+    return vals
+
+
+def summarize_traffic(dirs, copy_bytes: int):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the op, each scaled by
+    the bytes-per-KiB ratio the same counter shows for a plain copy."""
+    import statistics
+    if copy_bytes <= 0:
+        raise SystemExit("--copy-bytes is required")
+    op_fetch = statistics.median(_counter_values(dirs[0], "FETCH_SIZE", "kkt_solve_kernel"))
+    op_write = statistics.median(_counter_values(dirs[1], "WRITE_SIZE", "kkt_solve_kernel"))
+    cp_fetch = statistics.median(_counter_values(dirs[2], "FETCH_SIZE", "copy"))
+    cp_write = statistics.median(_counter_values(dirs[3], "WRITE_SIZE", "copy"))
+    f_scale = copy_bytes / cp_fetch
+    w_scale = copy_bytes / cp_write
+    fetch_b, write_b = op_fetch * f_scale, op_write * w_scale
+    lines = [
+        "# HBM traffic of kkt_solve_kernel, bench workload T8192_H8_bf16_f32 (B=1,T=8192,H=8,K=128 bf16 -> fp32)",
+        "# commands (run from the repository root, then summarized by the last one):",
+        "#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d <op_fetch> -- python bench.py --timing eager --steps 20 --warmup 2 --no-cpu-baseline",
+        "#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d <op_write> -- python bench.py --timing eager --steps 20 --warmup 2 --no-cpu-baseline",
+        f"#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d <copy_fetch> -- python bench.py --copy-calibration {copy_bytes} --steps 20",
+        f"#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d <copy_write> -- python bench.py --copy-calibration {copy_bytes} --steps 20",
+        f"#   python bench.py --summarize-traffic <op_fetch> <op_write> <copy_fetch> <copy_write> --copy-bytes {copy_bytes}",
+        f"kernel_source_sha256_16: {source_digest()}",
+        f"op_fetch_size_kib_median: {op_fetch:.1f}",
+        f"op_write_size_kib_median: {op_write:.1f}",
+        f"copy_bytes: {copy_bytes}",
+        f"copy_fetch_size_kib_median: {cp_fetch:.1f}",
+        f"copy_write_size_kib_median: {cp_write:.1f}",
+        f"fetch_bytes_per_kib: {f_scale:.2f}",
+        f"write_bytes_per_kib: {w_scale:.2f}",
+        f"fetch_bytes_per_launch: {fetch_b:.0f}",
+        f"write_bytes_per_launch: {write_b:.0f}",
+        f"hbm_bytes_per_launch: {fetch_b + write_b:.0f}",
+    ]
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -99,7 +169,17 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--detail", action="store_true", help="also print per-launch event timings to stderr")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="instead of the op, run --steps plain device copies of BYTES bytes (the reference "
+                         "kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--summarize-traffic", nargs=4, metavar=("OP_FETCH", "OP_WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="write the HBM-traffic summary from four rocprofv3 --pmc output directories")
+    ap.add_argument("--copy-bytes", type=int, default=0, help="size used by the copy-calibration runs")
     args = ap.parse_args()
+
+    if args.summarize_traffic:
+        summarize_traffic(args.summarize_traffic, args.copy_bytes)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the fused KKT + solve has no cross-GPU step, and this "
@@ -108,6 +188,10 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, args.steps)
+        return
 
     from chunked_gated_delta_token_amd import kkt
     from chunked_gated_delta_token_amd import workloads as W
