@@ -22,12 +22,13 @@
 //   a3  g and beta: one row per lane.
 //   a4  Gram on MFMA (bf16/f16: 16x16x32, fp32: 16x16x4), fp32 accumulate,
 //       only the 10 lower 16x16 blocks.
-//   a5  epilogue on the accumulators.  When the chunk's gate values span at
-//       most 50 the clamp cannot bind, and exp(g_i - g_j) factors into
-//       exp(g_i - g_ref) exp(g_ref - g_j) with g_ref = g_0: each lane
-//       computes one row factor r = beta exp(g - g_ref) and one column factor
-//       c = exp(g_ref - g) for its own row, and every element is (r_i S) c_j.
-//       Otherwise every element takes the clamped exp of its own difference.
+//   a5  epilogue on the accumulators.  When every gate value of the chunk
+//       is within 25 of g_0, no pair differs by more than 50, the clamp
+//       cannot bind, and exp(g_i - g_j) factors into exp(g_i - g_0)
+//       exp(g_0 - g_j): each lane computes one row factor r = beta exp(g - g_0)
+//       and one column factor c = exp(g_0 - g) for its own row, and every
+//       element is (r_i S) c_j.  Otherwise every element takes the clamped exp
+//       of its own difference.
 //   a6  the four 16x16 unit-lower diagonal blocks inverted side by side by
 //       forward substitution: lane (block, column) keeps one column in
 //       VGPRs, row r needs rows < r only, all 15 steps unrolled (the pages'
@@ -163,20 +164,6 @@ template <> __device__ __forceinline__ f32x4 gram_step<Elt::F32>(u32x4 a, u32x4 
     c = __builtin_amdgcn_mfma_f32_16x16x4f32(af[2], bf[2], c, 0, 0, 0);
     c = __builtin_amdgcn_mfma_f32_16x16x4f32(af[3], bf[3], c, 0, 0, 0);
     return c;
-}
-
-__device__ __forceinline__ float wave_max(float v)
-{
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) v = fmaxf(v, __shfl_xor(v, d, kWave));
-    return v;
-}
-
-__device__ __forceinline__ float wave_min(float v)
-{
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) v = fminf(v, __shfl_xor(v, d, kWave));
-    return v;
 }
 
 // ---------------------------------------------------------------- launch arguments
@@ -356,13 +343,12 @@ void kkt_solve_kernel(const KernelArgs args)
     // ---- a5: epilogue
     bool factored = true;
     if (has_g) {
-        const float gmax = wave_max(valid ? gv : -__builtin_inff());
-        const float gmin = wave_min(valid ? gv : __builtin_inff());
-        factored = (gmax - gmin) <= kGateClamp;
         // reference: row 0's gate (always a valid row), so the factors of
-        // rows < L do not depend on L; with the spread <= 50 every factor
-        // lies in [e^-50, e^50]
-        const float gref = __shfl(gv, 0, kWave);
+        // rows < L do not depend on L.  If every valid row is within 25 of
+        // it, every pair differs by at most 50 (the clamp cannot bind) and
+        // every factor lies in [e^-25, e^25].
+        const float gref = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, gv)));
+        factored = __all(!valid || fabsf(gv - gref) <= 0.5f * kGateClamp);
         if (factored) {
             const float d = gv - gref;
             lds.row_scale[lane] = valid ? bv * __expf(d) : 0.0f;
@@ -517,17 +503,24 @@ void kkt_solve_kernel(const KernelArgs args)
     const f32x4 wt31 = mm16(A[3][1], xa[3], zero4);
     const f32x4 wt32 = mm16(A[3][2], xa[3], zero4);
 
-    // X_ij = 0 - sum(...): exact negation that turns an all-zero sum into +0.0
+    // X_ij = 0 - sum(...): exact negation that turns an all-zero sum into +0.0.
+    // The partial products that do not wait on this level's results are
+    // issued before each block-row store, so the MFMA pipe works through them
+    // while the store's LDS and memory instructions execute.
     const f32x4 x10 = zero4 - mm16(wt10, xd[0], zero4);
     const f32x4 x21 = zero4 - mm16(wt21, xd[1], zero4);
     const f32x4 x32 = zero4 - mm16(wt32, xd[2], zero4);
+    const f32x4 p20 = mm16(wt20, xd[0], zero4);
+    const f32x4 p31 = mm16(wt31, xd[1], zero4);
+    f32x4 p30 = mm16(wt30, xd[0], zero4);
     store_block_row(1, x10, xd[1], zero4, zero4);
 
-    const f32x4 x20 = zero4 - mm16(wt21, x10, mm16(wt20, xd[0], zero4));
-    const f32x4 x31 = zero4 - mm16(wt32, x21, mm16(wt31, xd[1], zero4));
+    const f32x4 x20 = zero4 - mm16(wt21, x10, p20);
+    const f32x4 x31 = zero4 - mm16(wt32, x21, p31);
+    p30 = mm16(wt31, x10, p30);
     store_block_row(2, x20, x21, xd[2], zero4);
 
-    const f32x4 x30 = zero4 - mm16(wt32, x20, mm16(wt31, x10, mm16(wt30, xd[0], zero4)));
+    const f32x4 x30 = zero4 - mm16(wt32, x20, p30);
     store_block_row(3, x30, x31, x32, xd[3]);
 }
 
