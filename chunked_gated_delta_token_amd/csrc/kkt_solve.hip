@@ -31,9 +31,11 @@
 //       of its own difference.
 //   a6  the four 16x16 unit-lower diagonal blocks inverted side by side by
 //       forward substitution: lane (block, column) keeps one column in
-//       VGPRs, row r needs rows < r only, all 15 steps unrolled (the pages'
-//       static row loop and side-by-side 16x16 blocks, PyPTO GatedDeltaRule
-//       case, sections 3.3.1, 3.3.2 and 3.4).
+//       VGPRs, all 15 steps unrolled (the pages' static row loop and
+//       side-by-side 16x16 blocks, PyPTO GatedDeltaRule case, sections 3.3.1,
+//       3.3.2 and 3.4).  The updates are right-looking (column p of A applied
+//       to every later row as soon as x[p] is final), so the dependent chain is
+//       one FMA per row.
 //   a7  the six off-diagonal 16x16 blocks, fp32 MFMA:
 //         W_ik = X_ii A_ik                      (all six independent)
 //         X_ij = -sum_{k=j}^{i-1} W_ik X_kj     (three dependency levels)
@@ -401,52 +403,63 @@ void kkt_solve_kernel(const KernelArgs args)
             }
         }
     }
-    // strict lower triangle inside the diagonal blocks, then to LDS for the solve
+    // strict lower triangle inside the diagonal blocks, stored transposed
+    // (blk[d][col][row]): lane (q, n) holds rows 4q..4q+3 of column n, one
+    // 16-byte write, and the solve below reads columns as contiguous rows
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+        f32x4 v;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) lds.blk[i][4 * q + r][m] = (4 * q + r > m) ? A[i][i][r] : 0.0f;
+        for (int r = 0; r < 4; ++r) v[r] = (4 * q + r > m) ? A[i][i][r] : 0.0f;
+        *reinterpret_cast<f32x4*>(&lds.blk[i][m][4 * q]) = v;
     }
     wave_lds_sync();
 
     // ---- a6: X_dd = (I + A_dd)^{-1}; lane (d = lane / 16, c = lane % 16)
-    // computes column c of X_dd: x[r] = [r == c] - sum_{p < r} A[r][p] x[p].
+    // computes column c of X_dd by right-looking forward substitution: once
+    // x[p] is final, every later row takes its term, acc[r] -= A[r][p] x[p].
+    // Each step's updates are independent of each other, so the dependent
+    // chain is one FMA per row; column p of A_dd is row p of the transposed
+    // block.  acc[r] starts at [r == c]; rows above c stay exactly 0.
     {
         const int d = lane / 16;
         const int c = lane % 16;
-        float x[16];
-        x[0] = (c == 0) ? 1.0f : 0.0f;
+        float acc[16];
 #pragma unroll
-        for (int r = 1; r < 16; ++r) {
-            float arow[16];
+        for (int r = 0; r < 16; ++r) acc[r] = (r == c) ? 1.0f : 0.0f;
 #pragma unroll
-            for (int u = 0; u < (r + 3) / 4; ++u) {
-                const f32x4 v = *reinterpret_cast<const f32x4*>(&lds.blk[d][r][4 * u]);
-                arow[4 * u + 0] = v[0];
-                arow[4 * u + 1] = v[1];
-                arow[4 * u + 2] = v[2];
-                arow[4 * u + 3] = v[3];
+        for (int p = 0; p < 15; ++p) {
+            float col[16];
+#pragma unroll
+            for (int u = (p + 1) / 4; u < 4; ++u) {
+                const f32x4 v = *reinterpret_cast<const f32x4*>(&lds.blk[d][p][4 * u]);
+                col[4 * u + 0] = v[0];
+                col[4 * u + 1] = v[1];
+                col[4 * u + 2] = v[2];
+                col[4 * u + 3] = v[3];
             }
-            float acc = (r == c) ? 1.0f : 0.0f;
 #pragma unroll
-            for (int p = 0; p < r; ++p) acc = __builtin_fmaf(-arow[p], x[p], acc);
-            x[r] = acc;
+            for (int r = p + 1; r < 16; ++r) acc[r] = __builtin_fmaf(-col[r], acc[p], acc[r]);
         }
         wave_lds_sync();  // every read of A_dd precedes the overwrite with X_dd
+        // X_dd stored transposed as well: column c is contiguous
 #pragma unroll
-        for (int r = 0; r < 16; ++r) lds.blk[d][r][c] = x[r];
+        for (int u = 0; u < 4; ++u) {
+            const f32x4 v = {acc[4 * u], acc[4 * u + 1], acc[4 * u + 2], acc[4 * u + 3]};
+            *reinterpret_cast<f32x4*>(&lds.blk[d][c][4 * u]) = v;
+        }
     }
     wave_lds_sync();
 
-    // X_dd in both operand layouts:
+    // X_dd in both operand layouts (blk[d][col][row] = X_dd[row][col]):
     //   xa[d]: lane (q, m) holds X_dd[m][4q .. 4q+3]   (left operand)
     //   xd[d]: lane (q, n) holds X_dd[4q .. 4q+3][n]   (right operand / result layout)
     f32x4 xa[4], xd[4];
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-        xa[d] = *reinterpret_cast<const f32x4*>(&lds.blk[d][m][4 * q]);
+        xd[d] = *reinterpret_cast<const f32x4*>(&lds.blk[d][m][4 * q]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) xd[d][r] = lds.blk[d][4 * q + r][m];
+        for (int r = 0; r < 4; ++r) xa[d][r] = lds.blk[d][4 * q + r][m];
     }
 
     // ---- a8 helper: stage one 16-row block row and write full output rows
