@@ -108,27 +108,23 @@ template <> struct EltInfo<Elt::F32> { using storage = float; static constexpr i
 template <> struct EltInfo<Elt::BF16> { using storage = uint16_t; static constexpr int bytes = 2; };
 template <> struct EltInfo<Elt::F16> { using storage = uint16_t; static constexpr int bytes = 2; };
 
-// fp32 -> bf16 bits, round to nearest even (the inputs are never NaN here).
-__device__ __forceinline__ uint32_t bf16_bits_rne(float x)
-{
-    const uint32_t u = __builtin_bit_cast(uint32_t, x);
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
-__device__ __forceinline__ uint32_t f16_bits_rne(float x)
-{
-    const _Float16 h = (_Float16)x;  // v_cvt_f16_f32 under the default round-to-nearest-even mode
-    return (uint32_t)__builtin_bit_cast(uint16_t, h);
-}
+// Two fp32 values -> packed 16-bit pair (low half first), rounded to nearest
+// even by the hardware converts (v_cvt_pk_bf16_f32 / v_cvt_pk_f16_f32 under
+// the default round-to-nearest-even mode).
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 template <Elt E> __device__ __forceinline__ uint32_t pack2(float lo, float hi);
 template <> __device__ __forceinline__ uint32_t pack2<Elt::BF16>(float lo, float hi)
 {
-    return bf16_bits_rne(lo) | (bf16_bits_rne(hi) << 16);
+    const f32x2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 template <> __device__ __forceinline__ uint32_t pack2<Elt::F16>(float lo, float hi)
 {
-    return f16_bits_rne(lo) | (f16_bits_rne(hi) << 16);
+    const f32x2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
 }
 
 // ---------------------------------------------------------------- MFMA helpers
@@ -639,6 +635,14 @@ extern "C" kkt_status_t kkt_solve(const void* k, const float* g, const float* be
     }
     if (T == 0) return KKT_OK;
     if (k == nullptr || out == nullptr) return fail(KKT_ERR_INVALID_ARGUMENT, "k and out must not be NULL");
+    // the kernel moves k and out in 16-byte vectors, g / beta / cu_seqlens in 4-byte words
+    if ((reinterpret_cast<uintptr_t>(k) & 15u) != 0 || (reinterpret_cast<uintptr_t>(out) & 15u) != 0) {
+        return fail(KKT_ERR_INVALID_ARGUMENT, "k and out must be 16-byte aligned");
+    }
+    if ((reinterpret_cast<uintptr_t>(g) & 3u) != 0 || (reinterpret_cast<uintptr_t>(beta) & 3u) != 0 ||
+        (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0) {
+        return fail(KKT_ERR_INVALID_ARGUMENT, "g, beta and cu_seqlens must be 4-byte aligned");
+    }
 
     // 32-bit in-tile offsets: 64 rows of one head must span < 2 GiB
     const int64_t k_row_bytes = H * K * dtype_bytes(in_dtype);

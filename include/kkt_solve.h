@@ -80,6 +80,9 @@ typedef enum {
  *              sequences).  Must not overlap any input.
  *   stream     HIP stream the kernel is enqueued on (NULL: the null stream).
  *
+ * Alignment: k and out 16-byte aligned; g, beta and cu_seqlens 4-byte aligned
+ * (KKT_ERR_INVALID_ARGUMENT otherwise).
+ *
  * All pointers are owned by the caller; the library allocates nothing and
  * keeps no pointer after the call returns.  The call is asynchronous: it
  * returns once the kernel is enqueued, and faults during execution surface at

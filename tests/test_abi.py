@@ -51,8 +51,8 @@ def test_version(lib):
 
 
 def _call(lib, **over):
-    args = dict(k=1, g=None, beta=None, cu=None, num_seqs=0, B=1, T=64, H=1, K=128, chunk_size=64,
-                in_dtype=1, out_dtype=0, out=1, stream=None)
+    args = dict(k=16, g=None, beta=None, cu=None, num_seqs=0, B=1, T=64, H=1, K=128, chunk_size=64,
+                in_dtype=1, out_dtype=0, out=16, stream=None)
     args.update(over)
     return lib.kkt_solve(args["k"], args["g"], args["beta"], args["cu"], args["num_seqs"], args["B"],
                          args["T"], args["H"], args["K"], args["chunk_size"], args["in_dtype"],
@@ -73,6 +73,11 @@ def _call(lib, **over):
     (dict(cu=1, num_seqs=0), 1, "cu_seqlens"),
     (dict(k=None), 1, "NULL"),
     (dict(out=None), 1, "NULL"),
+    (dict(k=16 + 2), 1, "16-byte aligned"),
+    (dict(out=64 + 8), 1, "16-byte aligned"),
+    (dict(g=16 + 2), 1, "4-byte aligned"),
+    (dict(beta=16 + 1), 1, "4-byte aligned"),
+    (dict(cu=16 + 2, num_seqs=1), 1, "4-byte aligned"),
 ])
 def test_invalid_arguments_rejected_on_host(lib, over, status, msg):
     from chunked_gated_delta_token_amd import kkt

@@ -311,3 +311,17 @@ def test_error_paths(kkt):
                                args["chunk_size"], args["in_dtype"], 0, out.data_ptr(), None)
         assert st == status, (kwargs, st, kkt.last_error())
         assert kkt.last_error()
+
+
+@pytest.mark.parametrize("out_dtype", ["bf16", "f16"])
+def test_16bit_output_is_rne_of_fp32_output(kkt, out_dtype):
+    """The 16-bit outputs are the kernel's own fp32 results rounded to nearest
+    even, bit for bit (same inputs, same arithmetic up to the store)."""
+    inp = W.generate("T256_H8_bf16_f32", B=2, T=300, H=5, seed=650)
+    f32 = run_gpu(kkt, inp, "f32")
+    got = run_gpu(kkt, inp, out_dtype)
+    if out_dtype == "bf16":
+        exp = oracle.round_to_bf16_bits(f32.astype(np.float64))
+    else:
+        exp = f32.astype(np.float16).view(np.uint16)
+    assert np.array_equal(got, exp), int(np.sum(got != exp))
