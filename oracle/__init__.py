@@ -60,6 +60,11 @@ def _load():
                                      ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                      ctypes.c_int64, ctypes.c_int, dp]
     lib.kkt_oracle_solve.restype = ctypes.c_int
+    lib.kkt_oracle_scaled_dot.argtypes = lib.kkt_oracle_solve.argtypes
+    lib.kkt_oracle_scaled_dot.restype = ctypes.c_int
+    lib.kkt_oracle_solve_tril.argtypes = [dp, ip, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                          ctypes.c_int64, ctypes.c_int64, dp]
+    lib.kkt_oracle_solve_tril.restype = ctypes.c_int
     lib.kkt_oracle_num_threads.argtypes = []
     lib.kkt_oracle_num_threads.restype = ctypes.c_int
     _lib = lib
@@ -77,15 +82,7 @@ def _ptr(a, ctype):
     return a.ctypes.data_as(ctypes.POINTER(ctype))
 
 
-def kkt_solve_ref(k, g=None, beta=None, cu_seqlens=None, chunk_size: int = 64,
-                  clamp_gate: bool = True) -> np.ndarray:
-    """Exact (fp64) rows of (I + A)^{-1} per chunk, shape [B, T, H, chunk_size].
-
-    ``k`` [B,T,H,K], ``g`` / ``beta`` [B,T,H] (or None), ``cu_seqlens`` int
-    [N+1] (or None; then B must be 1 for varlen).  Any real dtype is accepted;
-    values are widened to fp64 (exact for fp32, fp16 and bf16 values).
-    ``clamp_gate`` clamps g_i - g_j to [-50, 50] before exp, as the pages do.
-    """
+def _kkt_call(fn_name, k, g, beta, cu_seqlens, chunk_size, clamp_gate):
     lib = _load()
     k64 = np.ascontiguousarray(k, dtype=np.float64)
     if k64.ndim != 4:
@@ -96,19 +93,57 @@ def kkt_solve_ref(k, g=None, beta=None, cu_seqlens=None, chunk_size: int = 64,
     for name, a in (("g", g64), ("beta", b64)):
         if a is not None and a.shape != (B, T, H):
             raise ValueError(f"{name} must be [B,T,H]={B, T, H}, got {a.shape}")
-    cu = None
-    num_seqs = 0
-    if cu_seqlens is not None:
-        cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
-        num_seqs = cu.shape[0] - 1
+    cu, num_seqs = _cu(cu_seqlens)
     out = np.empty((B, T, H, chunk_size), dtype=np.float64)
-    rc = lib.kkt_oracle_solve(_ptr(k64, ctypes.c_double), _ptr(g64, ctypes.c_double),
-                              _ptr(b64, ctypes.c_double), _ptr(cu, ctypes.c_int32), num_seqs,
-                              B, T, H, K, chunk_size, 1 if clamp_gate else 0,
-                              _ptr(out, ctypes.c_double))
+    rc = getattr(lib, fn_name)(_ptr(k64, ctypes.c_double), _ptr(g64, ctypes.c_double),
+                               _ptr(b64, ctypes.c_double), _ptr(cu, ctypes.c_int32), num_seqs,
+                               B, T, H, K, chunk_size, 1 if clamp_gate else 0, _ptr(out, ctypes.c_double))
     if rc != 0:
-        raise ValueError(f"kkt_oracle_solve failed with code {rc}")
+        raise ValueError(f"{fn_name} failed with code {rc}")
     return out
+
+
+def _cu(cu_seqlens):
+    if cu_seqlens is None:
+        return None, 0
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    return cu, cu.shape[0] - 1
+
+
+def scaled_dot_ref(k, g=None, beta=None, cu_seqlens=None, chunk_size: int = 64,
+                   clamp_gate: bool = True) -> np.ndarray:
+    """The first step alone: per chunk the strictly lower A (fp64), row
+    t0+i holding A[i][0..chunk_size-1], zeros on and above the diagonal."""
+    return _kkt_call("kkt_oracle_scaled_dot", k, g, beta, cu_seqlens, chunk_size, clamp_gate)
+
+
+def solve_tril_ref(A, cu_seqlens=None, chunk_size: int = 64) -> np.ndarray:
+    """The second step alone: rows of (I + strict_lower(A_chunk))^{-1} per
+    chunk; A's diagonal and upper entries are ignored."""
+    lib = _load()
+    a64 = np.ascontiguousarray(A, dtype=np.float64)
+    if a64.ndim != 4 or a64.shape[3] != chunk_size:
+        raise ValueError("A must be [B,T,H,chunk_size]")
+    B, T, H, _ = a64.shape
+    cu, num_seqs = _cu(cu_seqlens)
+    out = np.empty_like(a64)
+    rc = lib.kkt_oracle_solve_tril(_ptr(a64, ctypes.c_double), _ptr(cu, ctypes.c_int32), num_seqs,
+                                   B, T, H, chunk_size, _ptr(out, ctypes.c_double))
+    if rc != 0:
+        raise ValueError(f"kkt_oracle_solve_tril failed with code {rc}")
+    return out
+
+
+def kkt_solve_ref(k, g=None, beta=None, cu_seqlens=None, chunk_size: int = 64,
+                  clamp_gate: bool = True) -> np.ndarray:
+    """Exact (fp64) rows of (I + A)^{-1} per chunk, shape [B, T, H, chunk_size].
+
+    ``k`` [B,T,H,K], ``g`` / ``beta`` [B,T,H] (or None), ``cu_seqlens`` int
+    [N+1] (or None; then B must be 1 for varlen).  Any real dtype is accepted;
+    values are widened to fp64 (exact for fp32, fp16 and bf16 values).
+    ``clamp_gate`` clamps g_i - g_j to [-50, 50] before exp, as the pages do.
+    """
+    return _kkt_call("kkt_oracle_solve", k, g, beta, cu_seqlens, chunk_size, clamp_gate)
 
 
 def round_to_bf16_bits(x: np.ndarray) -> np.ndarray:

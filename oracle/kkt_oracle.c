@@ -35,6 +35,9 @@
  *
  *   g == NULL means no gate (factor 1); beta == NULL means beta_i = 1.
  *
+ * The two steps of the unfused chain are also exposed on their own
+ * (kkt_oracle_scaled_dot: A; kkt_oracle_solve_tril: (I + A)^{-1} from A).
+ *
  * The inverse is taken by generic Gauss-Jordan elimination with partial
  * pivoting on the augmented matrix [M | I].  It deliberately does not use the
  * fact that M is unit lower triangular, so that it is an independent route to
@@ -185,6 +188,63 @@ int kkt_oracle_num_threads(void)
 #endif
 }
 
+/* The chunks of a call, in order: batch row or sequence, then position. */
+typedef struct {
+    int64_t n;
+    int64_t* b;
+    int64_t* t0;
+    int64_t* len;
+} chunk_list;
+
+static void free_chunks(chunk_list* c)
+{
+    free(c->b);
+    free(c->t0);
+    free(c->len);
+}
+
+static int check_and_list_chunks(const int32_t* cu_seqlens, int64_t num_seqs, int64_t B, int64_t T,
+                                 int64_t H, int64_t chunk_size, chunk_list* out)
+{
+    out->n = 0;
+    out->b = out->t0 = out->len = NULL;
+    if (B < 1 || T < 0 || H < 1 || chunk_size < 1) return KKT_ORACLE_BAD_ARGUMENT;
+    if (cu_seqlens != NULL) {
+        if (B != 1 || num_seqs < 1 || cu_seqlens[0] != 0 || cu_seqlens[num_seqs] != T) {
+            return KKT_ORACLE_BAD_ARGUMENT;
+        }
+        for (int64_t s = 0; s < num_seqs; ++s) {
+            if (cu_seqlens[s + 1] < cu_seqlens[s]) return KKT_ORACLE_BAD_ARGUMENT;
+        }
+    }
+    const int64_t n_rows = (cu_seqlens != NULL) ? num_seqs : B;
+    int64_t n_chunks = 0;
+    for (int64_t s = 0; s < n_rows; ++s) {
+        const int64_t len = (cu_seqlens != NULL) ? (int64_t)cu_seqlens[s + 1] - cu_seqlens[s] : T;
+        n_chunks += (len + chunk_size - 1) / chunk_size;
+    }
+    out->b = (int64_t*)malloc(sizeof(int64_t) * (size_t)(n_chunks + 1));
+    out->t0 = (int64_t*)malloc(sizeof(int64_t) * (size_t)(n_chunks + 1));
+    out->len = (int64_t*)malloc(sizeof(int64_t) * (size_t)(n_chunks + 1));
+    if (out->b == NULL || out->t0 == NULL || out->len == NULL) {
+        free_chunks(out);
+        return KKT_ORACLE_NO_MEMORY;
+    }
+    int64_t n = 0;
+    for (int64_t s = 0; s < n_rows; ++s) {
+        const int64_t bos = (cu_seqlens != NULL) ? cu_seqlens[s] : 0;
+        const int64_t eos = (cu_seqlens != NULL) ? cu_seqlens[s + 1] : T;
+        for (int64_t t0 = bos; t0 < eos; t0 += chunk_size) {
+            out->b[n] = (cu_seqlens != NULL) ? 0 : s;
+            out->t0[n] = t0;
+            out->len[n] = (eos - t0 < chunk_size) ? (eos - t0) : chunk_size;
+            ++n;
+        }
+    }
+    out->n = n;
+    return KKT_ORACLE_OK;
+}
+
 /*
  * Full oracle.
  *   k          [B,T,H,K] fp64, contiguous
@@ -200,48 +260,12 @@ int kkt_oracle_solve(const double* k, const double* g, const double* beta,
                      int64_t B, int64_t T, int64_t H, int64_t K,
                      int64_t chunk_size, int clamp_gate, double* out)
 {
-    if (k == NULL || out == NULL || B < 1 || T < 0 || H < 1 || K < 1 || chunk_size < 1) {
-        return KKT_ORACLE_BAD_ARGUMENT;
-    }
-    if (cu_seqlens != NULL) {
-        if (B != 1 || num_seqs < 1 || cu_seqlens[0] != 0 || cu_seqlens[num_seqs] != T) {
-            return KKT_ORACLE_BAD_ARGUMENT;
-        }
-        for (int64_t s = 0; s < num_seqs; ++s) {
-            if (cu_seqlens[s + 1] < cu_seqlens[s]) return KKT_ORACLE_BAD_ARGUMENT;
-        }
-    }
+    if (k == NULL || out == NULL || K < 1) return KKT_ORACLE_BAD_ARGUMENT;
+    chunk_list ch;
+    int status = check_and_list_chunks(cu_seqlens, num_seqs, B, T, H, chunk_size, &ch);
+    if (status != KKT_ORACLE_OK) return status;
 
-    /* List the chunks: (b, t0, L). */
-    int64_t n_chunks = 0;
-    const int64_t n_seq_rows = (cu_seqlens != NULL) ? num_seqs : B;
-    for (int64_t s = 0; s < n_seq_rows; ++s) {
-        const int64_t len = (cu_seqlens != NULL) ? (int64_t)cu_seqlens[s + 1] - cu_seqlens[s] : T;
-        n_chunks += (len + chunk_size - 1) / chunk_size;
-    }
-    int64_t* chunk_b = (int64_t*)malloc(sizeof(int64_t) * (size_t)(n_chunks + 1));
-    int64_t* chunk_t0 = (int64_t*)malloc(sizeof(int64_t) * (size_t)(n_chunks + 1));
-    int64_t* chunk_len = (int64_t*)malloc(sizeof(int64_t) * (size_t)(n_chunks + 1));
-    if (chunk_b == NULL || chunk_t0 == NULL || chunk_len == NULL) {
-        free(chunk_b);
-        free(chunk_t0);
-        free(chunk_len);
-        return KKT_ORACLE_NO_MEMORY;
-    }
-    int64_t n = 0;
-    for (int64_t s = 0; s < n_seq_rows; ++s) {
-        const int64_t bos = (cu_seqlens != NULL) ? cu_seqlens[s] : 0;
-        const int64_t eos = (cu_seqlens != NULL) ? cu_seqlens[s + 1] : T;
-        for (int64_t t0 = bos; t0 < eos; t0 += chunk_size) {
-            chunk_b[n] = (cu_seqlens != NULL) ? 0 : s;
-            chunk_t0[n] = t0;
-            chunk_len[n] = (eos - t0 < chunk_size) ? (eos - t0) : chunk_size;
-            ++n;
-        }
-    }
-
-    const int64_t n_tiles = n_chunks * H;
-    int status = KKT_ORACLE_OK;
+    const int64_t n_tiles = ch.n * H;
 #pragma omp parallel
     {
         const int64_t cs = chunk_size;
@@ -255,8 +279,8 @@ int kkt_oracle_solve(const double* k, const double* g, const double* beta,
             if (local != KKT_ORACLE_OK) continue;
             const int64_t c = tile / H;
             const int64_t h = tile % H;
-            const int rc = solve_chunk(k, g, beta, T, H, K, chunk_size, chunk_b[c], h,
-                                       chunk_t0[c], chunk_len[c], clamp_gate, out, A, M, X, W);
+            const int rc = solve_chunk(k, g, beta, T, H, K, chunk_size, ch.b[c], h,
+                                       ch.t0[c], ch.len[c], clamp_gate, out, A, M, X, W);
             if (rc != KKT_ORACLE_OK) local = rc;
         }
         if (local != KKT_ORACLE_OK) {
@@ -268,8 +292,104 @@ int kkt_oracle_solve(const double* k, const double* g, const double* beta,
         free(X);
         free(W);
     }
-    free(chunk_b);
-    free(chunk_t0);
-    free(chunk_len);
+    free_chunks(&ch);
+    return status;
+}
+
+/*
+ * First step of the unfused chain alone (the pages' chunk_scaled_dot_kkt_fwd,
+ * named in the PR #135 description): the strictly lower matrix A of every
+ * chunk, row t0+i of A_out holding A[i][0 .. chunk_size-1] (0 for j >= i).
+ * Arguments as for kkt_oracle_solve; A_out is [B,T,H,chunk_size] fp64.
+ */
+int kkt_oracle_scaled_dot(const double* k, const double* g, const double* beta,
+                          const int32_t* cu_seqlens, int64_t num_seqs,
+                          int64_t B, int64_t T, int64_t H, int64_t K,
+                          int64_t chunk_size, int clamp_gate, double* A_out)
+{
+    if (k == NULL || A_out == NULL || K < 1) return KKT_ORACLE_BAD_ARGUMENT;
+    chunk_list ch;
+    int status = check_and_list_chunks(cu_seqlens, num_seqs, B, T, H, chunk_size, &ch);
+    if (status != KKT_ORACLE_OK) return status;
+    const int64_t n_tiles = ch.n * H;
+#pragma omp parallel
+    {
+        const int64_t cs = chunk_size;
+        double* A = (double*)malloc(sizeof(double) * (size_t)(cs * cs));
+        int local = A ? KKT_ORACLE_OK : KKT_ORACLE_NO_MEMORY;
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t tile = 0; tile < n_tiles; ++tile) {
+            if (local != KKT_ORACLE_OK) continue;
+            const int64_t c = tile / H;
+            const int64_t h = tile % H;
+            const int64_t L = ch.len[c];
+            build_chunk_matrix(k, g, beta, T, H, K, ch.b[c], h, ch.t0[c], L, clamp_gate, A);
+            for (int64_t i = 0; i < L; ++i) {
+                double* row = A_out + ((ch.b[c] * T + ch.t0[c] + i) * H + h) * chunk_size;
+                for (int64_t j = 0; j < chunk_size; ++j) row[j] = (j < L) ? A[i * L + j] : 0.0;
+            }
+        }
+        if (local != KKT_ORACLE_OK) {
+#pragma omp critical
+            status = local;
+        }
+        free(A);
+    }
+    free_chunks(&ch);
+    return status;
+}
+
+/*
+ * Second step alone (the pages' solve_tril): reads per chunk the strictly
+ * lower part of A (A_in[t0+i][h][j] for j < i; the diagonal and everything
+ * above it are ignored) and writes the rows of (I + A)^{-1}, inverted by the
+ * same generic Gauss-Jordan elimination.  A_in and out are
+ * [B,T,H,chunk_size] fp64.
+ */
+int kkt_oracle_solve_tril(const double* A_in, const int32_t* cu_seqlens, int64_t num_seqs,
+                          int64_t B, int64_t T, int64_t H, int64_t chunk_size, double* out)
+{
+    if (A_in == NULL || out == NULL) return KKT_ORACLE_BAD_ARGUMENT;
+    chunk_list ch;
+    int status = check_and_list_chunks(cu_seqlens, num_seqs, B, T, H, chunk_size, &ch);
+    if (status != KKT_ORACLE_OK) return status;
+    const int64_t n_tiles = ch.n * H;
+#pragma omp parallel
+    {
+        const int64_t cs = chunk_size;
+        double* M = (double*)malloc(sizeof(double) * (size_t)(cs * cs));
+        double* X = (double*)malloc(sizeof(double) * (size_t)(cs * cs));
+        double* W = (double*)malloc(sizeof(double) * (size_t)(2 * cs * cs));
+        int local = (M && X && W) ? KKT_ORACLE_OK : KKT_ORACLE_NO_MEMORY;
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t tile = 0; tile < n_tiles; ++tile) {
+            if (local != KKT_ORACLE_OK) continue;
+            const int64_t c = tile / H;
+            const int64_t h = tile % H;
+            const int64_t L = ch.len[c];
+            for (int64_t i = 0; i < L; ++i) {
+                const double* arow = A_in + ((ch.b[c] * T + ch.t0[c] + i) * H + h) * chunk_size;
+                for (int64_t j = 0; j < L; ++j) {
+                    M[i * L + j] = (i == j) ? 1.0 : ((j < i) ? arow[j] : 0.0);
+                }
+            }
+            if (gauss_jordan_inverse(L, M, X, W) != 0) {
+                local = KKT_ORACLE_SINGULAR;
+                continue;
+            }
+            for (int64_t i = 0; i < L; ++i) {
+                double* row = out + ((ch.b[c] * T + ch.t0[c] + i) * H + h) * chunk_size;
+                for (int64_t j = 0; j < chunk_size; ++j) row[j] = (j < L) ? X[i * L + j] : 0.0;
+            }
+        }
+        if (local != KKT_ORACLE_OK) {
+#pragma omp critical
+            status = local;
+        }
+        free(M);
+        free(X);
+        free(W);
+    }
+    free_chunks(&ch);
     return status;
 }

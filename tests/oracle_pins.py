@@ -362,3 +362,65 @@ ALL_PINS = [
     pin_prefix,
     pin_neutral_gate_beta,
 ]
+
+
+# --------------------------------------------------------------------------
+# The two steps of the unfused chain on their own.  These pins take
+# (solve, scaled_dot, solve_tril).
+# --------------------------------------------------------------------------
+def split_pin_golden_A(solve, scaled_dot, solve_tril):
+    with open(GOLDEN) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        k = np.array(c["k"], dtype=np.float64)
+        T, K = k.shape
+        k = k.reshape(1, T, 1, K)
+        beta = None if c["beta"] is None else np.array(c["beta"]).reshape(1, T, 1)
+        g = None if c["g"] is None else np.array(c["g"]).reshape(1, T, 1)
+        cu = None if c["cu_seqlens"] is None else np.array(c["cu_seqlens"], dtype=np.int32)
+        A = scaled_dot(k, g, beta, cu)
+        for t, row in enumerate(c["expected_A_rows"]):
+            exp = np.zeros(CH)
+            exp[:len(row)] = row
+            tol = c.get("tol", 0.0) + c.get("tol_rel", 0.0) * np.abs(exp)
+            assert np.all(np.abs(A[0, t, 0] - exp) <= tol), (c["name"], t, A[0, t, 0, :4])
+
+
+def split_pin_solve_tril_library_inverse(solve, scaled_dot, solve_tril):
+    """Random strictly lower A against numpy.linalg.inv(I + A), chunk by chunk;
+    whatever sits on or above A's diagonal is ignored."""
+    rng = np.random.default_rng(40)
+    B, T, H = 2, 150, 3
+    A = rng.uniform(-0.3, 0.3, (B, T, H, CH))
+    garbage = A.copy()
+    for t in range(T):
+        i = t % CH
+        A[:, t, :, i:] = 0.0
+        garbage[:, t, :, i:] = rng.uniform(-50, 50, (B, H, CH - i))
+    X = solve_tril(A)
+    assert np.array_equal(solve_tril(garbage), X)
+    for b in range(B):
+        for h in range(H):
+            for t0 in range(0, T, CH):
+                L = min(CH, T - t0)
+                ref = np.linalg.inv(np.eye(L) + A[b, t0:t0 + L, h, :L])
+                got = X[b, t0:t0 + L, h, :L]
+                assert np.max(np.abs(got - ref)) <= 1e-13 * max(1.0, np.max(np.abs(ref)))
+                assert np.all(X[b, t0:t0 + L, h, L:] == 0.0)
+
+
+def split_pin_composition(solve, scaled_dot, solve_tril):
+    """solve_tril(scaled_dot(x)) is the fused result, bit for bit, also for
+    packed sequences (the pages' fused op equals the two-step chain)."""
+    rng = np.random.default_rng(41)
+    lens = [70, 1, 0, 129, 3]
+    T, H, K = sum(lens), 2, 16
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    k = _unit_keys(rng, 1, T, H, K)
+    beta = rng.uniform(0.1, 0.9, (1, T, H))
+    g = -np.cumsum(rng.uniform(0, 0.1, (1, T, H)), axis=1)
+    for cu_ in (None, cu):
+        assert np.array_equal(solve_tril(scaled_dot(k, g, beta, cu_), cu_), solve(k, g, beta, cu_))
+
+
+SPLIT_PINS = [split_pin_golden_A, split_pin_solve_tril_library_inverse, split_pin_composition]

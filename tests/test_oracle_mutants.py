@@ -28,17 +28,23 @@ MUTANTS = [
     ("diagonal_in_A", "for (int64_t j = 0; j < i; ++j) {\n            const int64_t tj",
      "for (int64_t j = 0; j <= i; ++j) {\n            const int64_t tj"),
     ("minus_A", "((i == j) ? 1.0 : 0.0) + A[i * L + j]", "((i == j) ? 1.0 : 0.0) - A[i * L + j]"),
-    ("transposed_output", "row[j] = (j < L) ? X[i * L + j] : 0.0;", "row[j] = (j < L) ? X[j * L + i] : 0.0;"),
+    ("transposed_output", "            row[j] = (j < L) ? X[i * L + j] : 0.0;\n        }\n    }\n    return KKT_ORACLE_OK;",
+     "            row[j] = (j < L) ? X[j * L + i] : 0.0;\n        }\n    }\n    return KKT_ORACLE_OK;"),
     ("elimination_sign", "W[r * w + x] -= f * W[c * w + x];", "W[r * w + x] += f * W[c * w + x];"),
     ("clamp_bound_5", "static const double GATE_CLAMP = 50.0;", "static const double GATE_CLAMP = 5.0;"),
     ("no_clamp", "if (clamp_gate) {\n                    if (d > GATE_CLAMP)",
      "if (0) {\n                    if (d > GATE_CLAMP)"),
     ("gate_of_wrong_token", "double d = g[ti] - g[tj];", "double d = g[ti] - g[tj + (j > 0 ? -H : 0)];"),
     # chunk length taken from the full T instead of the sequence end
-    ("sequence_end_uses_T", "chunk_len[n] = (eos - t0 < chunk_size) ? (eos - t0) : chunk_size;",
-     "chunk_len[n] = (T - t0 < chunk_size) ? (T - t0) : chunk_size;"),
+    ("sequence_end_uses_T", "out->len[n] = (eos - t0 < chunk_size) ? (eos - t0) : chunk_size;",
+     "out->len[n] = (T - t0 < chunk_size) ? (T - t0) : chunk_size;"),
     # chunk starts snapped to the global 64-token grid instead of the sequence start
-    ("chunks_ignore_sequence_start", "chunk_t0[n] = t0;", "chunk_t0[n] = t0 - bos % chunk_size;"),
+    ("chunks_ignore_sequence_start", "out->t0[n] = t0;", "out->t0[n] = t0 - bos % chunk_size;"),
+    # the split steps: A written transposed; solve_tril reading A's upper part
+    ("scaled_dot_transposed", "for (int64_t j = 0; j < chunk_size; ++j) row[j] = (j < L) ? A[i * L + j] : 0.0;",
+     "for (int64_t j = 0; j < chunk_size; ++j) row[j] = (j < L) ? A[j * L + i] : 0.0;"),
+    ("solve_tril_reads_upper", "M[i * L + j] = (i == j) ? 1.0 : ((j < i) ? arow[j] : 0.0);",
+     "M[i * L + j] = (i == j) ? 1.0 : arow[j];"),
     ("key_of_previous_token", "const double* kj = k + tj * K;", "const double* kj = k + (tj >= H ? tj - H : tj) * K;"),
 ]
 
@@ -56,12 +62,50 @@ def _build(src_text, tmpdir, name):
     lib.kkt_oracle_solve.argtypes = [dp, dp, dp, ip, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                      ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, dp]
     lib.kkt_oracle_solve.restype = ctypes.c_int
+    lib.kkt_oracle_scaled_dot.argtypes = lib.kkt_oracle_solve.argtypes
+    lib.kkt_oracle_scaled_dot.restype = ctypes.c_int
+    lib.kkt_oracle_solve_tril.argtypes = [dp, ip, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                          ctypes.c_int64, ctypes.c_int64, dp]
+    lib.kkt_oracle_solve_tril.restype = ctypes.c_int
     return lib
 
 
+def _ptr(a, t):
+    return None if a is None else a.ctypes.data_as(ctypes.POINTER(t))
+
+
+def _split(lib):
+    def scaled_dot(k, g=None, beta=None, cu=None, chunk_size=64):
+        k = np.ascontiguousarray(k, dtype=np.float64)
+        B, T, H, K = k.shape
+        g = None if g is None else np.ascontiguousarray(g, dtype=np.float64)
+        beta = None if beta is None else np.ascontiguousarray(beta, dtype=np.float64)
+        cu = None if cu is None else np.ascontiguousarray(cu, dtype=np.int32)
+        out = np.empty((B, T, H, chunk_size))
+        rc = lib.kkt_oracle_scaled_dot(_ptr(k, ctypes.c_double), _ptr(g, ctypes.c_double),
+                                       _ptr(beta, ctypes.c_double), _ptr(cu, ctypes.c_int32),
+                                       0 if cu is None else len(cu) - 1, B, T, H, K, chunk_size, 1,
+                                       _ptr(out, ctypes.c_double))
+        if rc != 0:
+            raise ValueError(rc)
+        return out
+
+    def solve_tril(A, cu=None, chunk_size=64):
+        A = np.ascontiguousarray(A, dtype=np.float64)
+        B, T, H, _ = A.shape
+        cu = None if cu is None else np.ascontiguousarray(cu, dtype=np.int32)
+        out = np.empty_like(A)
+        rc = lib.kkt_oracle_solve_tril(_ptr(A, ctypes.c_double), _ptr(cu, ctypes.c_int32),
+                                       0 if cu is None else len(cu) - 1, B, T, H, chunk_size,
+                                       _ptr(out, ctypes.c_double))
+        if rc != 0:
+            raise ValueError(rc)
+        return out
+    return scaled_dot, solve_tril
+
+
 def _solver(lib):
-    def ptr(a, t):
-        return None if a is None else a.ctypes.data_as(ctypes.POINTER(t))
+    ptr = _ptr
 
     def solve(k, g=None, beta=None, cu=None, chunk_size=64, clamp_gate=True):
         k = np.ascontiguousarray(k, dtype=np.float64)
@@ -87,9 +131,12 @@ def tmpdir():
 
 def test_unmutated_copy_passes(tmpdir):
     with open(SRC) as f:
-        solve = _solver(_build(f.read(), tmpdir, "clean"))
+        lib = _build(f.read(), tmpdir, "clean")
+    solve = _solver(lib)
     for pin in oracle_pins.ALL_PINS:
         pin(solve)
+    for pin in oracle_pins.SPLIT_PINS:
+        pin(solve, *_split(lib))
 
 
 @pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
@@ -97,11 +144,18 @@ def test_mutant_is_caught(tmpdir, name, old, new):
     with open(SRC) as f:
         text = f.read()
     assert text.count(old) == 1, f"mutation site for {name} not found exactly once"
-    solve = _solver(_build(text.replace(old, new), tmpdir, name))
+    lib = _build(text.replace(old, new), tmpdir, name)
+    solve = _solver(lib)
+    scaled_dot, solve_tril = _split(lib)
     caught = []
     for pin in oracle_pins.ALL_PINS:
         try:
             pin(solve)
+        except (AssertionError, ValueError, IndexError, FloatingPointError):
+            caught.append(pin.__name__)
+    for pin in oracle_pins.SPLIT_PINS:
+        try:
+            pin(solve, scaled_dot, solve_tril)
         except (AssertionError, ValueError, IndexError, FloatingPointError):
             caught.append(pin.__name__)
     assert caught, f"mutant {name} passed every pin"

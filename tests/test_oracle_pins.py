@@ -16,6 +16,12 @@ def test_pin(pin):
     pin(_solve)
 
 
+@pytest.mark.parametrize("pin", oracle_pins.SPLIT_PINS, ids=lambda f: f.__name__)
+def test_split_pin(pin):
+    pin(_solve, lambda k, g, b, cu: oracle.scaled_dot_ref(k, g, b, cu),
+        lambda A, cu=None: oracle.solve_tril_ref(A, cu))
+
+
 def test_clamp_flag_is_the_pure_definition_when_off():
     # with the clamp off, a gate difference of 60 is exp(60)
     k = np.ones((1, 2, 1, 1))
