@@ -1,6 +1,6 @@
 """Benchmark of the fused chunk-local KKT + triangular solve on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload NAME]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload NAME] [--op OP]
 
 One step = one call of the fused op (the whole hot path: tile map, K load,
 Gram, gate/beta epilogue, diagonal solve, block merge, store) over one batch
@@ -9,6 +9,11 @@ bf16 keys and fp32 output.  Inputs are resident in HBM before the timed
 region starts.  Successive steps rotate over R copies of the input and output
 buffers whose total size exceeds twice the 256 MB Infinity Cache, so every
 step reads its keys from HBM.
+
+--op picks what one step is: the fused op (default), or one step of the
+unfused two-step chain on its own (scaled_dot: k, g, beta -> A in fp32;
+solve_tril: A -> (I+A)^{-1}), or the whole chain (both launches, A through
+HBM).
 
 Timed region: K steps captured in one HIP graph (launch overhead of the
 Python/ctypes call path is not the op's), bracketed by a device
@@ -31,20 +36,49 @@ if ROOT not in sys.path:
 METRIC = "fused KKT+solve ms/iter & achieved HBM GB/s at (1,8192,8,128) bf16, 1 GPU"
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E peak
 PAGES_FUSED_MS = 0.3593         # Ascend 910B fused op at (1,8192,8,128), PR #135 perf table (context only)
+PAGES_TWO_OP_MS = 0.4318        # Ascend 910B two-op chain at (1,8192,8,128), same table (context only)
 MALL_BYTES = 256 << 20
 KERNEL_SRC = os.path.join(ROOT, "chunked_gated_delta_token_amd", "csrc", "kkt_solve.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_kkt_solve_T8192_H8_bf16_f32.txt")
+# the kernel each op launches (chain: both of the unfused steps)
+KERNELS = {"fused": "kkt_solve_kernel", "scaled_dot": "kkt_scaled_dot_kernel",
+           "solve_tril": "kkt_solve_tril_kernel", "chain": "kkt_scaled_dot_kernel+kkt_solve_tril_kernel"}
+ENTRY = {"fused": "kkt_solve", "scaled_dot": "kkt_scaled_dot", "solve_tril": "kkt_solve_tril"}
+
+
+def traffic_file(op: str, workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"traffic_{ENTRY[op]}_{workload}.txt")
+
 
 ESIZE = {"f32": 4, "bf16": 2, "f16": 2}
 
 
-def algorithmic_bytes(w, n_tokens: int) -> int:
-    """Minimum bytes one call must move: k once, g and beta once (when given),
-    the output once.  (cu_seqlens, a few bytes, is ignored.)"""
+def chunk_lengths(w, cu_seqlens):
+    """Lengths L of every chunk of one head."""
+    if cu_seqlens is None:
+        full, tail = divmod(w.T, 64)
+        return [64] * full * w.B + ([tail] * w.B if tail else [])
+    out = []
+    for s in range(len(cu_seqlens) - 1):
+        n = int(cu_seqlens[s + 1]) - int(cu_seqlens[s])
+        out += [64] * (n // 64) + ([n % 64] if n % 64 else [])
+    return out
+
+
+def algorithmic_bytes(w, n_tokens: int, op: str = "fused", cu_seqlens=None) -> int:
+    """Minimum bytes one step must move.  fused and chain: k once, g and beta
+    once (when given), the output once (the chain's A round trip is its own
+    overhead, not the step's work).  scaled_dot: k, g, beta, and A in fp32.
+    solve_tril: the strictly lower entries of A (L (L-1) / 2 fp32 values per
+    chunk and head) and the output.  (cu_seqlens, a few bytes, is ignored.)"""
     H, K = w.H, w.K
-    per_token = H * K * ESIZE[w.in_dtype] + H * 64 * ESIZE[w.out_dtype]
-    per_token += H * 4 * (int(w.gate) + int(w.beta))
-    return per_token * n_tokens
+    k_gb = H * K * ESIZE[w.in_dtype] + H * 4 * (int(w.gate) + int(w.beta))
+    out = H * 64 * ESIZE[w.out_dtype]
+    if op in ("fused", "chain"):
+        return (k_gb + out) * n_tokens
+    if op == "scaled_dot":
+        return (k_gb + H * 64 * 4) * n_tokens
+    lower = sum(L * (L - 1) // 2 for L in chunk_lengths(w, cu_seqlens)) * 4 * H
+    return lower + out * n_tokens
 
 
 def source_digest() -> str:
@@ -52,13 +86,13 @@ def source_digest() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def read_traffic(digest: str):
+def read_traffic(digest: str, path: str):
     """HBM bytes per launch from the committed counter summary, if it was
     taken on the current kernel source; None otherwise."""
-    if not os.path.exists(TRAFFIC_FILE):
+    if not os.path.exists(path):
         return None
     vals = {}
-    with open(TRAFFIC_FILE) as f:
+    with open(path) as f:
         for line in f:
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
@@ -71,22 +105,35 @@ def read_traffic(digest: str):
         return None
 
 
-def cpu_baseline(inp, nbytes: int, budget_s: float):
-    """The fp64 oracle (as it is) on the same workload, repeated until about
-    budget_s seconds of CPU work; throughput in the metric's unit."""
+def cpu_baseline(inp, nbytes: int, budget_s: float, op: str = "fused"):
+    """The fp64 oracle (as it is) for the same step on the same workload,
+    repeated until about budget_s seconds of CPU work; throughput in the
+    metric's unit."""
     import oracle
-    k64, g, b = inp.k64(), inp.g, inp.beta
+    k64, g, b, cu = inp.k64(), inp.g, inp.beta, inp.cu_seqlens
     g64 = None if g is None else g.astype("float64")
     b64 = None if b is None else b.astype("float64")
+    A = None
+    if op == "solve_tril":
+        A = oracle.scaled_dot_ref(k64, g64, b64, cu).astype("float32").astype("float64")
     reps, t0 = 0, time.perf_counter()
     while True:
-        oracle.kkt_solve_ref(k64, g64, b64, inp.cu_seqlens)
+        if op == "fused":
+            oracle.kkt_solve_ref(k64, g64, b64, cu)
+        elif op == "scaled_dot":
+            oracle.scaled_dot_ref(k64, g64, b64, cu)
+        elif op == "solve_tril":
+            oracle.solve_tril_ref(A, cu)
+        else:
+            oracle.solve_tril_ref(oracle.scaled_dot_ref(k64, g64, b64, cu), cu)
         reps += 1
         el = time.perf_counter() - t0
         if el >= budget_s:
             break
+    what = {"fused": "the fused op", "scaled_dot": "A alone", "solve_tril": "the solve of a given A",
+            "chain": "A, then its solve"}[op]
     return {"value": nbytes * reps / el / 1e9, "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"the whole workload, {reps} calls in {el:.1f} s (fp64, OpenMP over chunk-head tiles)"}
+            "sample": f"the whole workload ({what}), {reps} calls in {el:.1f} s (fp64, OpenMP over chunk-head tiles)"}
 
 
 def copy_calibration(nbytes: int, steps: int):
@@ -120,27 +167,31 @@ def _counter_values(directory: str, counter: str, kernel_substr: str):
     return vals
 
 
-def summarize_traffic(dirs, copy_bytes: int):
-    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the op, each scaled by
-    the bytes-per-KiB ratio the same counter shows for a plain copy."""
+def summarize_traffic(dirs, copy_bytes: int, op: str, workload: str):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the op's kernel, each
+    scaled by the bytes-per-KiB ratio the same counter shows for a plain copy."""
     import statistics
     if copy_bytes <= 0:
         raise SystemExit("--copy-bytes is required")
-    op_fetch = statistics.median(_counter_values(dirs[0], "FETCH_SIZE", "kkt_solve_kernel"))
-    op_write = statistics.median(_counter_values(dirs[1], "WRITE_SIZE", "kkt_solve_kernel"))
+    if op == "chain":
+        raise SystemExit("traffic is summarized per kernel: use --op fused, scaled_dot or solve_tril")
+    kname = KERNELS[op]
+    op_fetch = statistics.median(_counter_values(dirs[0], "FETCH_SIZE", kname))
+    op_write = statistics.median(_counter_values(dirs[1], "WRITE_SIZE", kname))
     cp_fetch = statistics.median(_counter_values(dirs[2], "FETCH_SIZE", "copy"))
     cp_write = statistics.median(_counter_values(dirs[3], "WRITE_SIZE", "copy"))
     f_scale = copy_bytes / cp_fetch
     w_scale = copy_bytes / cp_write
     fetch_b, write_b = op_fetch * f_scale, op_write * w_scale
+    sel = f"--op {op} --workload {workload}"
     lines = [
-        "# HBM traffic of kkt_solve_kernel, bench workload T8192_H8_bf16_f32 (B=1,T=8192,H=8,K=128 bf16 -> fp32)",
+        f"# HBM traffic of {kname}, workload {workload}",
         "# commands (run from the repository root, then summarized by the last one):",
-        "#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d <op_fetch> -- python bench.py --timing eager --steps 20 --warmup 2 --no-cpu-baseline",
-        "#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d <op_write> -- python bench.py --timing eager --steps 20 --warmup 2 --no-cpu-baseline",
+        f"#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d <op_fetch> -- python bench.py {sel} --timing eager --steps 20 --warmup 2 --no-cpu-baseline",
+        f"#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d <op_write> -- python bench.py {sel} --timing eager --steps 20 --warmup 2 --no-cpu-baseline",
         f"#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d <copy_fetch> -- python bench.py --copy-calibration {copy_bytes} --steps 20",
         f"#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d <copy_write> -- python bench.py --copy-calibration {copy_bytes} --steps 20",
-        f"#   python bench.py --summarize-traffic <op_fetch> <op_write> <copy_fetch> <copy_write> --copy-bytes {copy_bytes}",
+        f"#   python bench.py --summarize-traffic <op_fetch> <op_write> <copy_fetch> <copy_write> --copy-bytes {copy_bytes} {sel}",
         f"kernel_source_sha256_16: {source_digest()}",
         f"op_fetch_size_kib_median: {op_fetch:.1f}",
         f"op_write_size_kib_median: {op_write:.1f}",
@@ -153,8 +204,9 @@ def summarize_traffic(dirs, copy_bytes: int):
         f"write_bytes_per_launch: {write_b:.0f}",
         f"hbm_bytes_per_launch: {fetch_b + write_b:.0f}",
     ]
-    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
-    with open(TRAFFIC_FILE, "w") as f:
+    path = traffic_file(op, workload)
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
@@ -165,6 +217,8 @@ def main():
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=None)
+    ap.add_argument("--op", choices=["fused", "scaled_dot", "solve_tril", "chain"], default="fused",
+                    help="what one step runs (default: the fused op)")
     ap.add_argument("--timing", choices=["graph", "eager"], default="graph")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -178,7 +232,8 @@ def main():
     args = ap.parse_args()
 
     if args.summarize_traffic:
-        summarize_traffic(args.summarize_traffic, args.copy_bytes)
+        from chunked_gated_delta_token_amd import workloads as W
+        summarize_traffic(args.summarize_traffic, args.copy_bytes, args.op, args.workload or W.BENCH_WORKLOAD)
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -213,33 +268,71 @@ def main():
     b0 = None if inp.beta is None else torch.from_numpy(inp.beta).to(dev)
     cu0 = None if inp.cu_seqlens is None else torch.from_numpy(inp.cu_seqlens).to(dev)
     n_tokens = w.B * w.T
-    nbytes = algorithmic_bytes(w, n_tokens)
-    R = max(2, -(-2 * MALL_BYTES // nbytes))
+    op = args.op
+    nbytes = algorithmic_bytes(w, n_tokens, op, inp.cu_seqlens)
+    num_seqs = 0 if inp.cu_seqlens is None else len(inp.cu_seqlens) - 1
+    stream = torch.cuda.Stream(dev)
+    shape = (w.B, w.T, w.H, 64)
+    if op == "solve_tril":
+        # the solve's input: A of the workload, made once by the first step
+        A0 = torch.empty(shape, dtype=torch.float32, device=dev)
+        st = lib.kkt_scaled_dot(k0.data_ptr(), None if g0 is None else g0.data_ptr(),
+                                None if b0 is None else b0.data_ptr(), None if cu0 is None else cu0.data_ptr(),
+                                num_seqs, w.B, w.T, w.H, w.K, 64, kdt[w.in_dtype], A0.data_ptr(), None)
+        if st != 0:
+            raise RuntimeError(f"kkt_scaled_dot status {st}: {kkt.last_error()}")
+        torch.cuda.synchronize()
+    # bytes one buffer set occupies (every tensor a step touches)
+    a_bytes = int(np.prod(shape)) * 4
+    out_bytes = int(np.prod(shape)) * ESIZE[w.out_dtype]
+    set_bytes = {"fused": nbytes, "scaled_dot": nbytes, "chain": nbytes + a_bytes,
+                 "solve_tril": a_bytes + out_bytes}[op]
+    R = max(2, -(-2 * MALL_BYTES // set_bytes))
     sets = []
     for _ in range(R):
-        sets.append(dict(k=k0.clone(), g=None if g0 is None else g0.clone(), b=None if b0 is None else b0.clone(),
-                         cu=None if cu0 is None else cu0.clone(),
-                         out=torch.empty((w.B, w.T, w.H, 64), dtype=tdt[w.out_dtype], device=dev)))
+        s_ = dict(cu=None if cu0 is None else cu0.clone())
+        if op != "solve_tril":
+            s_.update(k=k0.clone(), g=None if g0 is None else g0.clone(), b=None if b0 is None else b0.clone())
+        if op in ("scaled_dot", "chain"):
+            s_["A"] = torch.empty(shape, dtype=torch.float32, device=dev)
+        if op == "solve_tril":
+            s_["A"] = A0.clone()
+        if op != "scaled_dot":
+            s_["out"] = torch.empty(shape, dtype=tdt[w.out_dtype], device=dev)
+        sets.append(s_)
     del k0, g0, b0
-    stream = torch.cuda.Stream(dev)
-    num_seqs = 0 if inp.cu_seqlens is None else len(inp.cu_seqlens) - 1
+    if op == "solve_tril":
+        del A0
 
     def ptr(t):
         return None if t is None else ctypes.c_void_p(t.data_ptr())
 
-    calls = [(ptr(s["k"]), ptr(s["g"]), ptr(s["b"]), ptr(s["cu"]), num_seqs, w.B, w.T, w.H, w.K, 64,
-              kdt[w.in_dtype], kdt[w.out_dtype], ptr(s["out"]), ctypes.c_void_p(stream.cuda_stream)) for s in sets]
+    sp = ctypes.c_void_p(stream.cuda_stream)
+
+    def step_calls(s_):
+        """(entry point, arguments) of the launches one step makes."""
+        kargs = (ptr(s_.get("k")), ptr(s_.get("g")), ptr(s_.get("b")), ptr(s_["cu"]), num_seqs, w.B, w.T, w.H, w.K, 64,
+                 kdt[w.in_dtype])
+        if op == "fused":
+            return [(lib.kkt_solve, kargs + (kdt[w.out_dtype], ptr(s_["out"]), sp))]
+        tril = (lib.kkt_solve_tril, (ptr(s_["A"]), ptr(s_["cu"]), num_seqs, w.B, w.T, w.H, 64, kdt[w.out_dtype],
+                                     ptr(s_.get("out")), sp))
+        dot = (lib.kkt_scaled_dot, kargs + (ptr(s_["A"]), sp))
+        return {"scaled_dot": [dot], "solve_tril": [tril], "chain": [dot, tril]}[op]
+
+    calls = [step_calls(s_) for s_ in sets]
 
     def launch(i):
-        st = lib.kkt_solve(*calls[i % R])
-        if st != 0:
-            raise RuntimeError(f"kkt_solve status {st}: {kkt.last_error()}")
+        for fn, a in calls[i % R]:
+            st = fn(*a)
+            if st != 0:
+                raise RuntimeError(f"{fn.__name__} status {st}: {kkt.last_error()}")
 
     # correctness guard on the bench inputs (cheap structural check, no oracle)
     with torch.cuda.stream(stream):
         launch(0)
     torch.cuda.synchronize()
-    o = sets[0]["out"].float()
+    o = sets[0]["A" if op == "scaled_dot" else "out"].float()
     assert torch.isfinite(o).all().item(), "non-finite output"
     del o
 
@@ -291,12 +384,17 @@ def main():
 
     achieved = nbytes / (ev_ms * 1e-3) / 1e9
     digest = source_digest()
-    traffic = read_traffic(digest)
+    traffic = None if op == "chain" else read_traffic(digest, traffic_file(op, name))
     n_tiles = w.H * (sum(-(-(int(inp.cu_seqlens[s + 1]) - int(inp.cu_seqlens[s])) // 64)
                          for s in range(num_seqs)) if num_seqs else w.B * (-(-w.T // 64)))
     value = nbytes / (ms_per_step * 1e-3) / 1e9
+    metric = METRIC if op == "fused" else {
+        "scaled_dot": "KKT A alone (first step of the unfused chain) ms/iter & achieved HBM GB/s, 1 GPU",
+        "solve_tril": "solve of a given A (second step of the unfused chain) ms/iter & achieved HBM GB/s, 1 GPU",
+        "chain": "unfused two-step chain (A through HBM) ms/iter & GB/s of the fused op's bytes, 1 GPU"}[op]
+    pages_ms = {"fused": PAGES_FUSED_MS, "chain": PAGES_TWO_OP_MS}.get(op)
     line = {
-        "metric": METRIC,
+        "metric": metric,
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -305,19 +403,20 @@ def main():
         "ms_per_step": round(ms_per_step, 6),
         "higher_is_better": True,
         "scaling": "weak",
-        "vs_baseline": round(PAGES_FUSED_MS / ms_per_step, 3) if name == W.BENCH_WORKLOAD else None,
+        "vs_baseline": round(pages_ms / ms_per_step, 3) if (pages_ms and name == W.BENCH_WORKLOAD) else None,
         "dtype": w.in_dtype,
         "data": "synthetic",
-        "config": {"workload": name, "B": w.B, "T": w.T, "H": w.H, "K": w.K, "in_dtype": w.in_dtype,
+        "config": {"workload": name, "op": op, "B": w.B, "T": w.T, "H": w.H, "K": w.K, "in_dtype": w.in_dtype,
                    "out_dtype": w.out_dtype, "gate": w.gate, "beta": w.beta, "tiles": n_tiles,
                    "algorithmic_bytes": nbytes, "buffer_sets": R, "timing": args.timing,
                    "chunks_per_s": round(n_tiles / (ms_per_step * 1e-3), 1)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "event_ms_per_launch": round(ev_ms, 6), "kernel_source_sha256_16": digest},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": KERNELS[op],
+                     "event_ms_per_step": round(ev_ms, 6), "launches_per_step": len(calls[0]),
+                     "kernel_source_sha256_16": digest},
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(inp, nbytes, args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(inp, nbytes, args.cpu_seconds, op)
     print(json.dumps(line), flush=True)
 
 

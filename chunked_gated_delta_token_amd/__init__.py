@@ -3,9 +3,11 @@ forward pass, for AMD Instinct MI355X (gfx950).
 
     from chunked_gated_delta_token_amd import kkt_solve
     X = kkt_solve(k, g, beta)          # [B, T, H, 64] rows of (I + A)^{-1}
+    A = kkt_scaled_dot(k, g, beta)     # the unfused chain: A alone (fp32) ...
+    X = kkt_solve_tril(A)              # ... then its solve
 
 The computation is the HIP library ``libkkt_solve.so`` (C ABI in
 ``include/kkt_solve.h``); this package only marshals arguments.
 """
-from .kkt import (KKTError, chunk_gated_delta_rule_fwd_kkt_solve, kkt_solve, last_error,  # noqa: F401
-                  load_library, version)
+from .kkt import (KKTError, chunk_gated_delta_rule_fwd_kkt_solve, chunk_scaled_dot_kkt_fwd,  # noqa: F401
+                  kkt_scaled_dot, kkt_solve, kkt_solve_tril, last_error, load_library, solve_tril, version)

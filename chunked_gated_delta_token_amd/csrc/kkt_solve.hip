@@ -54,7 +54,7 @@
 
 #include "kkt_solve.h"
 
-#define KKT_VERSION_NUMBER 200  // 0.2.0
+#define KKT_VERSION_NUMBER 300  // 0.3.0
 
 namespace {
 
@@ -102,6 +102,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 
 // ---------------------------------------------------------------- element types
 enum class Elt { F32, BF16, F16 };
+
+// What one launch computes.
+//   Fused:     k, g, beta -> (I + A)^{-1}            (the fused op)
+//   ScaledDot: k, g, beta -> A, fp32                 (first step of the unfused chain)
+//   SolveTril: A (fp32)   -> (I + strict_lower(A))^{-1}  (second step)
+enum class Mode { Fused, ScaledDot, SolveTril };
 
 template <Elt E> struct EltInfo;
 template <> struct EltInfo<Elt::F32> { using storage = float; static constexpr int bytes = 4; };
@@ -228,17 +234,14 @@ __device__ Tile varlen_tile(const int32_t* __restrict__ cu, int32_t num_seqs, in
 }
 
 // ---------------------------------------------------------------- the kernel
-template <Elt IN, Elt OUT, int K>
-__global__ __launch_bounds__(kWave * kWavesPerGroup)
-void kkt_solve_kernel(const KernelArgs args)
+template <Mode MODE, Elt IN, Elt OUT, int K>
+__device__ __forceinline__ void run_tile(const KernelArgs& args, WaveLds* lds_all)
 {
     constexpr int kInBytes = EltInfo<IN>::bytes;
     constexpr int kOutBytes = EltInfo<OUT>::bytes;
     constexpr int kElemsPer16B = 16 / kInBytes;            // 8 (16-bit) or 4 (fp32)
     constexpr int kSteps = K / (4 * kElemsPer16B);          // 16-byte fragments per row per lane
     static_assert(K % (4 * kElemsPer16B) == 0, "K must fill whole fragments");
-
-    __shared__ WaveLds lds_all[kWavesPerGroup];
 
     const int lane = threadIdx.x % kWave;
     // wave-uniform values are pinned to scalar registers so that the buffer
@@ -282,123 +285,201 @@ void kkt_solve_kernel(const KernelArgs args)
 
     // Buffer resources spanning exactly rows 0 .. L-1 of this tile.
     const int64_t tok = row0 * H + h;  // flat (token, head) index of row 0
-    const __amdgpu_buffer_rsrc_t k_rsrc = make_rsrc(
-        static_cast<const char*>(args.k) + tok * (int64_t)(K * kInBytes),
-        (uint32_t)(L - 1) * args.k_row_bytes + K * kInBytes);
     const __amdgpu_buffer_rsrc_t o_rsrc = make_rsrc(
         static_cast<char*>(args.out) + tok * (int64_t)(kChunk * kOutBytes),
         (uint32_t)(L - 1) * args.o_row_bytes + kChunk * kOutBytes);
 
-    // ---- a3: g and beta, one row per lane (rows >= L read as 0).  Issued
-    // before the K tile: loads complete in order, so waiting for these two
-    // does not wait for the whole tile.
-    const bool has_g = args.g != nullptr;
-    const bool valid = lane < L;
-    float gv = 0.0f, bv = 1.0f;
-    {
-        const uint32_t voff = (uint32_t)lane * (uint32_t)H * 4u;
-        const uint32_t span = (uint32_t)(L - 1) * (uint32_t)H * 4u + 4u;
-        // the loads return raw 32-bit words: reinterpret, do not convert
-        if (has_g) {
-            gv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(args.g + tok, span), voff, 0, 0));
-        }
-        if (args.beta != nullptr) {
-            bv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(args.beta + tok, span), voff, 0, 0));
-        }
-    }
-
-    // ---- a2: K fragments, all loads issued up front (rows >= L read as 0).
-    // Each load instruction reads 64 bytes of 16 rows; the next k-step reads
-    // the other half of the same 128-byte lines, so these loads are not
-    // marked streaming (the lines must survive in L2 until then).  The
-    // scheduling barrier keeps every load ahead of the first MFMA, so the
-    // whole tile is in flight at once.
-    u32x4 frag[4][kSteps];
-#pragma unroll
-    for (int bi = 0; bi < 4; ++bi) {
-        const uint32_t voff = (uint32_t)(16 * bi + m) * args.k_row_bytes + q * 16;
-#pragma unroll
-        for (int s = 0; s < kSteps; ++s) {
-            frag[bi][s] = __builtin_amdgcn_raw_buffer_load_b128(k_rsrc, voff + s * 64, 0, 0);
-        }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-
-    // ---- a4: Gram blocks.  Block (i, j): lane (q, n=m) holds rows 16i + 4q + r, column 16j + n.
-    auto gram = [&](int i, int j) -> f32x4 {
-        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int s = 0; s < kSteps; ++s) acc = gram_step<IN>(frag[i][s], frag[j][s], acc);
-        return acc;
-    };
-    f32x4 S[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-        for (int j = 0; j <= i; ++j) S[i][j] = gram(i, j);
-    }
-
-    // ---- a5: epilogue
-    bool factored = true;
-    if (has_g) {
-        // reference: row 0's gate (always a valid row), so the factors of
-        // rows < L do not depend on L.  If every valid row is within 25 of
-        // it, every pair differs by at most 50 (the clamp cannot bind) and
-        // every factor lies in [e^-25, e^25].
-        const float gref = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, gv)));
-        factored = __all(!valid || fabsf(gv - gref) <= 0.5f * kGateClamp);
-        if (factored) {
-            const float d = gv - gref;
-            lds.row_scale[lane] = valid ? bv * __expf(d) : 0.0f;
-            lds.col_scale[lane] = valid ? __expf(-d) : 0.0f;
-        } else {
-            lds.row_scale[lane] = valid ? bv : 0.0f;
-            lds.gate[lane] = valid ? gv : 0.0f;
-        }
-    } else {
-        lds.row_scale[lane] = valid ? bv : 0.0f;
-    }
-    wave_lds_sync();
+    // The 10 lower 16x16 blocks of A, result layout: A[i][j] lane (q, n)
+    // holds A_ij[4q .. 4q+3][n] (rows 16i + 4q + r, column 16j + n).  The
+    // diagonal blocks still hold their upper part here; it is masked below.
     f32x4 A[4][4];
-    if (!has_g) {
-        // A = beta_i S (rows >= L have beta 0 and zero keys)
+    if constexpr (MODE == Mode::SolveTril) {
+        // ---- A from memory (fp32 rows of 64; the kernel argument k carries A)
+        const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(
+            static_cast<const char*>(args.k) + tok * (int64_t)(kChunk * 4),
+            (uint32_t)(L - 1) * args.k_row_bytes + kChunk * 4);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const f32x4 rr = *reinterpret_cast<const f32x4*>(&lds.row_scale[16 * i + 4 * q]);
-#pragma unroll
-            for (int j = 0; j <= i; ++j) A[i][j] = rr * S[i][j];
-        }
-    } else if (factored) {
-        // A = (r_i S) c_j: both factors are zero outside the chunk's L rows
-        float cc[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) cc[j] = lds.col_scale[16 * j + m];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const f32x4 rr = *reinterpret_cast<const f32x4*>(&lds.row_scale[16 * i + 4 * q]);
-#pragma unroll
-            for (int j = 0; j <= i; ++j) A[i][j] = (rr * S[i][j]) * cc[j];
-        }
-    } else {
-        // A = beta_i S exp(clamp(g_i - g_j)); the clamp bounds the gate, so
-        // zero keys and zero beta outside the chunk still give 0
-        float gc[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) gc[j] = lds.gate[16 * j + m];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const f32x4 rr = *reinterpret_cast<const f32x4*>(&lds.row_scale[16 * i + 4 * q]);
-            const f32x4 gr = *reinterpret_cast<const f32x4*>(&lds.gate[16 * i + 4 * q]);
 #pragma unroll
             for (int j = 0; j <= i; ++j) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float d = fminf(fmaxf(gr[r] - gc[j], -kGateClamp), kGateClamp);
-                    A[i][j][r] = rr[r] * (S[i][j][r] * __expf(d));
+                    const uint32_t voff = (uint32_t)(16 * i + 4 * q + r) * args.k_row_bytes + (16 * j + m) * 4;
+                    A[i][j][r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(a_rsrc, voff, 0, 0));
                 }
             }
         }
+    } else {
+        const __amdgpu_buffer_rsrc_t k_rsrc = make_rsrc(
+            static_cast<const char*>(args.k) + tok * (int64_t)(K * kInBytes),
+            (uint32_t)(L - 1) * args.k_row_bytes + K * kInBytes);
+
+        // ---- a3: g and beta, one row per lane (rows >= L read as 0).  Issued
+        // before the K tile: loads complete in order, so waiting for these two
+        // does not wait for the whole tile.
+        const bool has_g = args.g != nullptr;
+        const bool valid = lane < L;
+        float gv = 0.0f, bv = 1.0f;
+        {
+            const uint32_t voff = (uint32_t)lane * (uint32_t)H * 4u;
+            const uint32_t span = (uint32_t)(L - 1) * (uint32_t)H * 4u + 4u;
+            // the loads return raw 32-bit words: reinterpret, do not convert
+            if (has_g) {
+                gv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(args.g + tok, span), voff, 0, 0));
+            }
+            if (args.beta != nullptr) {
+                bv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(args.beta + tok, span), voff, 0, 0));
+            }
+        }
+
+        // ---- a2: K fragments, all loads issued up front (rows >= L read as 0).
+        // Each load instruction reads 64 bytes of 16 rows; the next k-step reads
+        // the other half of the same 128-byte lines, so these loads are not
+        // marked streaming (the lines must survive in L2 until then).  The
+        // scheduling barrier keeps every load ahead of the first MFMA, so the
+        // whole tile is in flight at once.
+        u32x4 frag[4][kSteps];
+#pragma unroll
+        for (int bi = 0; bi < 4; ++bi) {
+            const uint32_t voff = (uint32_t)(16 * bi + m) * args.k_row_bytes + q * 16;
+#pragma unroll
+            for (int s = 0; s < kSteps; ++s) {
+                frag[bi][s] = __builtin_amdgcn_raw_buffer_load_b128(k_rsrc, voff + s * 64, 0, 0);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+
+        // ---- a4: Gram blocks.  Block (i, j): lane (q, n=m) holds rows 16i + 4q + r, column 16j + n.
+        auto gram = [&](int i, int j) -> f32x4 {
+            f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int s = 0; s < kSteps; ++s) acc = gram_step<IN>(frag[i][s], frag[j][s], acc);
+            return acc;
+        };
+        f32x4 S[4][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int j = 0; j <= i; ++j) S[i][j] = gram(i, j);
+        }
+
+        // ---- a5: epilogue
+        bool factored = true;
+        if (has_g) {
+            // reference: row 0's gate (always a valid row), so the factors of
+            // rows < L do not depend on L.  If every valid row is within 25 of
+            // it, every pair differs by at most 50 (the clamp cannot bind) and
+            // every factor lies in [e^-25, e^25].
+            const float gref = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, gv)));
+            factored = __all(!valid || fabsf(gv - gref) <= 0.5f * kGateClamp);
+            if (factored) {
+                const float d = gv - gref;
+                lds.row_scale[lane] = valid ? bv * __expf(d) : 0.0f;
+                lds.col_scale[lane] = valid ? __expf(-d) : 0.0f;
+            } else {
+                lds.row_scale[lane] = valid ? bv : 0.0f;
+                lds.gate[lane] = valid ? gv : 0.0f;
+            }
+        } else {
+            lds.row_scale[lane] = valid ? bv : 0.0f;
+        }
+        wave_lds_sync();
+        if (!has_g) {
+            // A = beta_i S (rows >= L have beta 0 and zero keys)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const f32x4 rr = *reinterpret_cast<const f32x4*>(&lds.row_scale[16 * i + 4 * q]);
+#pragma unroll
+                for (int j = 0; j <= i; ++j) A[i][j] = rr * S[i][j];
+            }
+        } else if (factored) {
+            // A = (r_i S) c_j: both factors are zero outside the chunk's L rows
+            float cc[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) cc[j] = lds.col_scale[16 * j + m];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const f32x4 rr = *reinterpret_cast<const f32x4*>(&lds.row_scale[16 * i + 4 * q]);
+#pragma unroll
+                for (int j = 0; j <= i; ++j) A[i][j] = (rr * S[i][j]) * cc[j];
+            }
+        } else {
+            // A = beta_i S exp(clamp(g_i - g_j)); the clamp bounds the gate, so
+            // zero keys and zero beta outside the chunk still give 0
+            float gc[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) gc[j] = lds.gate[16 * j + m];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const f32x4 rr = *reinterpret_cast<const f32x4*>(&lds.row_scale[16 * i + 4 * q]);
+                const f32x4 gr = *reinterpret_cast<const f32x4*>(&lds.gate[16 * i + 4 * q]);
+#pragma unroll
+                for (int j = 0; j <= i; ++j) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float d = fminf(fmaxf(gr[r] - gc[j], -kGateClamp), kGateClamp);
+                        A[i][j][r] = rr[r] * (S[i][j][r] * __expf(d));
+                    }
+                }
+            }
+        }
+    }  // A from k, g, beta
+    // ---- a8 helper: stage one 16-row block row and write full output rows
+    // (rows >= L fall outside o_rsrc and are dropped)
+    const f32x4 zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
+    auto store_block_row = [&](int i, f32x4 b0, f32x4 b1, f32x4 b2, f32x4 b3) {
+        wave_lds_sync();  // earlier reads of the area are done
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            lds.stage[4 * q + r][0 + m] = b0[r];
+            lds.stage[4 * q + r][16 + m] = b1[r];
+            lds.stage[4 * q + r][32 + m] = b2[r];
+            lds.stage[4 * q + r][48 + m] = b3[r];
+        }
+        wave_lds_sync();
+        if constexpr (OUT == Elt::F32) {
+            // 16 lanes per 256-byte row, 4 rows per pass
+            const int rsub = lane / 16, c4 = (lane % 16) * 4;
+#pragma unroll
+            for (int it = 0; it < 4; ++it) {
+                const int rr = 4 * it + rsub;
+                const f32x4 v = *reinterpret_cast<const f32x4*>(&lds.stage[rr][c4]);
+                const uint32_t voff = (uint32_t)(16 * i + rr) * args.o_row_bytes + c4 * 4;
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), o_rsrc, voff, 0, kNonTemporal);
+            }
+        } else {
+            // 8 lanes per 128-byte row, 8 rows per pass
+            const int rsub = lane / 8, c8 = (lane % 8) * 8;
+#pragma unroll
+            for (int it = 0; it < 2; ++it) {
+                const int rr = 8 * it + rsub;
+                const f32x4 v0 = *reinterpret_cast<const f32x4*>(&lds.stage[rr][c8]);
+                const f32x4 v1 = *reinterpret_cast<const f32x4*>(&lds.stage[rr][c8 + 4]);
+                u32x4 p;
+                p[0] = pack2<OUT>(v0[0], v0[1]);
+                p[1] = pack2<OUT>(v0[2], v0[3]);
+                p[2] = pack2<OUT>(v1[0], v1[1]);
+                p[3] = pack2<OUT>(v1[2], v1[3]);
+                const uint32_t voff = (uint32_t)(16 * i + rr) * args.o_row_bytes + c8 * 2;
+                __builtin_amdgcn_raw_buffer_store_b128(p, o_rsrc, voff, 0, kNonTemporal);
+            }
+        }
+    };
+
+    if constexpr (MODE == Mode::ScaledDot) {
+        // ---- A itself: strict lower triangle of every chunk, zeros elsewhere
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) A[i][i][r] = (4 * q + r > m) ? A[i][i][r] : 0.0f;
+        }
+        store_block_row(0, A[0][0], zero4, zero4, zero4);
+        store_block_row(1, A[1][0], A[1][1], zero4, zero4);
+        store_block_row(2, A[2][0], A[2][1], A[2][2], zero4);
+        store_block_row(3, A[3][0], A[3][1], A[3][2], A[3][3]);
+        return;
     }
+
     // strict lower triangle inside the diagonal blocks, stored transposed
     // (blk[d][col][row]): lane (q, n) holds rows 4q..4q+3 of column n, one
     // 16-byte write, and the solve below reads columns as contiguous rows
@@ -458,48 +539,6 @@ void kkt_solve_kernel(const KernelArgs args)
         for (int r = 0; r < 4; ++r) xa[d][r] = lds.blk[d][4 * q + r][m];
     }
 
-    // ---- a8 helper: stage one 16-row block row and write full output rows
-    // (rows >= L fall outside o_rsrc and are dropped)
-    const f32x4 zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
-    auto store_block_row = [&](int i, f32x4 b0, f32x4 b1, f32x4 b2, f32x4 b3) {
-        wave_lds_sync();  // earlier reads of the area are done
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            lds.stage[4 * q + r][0 + m] = b0[r];
-            lds.stage[4 * q + r][16 + m] = b1[r];
-            lds.stage[4 * q + r][32 + m] = b2[r];
-            lds.stage[4 * q + r][48 + m] = b3[r];
-        }
-        wave_lds_sync();
-        if constexpr (OUT == Elt::F32) {
-            // 16 lanes per 256-byte row, 4 rows per pass
-            const int rsub = lane / 16, c4 = (lane % 16) * 4;
-#pragma unroll
-            for (int it = 0; it < 4; ++it) {
-                const int rr = 4 * it + rsub;
-                const f32x4 v = *reinterpret_cast<const f32x4*>(&lds.stage[rr][c4]);
-                const uint32_t voff = (uint32_t)(16 * i + rr) * args.o_row_bytes + c4 * 4;
-                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), o_rsrc, voff, 0, kNonTemporal);
-            }
-        } else {
-            // 8 lanes per 128-byte row, 8 rows per pass
-            const int rsub = lane / 8, c8 = (lane % 8) * 8;
-#pragma unroll
-            for (int it = 0; it < 2; ++it) {
-                const int rr = 8 * it + rsub;
-                const f32x4 v0 = *reinterpret_cast<const f32x4*>(&lds.stage[rr][c8]);
-                const f32x4 v1 = *reinterpret_cast<const f32x4*>(&lds.stage[rr][c8 + 4]);
-                u32x4 p;
-                p[0] = pack2<OUT>(v0[0], v0[1]);
-                p[1] = pack2<OUT>(v0[2], v0[3]);
-                p[2] = pack2<OUT>(v1[0], v1[1]);
-                p[3] = pack2<OUT>(v1[2], v1[3]);
-                const uint32_t voff = (uint32_t)(16 * i + rr) * args.o_row_bytes + c8 * 2;
-                __builtin_amdgcn_raw_buffer_store_b128(p, o_rsrc, voff, 0, kNonTemporal);
-            }
-        }
-    };
-
     // block row 0 is final already
     store_block_row(0, xd[0], zero4, zero4, zero4);
 
@@ -531,6 +570,32 @@ void kkt_solve_kernel(const KernelArgs args)
 
     const f32x4 x30 = zero4 - mm16(wt32, x20, p30);
     store_block_row(3, x30, x31, x32, xd[3]);
+}
+
+// One kernel per entry point, so that profiles name the operation.
+template <Elt IN, Elt OUT, int K>
+__global__ __launch_bounds__(kWave * kWavesPerGroup)
+void kkt_solve_kernel(const KernelArgs args)
+{
+    __shared__ WaveLds lds_all[kWavesPerGroup];
+    run_tile<Mode::Fused, IN, OUT, K>(args, lds_all);
+}
+
+template <Elt IN, int K>
+__global__ __launch_bounds__(kWave * kWavesPerGroup)
+void kkt_scaled_dot_kernel(const KernelArgs args)
+{
+    __shared__ WaveLds lds_all[kWavesPerGroup];
+    run_tile<Mode::ScaledDot, IN, Elt::F32, K>(args, lds_all);
+}
+
+// (the input-type and K arguments of run_tile are unused in this mode)
+template <Elt OUT>
+__global__ __launch_bounds__(kWave * kWavesPerGroup)
+void kkt_solve_tril_kernel(const KernelArgs args)
+{
+    __shared__ WaveLds lds_all[kWavesPerGroup];
+    run_tile<Mode::SolveTril, Elt::F32, OUT, 64>(args, lds_all);
 }
 
 // ---------------------------------------------------------------- host side
@@ -579,32 +644,40 @@ kkt_status_t validate_cu_seqlens(const int32_t* cu, int64_t num_seqs, int64_t T,
     return KKT_OK;
 }
 
-template <Elt IN, Elt OUT, int K>
-hipError_t launch(const KernelArgs& a, hipStream_t stream)
+hipError_t launch(void (*kernel)(KernelArgs), const KernelArgs& a, hipStream_t stream)
 {
     const int64_t groups = ((int64_t)a.n_tiles + kWavesPerGroup - 1) / kWavesPerGroup;
-    hipLaunchKernelGGL((kkt_solve_kernel<IN, OUT, K>), dim3((unsigned)groups), dim3(kWave * kWavesPerGroup), 0,
-                       stream, a);
+    hipLaunchKernelGGL(kernel, dim3((unsigned)groups), dim3(kWave * kWavesPerGroup), 0, stream, a);
     return hipGetLastError();
 }
 
 template <Elt IN, Elt OUT>
-hipError_t launch_k(int64_t K, const KernelArgs& a, hipStream_t stream)
+hipError_t launch_fused(int64_t K, const KernelArgs& a, hipStream_t stream)
 {
     switch (K) {
-    case 64: return launch<IN, OUT, 64>(a, stream);
-    case 128: return launch<IN, OUT, 128>(a, stream);
-    default: return launch<IN, OUT, 256>(a, stream);
+    case 64: return launch(kkt_solve_kernel<IN, OUT, 64>, a, stream);
+    case 128: return launch(kkt_solve_kernel<IN, OUT, 128>, a, stream);
+    default: return launch(kkt_solve_kernel<IN, OUT, 256>, a, stream);
     }
 }
 
 template <Elt IN>
-hipError_t launch_out(kkt_dtype_t od, int64_t K, const KernelArgs& a, hipStream_t stream)
+hipError_t launch_fused_out(kkt_dtype_t od, int64_t K, const KernelArgs& a, hipStream_t stream)
 {
     switch (od) {
-    case KKT_DTYPE_F32: return launch_k<IN, Elt::F32>(K, a, stream);
-    case KKT_DTYPE_BF16: return launch_k<IN, Elt::BF16>(K, a, stream);
-    default: return launch_k<IN, Elt::F16>(K, a, stream);
+    case KKT_DTYPE_F32: return launch_fused<IN, Elt::F32>(K, a, stream);
+    case KKT_DTYPE_BF16: return launch_fused<IN, Elt::BF16>(K, a, stream);
+    default: return launch_fused<IN, Elt::F16>(K, a, stream);
+    }
+}
+
+template <Elt IN>
+hipError_t launch_scaled_dot(int64_t K, const KernelArgs& a, hipStream_t stream)
+{
+    switch (K) {
+    case 64: return launch(kkt_scaled_dot_kernel<IN, 64>, a, stream);
+    case 128: return launch(kkt_scaled_dot_kernel<IN, 128>, a, stream);
+    default: return launch(kkt_scaled_dot_kernel<IN, 256>, a, stream);
     }
 }
 
@@ -616,38 +689,24 @@ int64_t dtype_bytes(kkt_dtype_t d) { return d == KKT_DTYPE_F32 ? 4 : 2; }
 // concurrent accesses over the whole tensor.
 constexpr int64_t kRemapMaxGroups = 1024;
 
-}  // namespace
-
-extern "C" kkt_status_t kkt_solve(const void* k, const float* g, const float* beta,
-                                  const int32_t* cu_seqlens, int64_t num_seqs,
-                                  int64_t B, int64_t T, int64_t H, int64_t K,
-                                  int64_t chunk_size, kkt_dtype_t in_dtype, kkt_dtype_t out_dtype,
-                                  void* out, hipStream_t stream)
+// Checks shared by every entry point and the launch geometry.  in_row_bytes
+// and out_row_bytes are the strides between consecutive tokens of one head.
+// Returns KKT_OK with a filled in; makes no HIP call unless the arguments pass.
+kkt_status_t setup(KernelArgs& a, const void* in, const float* g, const float* beta,
+                   const int32_t* cu_seqlens, int64_t num_seqs, int64_t B, int64_t T, int64_t H,
+                   int64_t in_row_bytes, int64_t out_row_bytes, void* out, hipStream_t stream)
 {
-    g_last_error.clear();
-    // ---- argument checks: no HIP call before they pass
-    if (chunk_size != kChunk) return fail(KKT_ERR_UNSUPPORTED, "chunk_size must be 64");
-    if (!valid_dtype((int)in_dtype) || !valid_dtype((int)out_dtype)) return fail(KKT_ERR_INVALID_ARGUMENT, "unknown dtype");
-    if (B < 1 || H < 1 || K < 1 || T < 0) return fail(KKT_ERR_INVALID_ARGUMENT, "B, H, K must be >= 1 and T >= 0");
-    if (K != 64 && K != 128 && K != 256) return fail(KKT_ERR_UNSUPPORTED, "K must be 64, 128 or 256");
-    if (cu_seqlens != nullptr && (B != 1 || num_seqs < 1)) {
-        return fail(KKT_ERR_INVALID_ARGUMENT, "cu_seqlens needs B == 1 and num_seqs >= 1");
-    }
-    if (T == 0) return KKT_OK;
-    if (k == nullptr || out == nullptr) return fail(KKT_ERR_INVALID_ARGUMENT, "k and out must not be NULL");
-    // the kernel moves k and out in 16-byte vectors, g / beta / cu_seqlens in 4-byte words
-    if ((reinterpret_cast<uintptr_t>(k) & 15u) != 0 || (reinterpret_cast<uintptr_t>(out) & 15u) != 0) {
-        return fail(KKT_ERR_INVALID_ARGUMENT, "k and out must be 16-byte aligned");
+    if (in == nullptr || out == nullptr) return fail(KKT_ERR_INVALID_ARGUMENT, "input and output must not be NULL");
+    // the kernel moves the row tensors in 16-byte vectors, g / beta / cu_seqlens in 4-byte words
+    if ((reinterpret_cast<uintptr_t>(in) & 15u) != 0 || (reinterpret_cast<uintptr_t>(out) & 15u) != 0) {
+        return fail(KKT_ERR_INVALID_ARGUMENT, "input and output must be 16-byte aligned");
     }
     if ((reinterpret_cast<uintptr_t>(g) & 3u) != 0 || (reinterpret_cast<uintptr_t>(beta) & 3u) != 0 ||
         (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0) {
         return fail(KKT_ERR_INVALID_ARGUMENT, "g, beta and cu_seqlens must be 4-byte aligned");
     }
-
     // 32-bit in-tile offsets: 64 rows of one head must span < 2 GiB
-    const int64_t k_row_bytes = H * K * dtype_bytes(in_dtype);
-    const int64_t o_row_bytes = H * kChunk * dtype_bytes(out_dtype);
-    if (kChunk * k_row_bytes >= (1LL << 31) || kChunk * o_row_bytes >= (1LL << 31)) {
+    if (kChunk * in_row_bytes >= (1LL << 31) || kChunk * out_row_bytes >= (1LL << 31)) {
         return fail(KKT_ERR_UNSUPPORTED, "H * K too large for one launch");
     }
     const int64_t chunks_per_row = (T + kChunk - 1) / kChunk;
@@ -668,8 +727,7 @@ extern "C" kkt_status_t kkt_solve(const void* k, const float* g, const float* be
         }
     }
 
-    KernelArgs a;
-    a.k = k;
+    a.k = in;
     a.g = g;
     a.beta = beta;
     a.cu_seqlens = cu_seqlens;
@@ -679,16 +737,101 @@ extern "C" kkt_status_t kkt_solve(const void* k, const float* g, const float* be
     a.H = (int32_t)H;
     a.chunks_per_row = (int32_t)chunks_per_row;
     a.n_tiles = (int32_t)n_tiles;
-    a.k_row_bytes = (uint32_t)k_row_bytes;
-    a.o_row_bytes = (uint32_t)o_row_bytes;
+    a.k_row_bytes = (uint32_t)in_row_bytes;
+    a.o_row_bytes = (uint32_t)out_row_bytes;
     const int64_t groups = (n_tiles + kWavesPerGroup - 1) / kWavesPerGroup;
     a.xcd_remap = groups <= kRemapMaxGroups ? 1 : 0;
+    return KKT_OK;
+}
+
+// Size checks of the entry points that take k.
+kkt_status_t check_k_sizes(int64_t B, int64_t T, int64_t H, int64_t K, int64_t num_seqs, const int32_t* cu_seqlens)
+{
+    if (B < 1 || H < 1 || K < 1 || T < 0) return fail(KKT_ERR_INVALID_ARGUMENT, "B, H, K must be >= 1 and T >= 0");
+    if (K != 64 && K != 128 && K != 256) return fail(KKT_ERR_UNSUPPORTED, "K must be 64, 128 or 256");
+    if (cu_seqlens != nullptr && (B != 1 || num_seqs < 1)) {
+        return fail(KKT_ERR_INVALID_ARGUMENT, "cu_seqlens needs B == 1 and num_seqs >= 1");
+    }
+    return KKT_OK;
+}
+
+}  // namespace
+
+extern "C" kkt_status_t kkt_solve(const void* k, const float* g, const float* beta,
+                                  const int32_t* cu_seqlens, int64_t num_seqs,
+                                  int64_t B, int64_t T, int64_t H, int64_t K,
+                                  int64_t chunk_size, kkt_dtype_t in_dtype, kkt_dtype_t out_dtype,
+                                  void* out, hipStream_t stream)
+{
+    g_last_error.clear();
+    // ---- argument checks: no HIP call before they pass
+    if (chunk_size != kChunk) return fail(KKT_ERR_UNSUPPORTED, "chunk_size must be 64");
+    if (!valid_dtype((int)in_dtype) || !valid_dtype((int)out_dtype)) return fail(KKT_ERR_INVALID_ARGUMENT, "unknown dtype");
+    kkt_status_t st = check_k_sizes(B, T, H, K, num_seqs, cu_seqlens);
+    if (st != KKT_OK) return st;
+    if (T == 0) return KKT_OK;
+    KernelArgs a;
+    st = setup(a, k, g, beta, cu_seqlens, num_seqs, B, T, H, H * K * dtype_bytes(in_dtype),
+               H * kChunk * dtype_bytes(out_dtype), out, stream);
+    if (st != KKT_OK) return st;
 
     hipError_t e;
     switch (in_dtype) {
-    case KKT_DTYPE_F32: e = launch_out<Elt::F32>(out_dtype, K, a, stream); break;
-    case KKT_DTYPE_BF16: e = launch_out<Elt::BF16>(out_dtype, K, a, stream); break;
-    default: e = launch_out<Elt::F16>(out_dtype, K, a, stream); break;
+    case KKT_DTYPE_F32: e = launch_fused_out<Elt::F32>(out_dtype, K, a, stream); break;
+    case KKT_DTYPE_BF16: e = launch_fused_out<Elt::BF16>(out_dtype, K, a, stream); break;
+    default: e = launch_fused_out<Elt::F16>(out_dtype, K, a, stream); break;
+    }
+    if (e != hipSuccess) return fail(KKT_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(e));
+    return KKT_OK;
+}
+
+extern "C" kkt_status_t kkt_scaled_dot(const void* k, const float* g, const float* beta,
+                                       const int32_t* cu_seqlens, int64_t num_seqs,
+                                       int64_t B, int64_t T, int64_t H, int64_t K,
+                                       int64_t chunk_size, kkt_dtype_t in_dtype, float* A, hipStream_t stream)
+{
+    g_last_error.clear();
+    if (chunk_size != kChunk) return fail(KKT_ERR_UNSUPPORTED, "chunk_size must be 64");
+    if (!valid_dtype((int)in_dtype)) return fail(KKT_ERR_INVALID_ARGUMENT, "unknown dtype");
+    kkt_status_t st = check_k_sizes(B, T, H, K, num_seqs, cu_seqlens);
+    if (st != KKT_OK) return st;
+    if (T == 0) return KKT_OK;
+    KernelArgs a;
+    st = setup(a, k, g, beta, cu_seqlens, num_seqs, B, T, H, H * K * dtype_bytes(in_dtype), H * kChunk * 4, A, stream);
+    if (st != KKT_OK) return st;
+
+    hipError_t e;
+    switch (in_dtype) {
+    case KKT_DTYPE_F32: e = launch_scaled_dot<Elt::F32>(K, a, stream); break;
+    case KKT_DTYPE_BF16: e = launch_scaled_dot<Elt::BF16>(K, a, stream); break;
+    default: e = launch_scaled_dot<Elt::F16>(K, a, stream); break;
+    }
+    if (e != hipSuccess) return fail(KKT_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(e));
+    return KKT_OK;
+}
+
+extern "C" kkt_status_t kkt_solve_tril(const float* A, const int32_t* cu_seqlens, int64_t num_seqs,
+                                       int64_t B, int64_t T, int64_t H, int64_t chunk_size,
+                                       kkt_dtype_t out_dtype, void* out, hipStream_t stream)
+{
+    g_last_error.clear();
+    if (chunk_size != kChunk) return fail(KKT_ERR_UNSUPPORTED, "chunk_size must be 64");
+    if (!valid_dtype((int)out_dtype)) return fail(KKT_ERR_INVALID_ARGUMENT, "unknown dtype");
+    if (B < 1 || H < 1 || T < 0) return fail(KKT_ERR_INVALID_ARGUMENT, "B, H must be >= 1 and T >= 0");
+    if (cu_seqlens != nullptr && (B != 1 || num_seqs < 1)) {
+        return fail(KKT_ERR_INVALID_ARGUMENT, "cu_seqlens needs B == 1 and num_seqs >= 1");
+    }
+    if (T == 0) return KKT_OK;
+    KernelArgs a;
+    kkt_status_t st = setup(a, A, nullptr, nullptr, cu_seqlens, num_seqs, B, T, H, H * kChunk * 4,
+                            H * kChunk * dtype_bytes(out_dtype), out, stream);
+    if (st != KKT_OK) return st;
+
+    hipError_t e;
+    switch (out_dtype) {
+    case KKT_DTYPE_F32: e = launch(kkt_solve_tril_kernel<Elt::F32>, a, stream); break;
+    case KKT_DTYPE_BF16: e = launch(kkt_solve_tril_kernel<Elt::BF16>, a, stream); break;
+    default: e = launch(kkt_solve_tril_kernel<Elt::F16>, a, stream); break;
     }
     if (e != hipSuccess) return fail(KKT_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(e));
     return KKT_OK;

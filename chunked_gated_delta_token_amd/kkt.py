@@ -26,6 +26,13 @@ SIGNATURES = {
                                  ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                  ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
                                  ctypes.c_void_p, ctypes.c_void_p]),
+    "kkt_scaled_dot": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                      ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                      ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                                      ctypes.c_void_p, ctypes.c_void_p]),
+    "kkt_solve_tril": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                      ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                      ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]),
     "kkt_last_error": (ctypes.c_char_p, []),
     "kkt_version": (ctypes.c_int, []),
 }
@@ -78,6 +85,50 @@ def version() -> int:
     return int(load_library().kkt_version())
 
 
+def _k_inputs(k, g, beta, cu_seqlens, chunk_size):
+    """Shared checks of the entry points that take k; returns contiguous
+    tensors and the number of sequences."""
+    if chunk_size != 64:
+        raise ValueError("chunk_size must be 64")
+    if k.dim() != 4:
+        raise ValueError("k must be [B, T, H, K]")
+    if k.dtype not in _TORCH_TO_KKT:
+        raise TypeError(f"unsupported k dtype {k.dtype}")
+    if not k.is_cuda:
+        raise ValueError("k must be a device tensor")
+    B, T, H, _ = k.shape
+    for name, t in (("g", g), ("beta", beta)):
+        if t is not None:
+            if t.shape != (B, T, H) or t.dtype != torch.float32 or t.device != k.device:
+                raise ValueError(f"{name} must be float32 [B,T,H] on k's device")
+    g = None if g is None else g.contiguous()
+    beta = None if beta is None else beta.contiguous()
+    cu_seqlens, num_seqs = _cu_input(cu_seqlens, k.device)
+    return k.contiguous(), g, beta, cu_seqlens, num_seqs
+
+
+def _cu_input(cu_seqlens, device):
+    if cu_seqlens is None:
+        return None, 0
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.device != device:
+        raise ValueError("cu_seqlens must be int32 [N+1] on the input's device")
+    return cu_seqlens.contiguous(), cu_seqlens.numel() - 1
+
+
+def _out_tensor(out, shape, dtype, device):
+    if out is None:
+        # uninitialised: the kernels write every element
+        return torch.empty(shape, dtype=dtype, device=device)
+    if out.shape != shape or out.dtype != dtype or not out.is_contiguous() or out.device != device:
+        raise ValueError(f"out must be contiguous {list(shape)} of dtype {dtype} on the input's device")
+    return out
+
+
+def _stream_ptr(stream, device):
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
 def kkt_solve(k: torch.Tensor, g: Optional[torch.Tensor] = None, beta: Optional[torch.Tensor] = None,
               cu_seqlens: Optional[torch.Tensor] = None, chunk_size: int = 64,
               output_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None,
@@ -92,39 +143,61 @@ def kkt_solve(k: torch.Tensor, g: Optional[torch.Tensor] = None, beta: Optional[
     otherwise it is allocated uninitialised, since the kernel writes every
     element.
     """
-    if chunk_size != 64:
-        raise ValueError("chunk_size must be 64")
-    if k.dim() != 4:
-        raise ValueError("k must be [B, T, H, K]")
-    if k.dtype not in _TORCH_TO_KKT:
-        raise TypeError(f"unsupported k dtype {k.dtype}")
-    if not k.is_cuda:
-        raise ValueError("k must be a device tensor")
+    k, g, beta, cu_seqlens, num_seqs = _k_inputs(k, g, beta, cu_seqlens, chunk_size)
     B, T, H, K = k.shape
-    k = k.contiguous()
-    for name, t in (("g", g), ("beta", beta)):
-        if t is not None:
-            if t.shape != (B, T, H) or t.dtype != torch.float32 or t.device != k.device:
-                raise ValueError(f"{name} must be float32 [B,T,H] on k's device")
-    g = None if g is None else g.contiguous()
-    beta = None if beta is None else beta.contiguous()
-    num_seqs = 0
-    if cu_seqlens is not None:
-        if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.device != k.device:
-            raise ValueError("cu_seqlens must be int32 [N+1] on k's device")
-        cu_seqlens = cu_seqlens.contiguous()
-        num_seqs = cu_seqlens.numel() - 1
     odt = k.dtype if output_dtype is None else output_dtype
     if odt not in _TORCH_TO_KKT:
         raise TypeError(f"unsupported output dtype {odt}")
-    if out is None:
-        out = torch.empty((B, T, H, 64), dtype=odt, device=k.device)
-    elif out.shape != (B, T, H, 64) or out.dtype != odt or not out.is_contiguous() or out.device != k.device:
-        raise ValueError("out must be contiguous [B,T,H,64] of the output dtype on k's device")
-    s = stream if stream is not None else torch.cuda.current_stream(k.device)
+    out = _out_tensor(out, (B, T, H, 64), odt, k.device)
     with torch.cuda.device(k.device):
         st = kkt_solve_raw(_ptr(k), _ptr(g), _ptr(beta), _ptr(cu_seqlens), num_seqs, B, T, H, K, chunk_size,
-                           _TORCH_TO_KKT[k.dtype], _TORCH_TO_KKT[odt], _ptr(out), ctypes.c_void_p(s.cuda_stream))
+                           _TORCH_TO_KKT[k.dtype], _TORCH_TO_KKT[odt], _ptr(out), _stream_ptr(stream, k.device))
+    if st != KKT_OK:
+        raise KKTError(st, last_error())
+    return out
+
+
+def kkt_scaled_dot(k: torch.Tensor, g: Optional[torch.Tensor] = None, beta: Optional[torch.Tensor] = None,
+                   cu_seqlens: Optional[torch.Tensor] = None, chunk_size: int = 64,
+                   out: Optional[torch.Tensor] = None,
+                   stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """The first step of the unfused chain alone: the strictly lower A of
+    every 64-token chunk, fp32 [B, T, H, 64], zeros on and above the diagonal
+    (MindSpeed-Ops PR #135, PR description: chunk_scaled_dot_kkt_fwd).
+    Arguments as for ``kkt_solve``."""
+    k, g, beta, cu_seqlens, num_seqs = _k_inputs(k, g, beta, cu_seqlens, chunk_size)
+    B, T, H, K = k.shape
+    out = _out_tensor(out, (B, T, H, 64), torch.float32, k.device)
+    with torch.cuda.device(k.device):
+        st = load_library().kkt_scaled_dot(_ptr(k), _ptr(g), _ptr(beta), _ptr(cu_seqlens), num_seqs, B, T, H, K,
+                                           chunk_size, _TORCH_TO_KKT[k.dtype], _ptr(out),
+                                           _stream_ptr(stream, k.device))
+    if st != KKT_OK:
+        raise KKTError(st, last_error())
+    return out
+
+
+def kkt_solve_tril(A: torch.Tensor, cu_seqlens: Optional[torch.Tensor] = None, chunk_size: int = 64,
+                   output_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None,
+                   stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """The second step alone: rows of (I + strict_lower(A))^{-1} per 64-token
+    chunk (MindSpeed-Ops PR #135, PR description: solve_tril).  ``A`` is fp32
+    [B, T, H, 64]; only its strictly lower entries are read.  ``output_dtype``
+    defaults to fp32."""
+    if chunk_size != 64:
+        raise ValueError("chunk_size must be 64")
+    if A.dim() != 4 or A.shape[3] != 64 or A.dtype != torch.float32 or not A.is_cuda:
+        raise ValueError("A must be a float32 device tensor [B, T, H, 64]")
+    A = A.contiguous()
+    B, T, H, _ = A.shape
+    cu_seqlens, num_seqs = _cu_input(cu_seqlens, A.device)
+    odt = torch.float32 if output_dtype is None else output_dtype
+    if odt not in _TORCH_TO_KKT:
+        raise TypeError(f"unsupported output dtype {odt}")
+    out = _out_tensor(out, (B, T, H, 64), odt, A.device)
+    with torch.cuda.device(A.device):
+        st = load_library().kkt_solve_tril(_ptr(A), _ptr(cu_seqlens), num_seqs, B, T, H, chunk_size,
+                                           _TORCH_TO_KKT[odt], _ptr(out), _stream_ptr(stream, A.device))
     if st != KKT_OK:
         raise KKTError(st, last_error())
     return out
@@ -134,3 +207,14 @@ def chunk_gated_delta_rule_fwd_kkt_solve(k, g=None, beta=None, cu_seqlens=None, 
                                          output_dtype=None):
     """The pages' name for the fused op (same semantics as ``kkt_solve``)."""
     return kkt_solve(k, g, beta, cu_seqlens, chunk_size, output_dtype)
+
+
+def chunk_scaled_dot_kkt_fwd(k, beta=None, g=None, cu_seqlens=None, chunk_size=64):
+    """The pages' name for the first step of the unfused chain (same
+    semantics as ``kkt_scaled_dot``; fp32 output)."""
+    return kkt_scaled_dot(k, g, beta, cu_seqlens, chunk_size)
+
+
+def solve_tril(A, cu_seqlens=None, output_dtype=None):
+    """The pages' name for the second step (same semantics as ``kkt_solve_tril``)."""
+    return kkt_solve_tril(A, cu_seqlens, 64, output_dtype)

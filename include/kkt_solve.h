@@ -96,6 +96,47 @@ kkt_status_t kkt_solve(const void* k, const float* g, const float* beta,
                        int64_t chunk_size, kkt_dtype_t in_dtype, kkt_dtype_t out_dtype,
                        void* out, hipStream_t stream);
 
+/*
+ * kkt_scaled_dot: the first step of the unfused two-step path on its own
+ * (PR #135 page, PR description: the fused op replaces
+ * chunk_scaled_dot_kkt_fwd followed by solve_tril; the first of those forms A).
+ *
+ *   Writes, for every chunk as defined above,
+ *     A_out[b][t0 + i][h][j] = A[i][j]   for j < i < L (the formula above)
+ *     A_out[b][t0 + i][h][j] = +0.0      for j >= i
+ *   in fp32, shape [B,T,H,64], every element of every covered row written.
+ *
+ *   k, g, beta, cu_seqlens, num_seqs, B, T, H, K, chunk_size, in_dtype, stream:
+ *   as for kkt_solve (same alignment rules, same errors).  A_out: device,
+ *   [B,T,H,64] fp32, contiguous, 16-byte aligned, must not overlap any input.
+ *   The A it writes is bit-identical to the A that kkt_solve inverts.
+ */
+kkt_status_t kkt_scaled_dot(const void* k, const float* g, const float* beta,
+                            const int32_t* cu_seqlens, int64_t num_seqs,
+                            int64_t B, int64_t T, int64_t H, int64_t K,
+                            int64_t chunk_size, kkt_dtype_t in_dtype,
+                            float* A_out, hipStream_t stream);
+
+/*
+ * kkt_solve_tril: the second step of the unfused path on its own (PR #135
+ * page, PR description: solve_tril turns the chunk-local A into (I+A)^{-1}).
+ *
+ *   A          device, [B,T,H,64] fp32, contiguous, 16-byte aligned.  For every
+ *              chunk (cut as above) only the strictly lower entries A[i][j],
+ *              j < i < L, are read; the diagonal, the upper part and the
+ *              columns j >= L are ignored (they may hold anything).
+ *   cu_seqlens, num_seqs, B, T, H, chunk_size, stream: as for kkt_solve.
+ *   out_dtype, out: as for kkt_solve: rows of (I + strict_lower(A))^{-1},
+ *              [B,T,H,64], upper zeros written.  out must not overlap A.
+ *
+ *   kkt_solve_tril(kkt_scaled_dot(k, ...)) with fp32 A in between gives
+ *   bit-identical results to kkt_solve(k, ...): both run the same solve on the
+ *   same fp32 values.  Errors: as for kkt_solve (no K, no in_dtype here).
+ */
+kkt_status_t kkt_solve_tril(const float* A, const int32_t* cu_seqlens, int64_t num_seqs,
+                            int64_t B, int64_t T, int64_t H, int64_t chunk_size,
+                            kkt_dtype_t out_dtype, void* out, hipStream_t stream);
+
 /* Text of the last non-OK status returned on the calling thread ("" if none).
  * The pointer stays valid until the next kkt_* call on the same thread. */
 const char* kkt_last_error(void);

@@ -84,3 +84,48 @@ def compare(got: np.ndarray, ref: np.ndarray, out_dtype: str, cu_seqlens=None, l
         assert not np.any(bad), (f"{label}: {int(bad.sum())} elements beyond 1 ulp "
                                  f"(max {int(dist.max())} ulp, first at {np.argwhere(bad)[0].tolist()})")
     return stats
+
+
+# ---------------------------------------------------------------- A (first step of the unfused chain)
+U32 = 2.0 ** -24          # unit roundoff of fp32
+GATE_ULPS = 128           # exp of a gate difference of magnitude <= 50, see compare_A
+
+
+def a_scale(k64: np.ndarray, g, beta, cu_seqlens=None) -> np.ndarray:
+    """Per element of A, the magnitude its rounding errors are relative to:
+    |beta_i| * sum_k |k_ik k_jk| * exp(clamp(g_i - g_j)), i.e. the oracle's A
+    of |k| and |beta| (an upper bound of |A| whose terms are all positive)."""
+    return oracle.scaled_dot_ref(np.abs(k64), g, None if beta is None else np.abs(beta), cu_seqlens)
+
+
+def compare_A(got: np.ndarray, ref: np.ndarray, scale: np.ndarray, K: int, cu_seqlens=None,
+              label: str = "") -> dict:
+    """A in fp32 against the oracle's fp64 A.
+
+    Structure, bit-exact: +0.0 on and above the diagonal and in columns >= L.
+    Strictly lower elements: |gpu - ref| <= (K + 128) 2^-24 scale.  K 2^-24
+    bounds an fp32 dot product of length K (products of 16-bit inputs are
+    exact in fp32; fp32 inputs add one rounding per product, within the same
+    bound); 128 2^-24 covers the gate: the difference g_i - g_j (or g_i - g_0
+    and g_0 - g_j, |.| <= 25, in the factored form) rounds with an absolute
+    error up to 50 2^-24, exp turns that into the same relative error, and the
+    exp2 instruction with its scaling by log2(e) adds about as much again, plus
+    the few products with beta.
+    """
+    B, T, H, C = ref.shape
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    _diag, upper, lower = (np.broadcast_to(m[None, :, None, :], ref.shape)
+                           for m in structural_masks(T, cu_seqlens))
+    zero_region = ~lower
+    stats = {"label": label, "elements": int(ref.size)}
+    assert not np.any(np.isnan(got)), f"{label}: NaN in A (unwritten elements?)"
+    assert np.all(got.view(np.uint32)[zero_region] == 0), f"{label}: A is not +0.0 on/above the diagonal"
+    err = np.abs(got.astype(np.float64) - ref)
+    bound = (K + GATE_ULPS) * U32 * scale
+    ratio = np.where(lower, err / np.maximum(bound, 1e-300), 0.0)
+    stats.update(max_err_over_bound=float(ratio.max()),
+                 max_rel_to_scale=float(np.max(np.where(lower, err / np.maximum(scale, 1e-300), 0.0))))
+    bad = lower & (err > bound)
+    assert not np.any(bad), (f"{label}: {int(bad.sum())} elements of A beyond (K+128) 2^-24 scale, "
+                             f"worst ratio {stats['max_err_over_bound']:.2f} at {np.argwhere(bad)[0].tolist()}")
+    return stats

@@ -33,7 +33,8 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["kkt_last_error", "kkt_solve", "kkt_version"]
+    assert declared_functions() == ["kkt_last_error", "kkt_scaled_dot", "kkt_solve", "kkt_solve_tril",
+                                    "kkt_version"]
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -47,7 +48,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version(lib):
-    assert lib.kkt_version() == 200
+    assert lib.kkt_version() == 300
 
 
 def _call(lib, **over):
@@ -85,6 +86,64 @@ def test_invalid_arguments_rejected_on_host(lib, over, status, msg):
     assert msg in kkt.last_error()
 
 
+def _call_scaled_dot(lib, **over):
+    args = dict(k=16, g=None, beta=None, cu=None, num_seqs=0, B=1, T=64, H=1, K=128, chunk_size=64,
+                in_dtype=1, A=16, stream=None)
+    args.update(over)
+    return lib.kkt_scaled_dot(args["k"], args["g"], args["beta"], args["cu"], args["num_seqs"], args["B"],
+                              args["T"], args["H"], args["K"], args["chunk_size"], args["in_dtype"], args["A"],
+                              args["stream"])
+
+
+@pytest.mark.parametrize("over,status,msg", [
+    (dict(chunk_size=128), 2, "chunk_size"),
+    (dict(in_dtype=5), 1, "dtype"),
+    (dict(H=0), 1, ">= 1"),
+    (dict(K=96), 2, "K must be"),
+    (dict(cu=16, num_seqs=1, B=3), 1, "cu_seqlens"),
+    (dict(k=None), 1, "NULL"),
+    (dict(A=None), 1, "NULL"),
+    (dict(A=16 + 4), 1, "16-byte aligned"),
+    (dict(g=16 + 2), 1, "4-byte aligned"),
+])
+def test_scaled_dot_invalid_arguments(lib, over, status, msg):
+    from chunked_gated_delta_token_amd import kkt
+    assert _call_scaled_dot(lib, **over) == status
+    assert msg in kkt.last_error()
+
+
+def _call_solve_tril(lib, **over):
+    args = dict(A=16, cu=None, num_seqs=0, B=1, T=64, H=1, chunk_size=64, out_dtype=0, out=16, stream=None)
+    args.update(over)
+    return lib.kkt_solve_tril(args["A"], args["cu"], args["num_seqs"], args["B"], args["T"], args["H"],
+                              args["chunk_size"], args["out_dtype"], args["out"], args["stream"])
+
+
+@pytest.mark.parametrize("over,status,msg", [
+    (dict(chunk_size=16), 2, "chunk_size"),
+    (dict(out_dtype=7), 1, "dtype"),
+    (dict(B=0), 1, ">= 1"),
+    (dict(T=-5), 1, ">= 1"),
+    (dict(cu=16, num_seqs=0), 1, "cu_seqlens"),
+    (dict(A=None), 1, "NULL"),
+    (dict(out=None), 1, "NULL"),
+    (dict(A=16 + 8), 1, "16-byte aligned"),
+    (dict(cu=16 + 1, num_seqs=1), 1, "4-byte aligned"),
+])
+def test_solve_tril_invalid_arguments(lib, over, status, msg):
+    from chunked_gated_delta_token_amd import kkt
+    assert _call_solve_tril(lib, **over) == status
+    assert msg in kkt.last_error()
+
+
+def test_split_entry_points_empty_is_a_no_op(lib):
+    from chunked_gated_delta_token_amd import kkt
+    assert _call_scaled_dot(lib, T=0, k=None, A=None) == 0
+    assert kkt.last_error() == ""
+    assert _call_solve_tril(lib, T=0, A=None, out=None) == 0
+    assert kkt.last_error() == ""
+
+
 def test_empty_sequence_is_a_no_op(lib):
     from chunked_gated_delta_token_amd import kkt
     assert _call(lib, T=0, k=None, out=None) == 0
@@ -96,6 +155,12 @@ def test_python_binding_rejects_chunk_size():
     from chunked_gated_delta_token_amd import kkt
     with pytest.raises(ValueError):
         kkt.kkt_solve(torch.zeros(1, 4, 1, 128), chunk_size=32)
+    with pytest.raises(ValueError):
+        kkt.kkt_scaled_dot(torch.zeros(1, 4, 1, 128), chunk_size=128)
+    with pytest.raises(ValueError):
+        kkt.kkt_solve_tril(torch.zeros(1, 4, 1, 64), chunk_size=16)
+    with pytest.raises(ValueError):  # host tensor: no CPU fallback
+        kkt.kkt_solve_tril(torch.zeros(1, 4, 1, 64))
 
 
 def test_header_compiles_as_c_and_links(tmp_path, lib):
