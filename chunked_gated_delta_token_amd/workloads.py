@@ -16,7 +16,9 @@ for Gated DeltaNet inputs):
   3. u_beta ~ N(0, 1) of shape [B,T,H]; beta = sigmoid(u_beta), rounded to fp32;
   4. u_g ~ N(4, 1) of shape [B,T,H]; g = chunk-local cumulative sum of
      logsigmoid(u_g) = -log1p(exp(-u_g)), in fp64, restarting at every
-     64-token chunk and at every sequence start, rounded to fp32.
+     64-token chunk and at every sequence start, rounded to fp32.  The
+     per-token decays logsigmoid(u_g), rounded to fp32, are kept as g_raw
+     (the input of the entry point that sums them itself).
 
 Draws happen in that order from ``numpy.random.default_rng(seed)`` (PCG64);
 steps 3 and 4 are skipped when the workload has no beta / no gate.
@@ -122,6 +124,7 @@ class Inputs:
     g: Optional[np.ndarray]          # float32 [B,T,H] or None
     beta: Optional[np.ndarray]       # float32 [B,T,H] or None
     cu_seqlens: Optional[np.ndarray]  # int32 [N+1] or None
+    g_raw: Optional[np.ndarray] = None  # float32 [B,T,H]: the per-token log-decays g sums, or None
 
     def k64(self, sl=None) -> np.ndarray:
         src = self.k_store if sl is None else self.k_store[sl]
@@ -200,12 +203,13 @@ def generate(w, *, B=None, T=None, H=None, K=None, seed=None, in_dtype=None,
     if w.beta:
         u = rng.standard_normal((w.B, w.T, w.H))
         b_arr = (1.0 / (1.0 + np.exp(-u))).astype(np.float32)
-    g_arr = None
+    g_arr = g_raw = None
     if w.gate:
         u = rng.normal(4.0, 1.0, (w.B, w.T, w.H))
         logsig = -np.log1p(np.exp(-u))
         g_arr = chunk_local_cumsum(logsig, starts, w.T).astype(np.float32)
-    return Inputs(w, np.ascontiguousarray(k_store), g_arr, b_arr, cu)
+        g_raw = logsig.astype(np.float32)
+    return Inputs(w, np.ascontiguousarray(k_store), g_arr, b_arr, cu, g_raw)
 
 
 def chunk_geometry(T: int, cu_seqlens=None, chunk: int = CHUNK):

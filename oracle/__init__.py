@@ -65,6 +65,9 @@ def _load():
     lib.kkt_oracle_solve_tril.argtypes = [dp, ip, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                           ctypes.c_int64, ctypes.c_int64, dp]
     lib.kkt_oracle_solve_tril.restype = ctypes.c_int
+    lib.kkt_oracle_chunk_cumsum.argtypes = [dp, ip, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                            ctypes.c_int64, ctypes.c_int64, dp]
+    lib.kkt_oracle_chunk_cumsum.restype = ctypes.c_int
     lib.kkt_oracle_num_threads.argtypes = []
     lib.kkt_oracle_num_threads.restype = ctypes.c_int
     _lib = lib
@@ -132,6 +135,31 @@ def solve_tril_ref(A, cu_seqlens=None, chunk_size: int = 64) -> np.ndarray:
     if rc != 0:
         raise ValueError(f"kkt_oracle_solve_tril failed with code {rc}")
     return out
+
+
+def chunk_cumsum_ref(a, cu_seqlens=None, chunk_size: int = 64) -> np.ndarray:
+    """Chunk-local inclusive cumulative sum of a per-token log-decay ``a``
+    [B,T,H] (fp64), restarted at every chunk: the gate the op takes."""
+    lib = _load()
+    a64 = np.ascontiguousarray(a, dtype=np.float64)
+    if a64.ndim != 3:
+        raise ValueError("a must be [B,T,H]")
+    B, T, H = a64.shape
+    cu, num_seqs = _cu(cu_seqlens)
+    out = np.zeros_like(a64)
+    rc = lib.kkt_oracle_chunk_cumsum(_ptr(a64, ctypes.c_double), _ptr(cu, ctypes.c_int32), num_seqs,
+                                     B, T, H, chunk_size, _ptr(out, ctypes.c_double))
+    if rc != 0:
+        raise ValueError(f"kkt_oracle_chunk_cumsum failed with code {rc}")
+    return out
+
+
+def kkt_solve_gate_cumsum_ref(k, a, beta=None, cu_seqlens=None, chunk_size: int = 64,
+                              clamp_gate: bool = True):
+    """The fused op fed with the per-token log-decay ``a`` instead of its
+    chunk-local sum: returns (rows of (I + A)^{-1}, the summed gate g)."""
+    g = chunk_cumsum_ref(a, cu_seqlens, chunk_size)
+    return kkt_solve_ref(k, g, beta, cu_seqlens, chunk_size, clamp_gate), g
 
 
 def kkt_solve_ref(k, g=None, beta=None, cu_seqlens=None, chunk_size: int = 64,

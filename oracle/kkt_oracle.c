@@ -38,6 +38,12 @@
  * The two steps of the unfused chain are also exposed on their own
  * (kkt_oracle_scaled_dot: A; kkt_oracle_solve_tril: (I + A)^{-1} from A).
  *
+ * The gate g the op takes is the chunk-local cumulative log-decay: the running
+ * sum, restarted at every chunk, of a per-token log-decay a_t.  The pages use
+ * g only in that summed form; kkt_oracle_chunk_cumsum forms it from a_t by
+ * that definition (g[t0 + i] = a[t0] + ... + a[t0 + i]), for the entry point
+ * that takes a_t itself.
+ *
  * The inverse is taken by generic Gauss-Jordan elimination with partial
  * pivoting on the augmented matrix [M | I].  It deliberately does not use the
  * fact that M is unit lower triangular, so that it is an independent route to
@@ -242,6 +248,36 @@ static int check_and_list_chunks(const int32_t* cu_seqlens, int64_t num_seqs, in
         }
     }
     out->n = n;
+    return KKT_ORACLE_OK;
+}
+
+/*
+ * Chunk-local inclusive cumulative sum of a per-token log-decay.
+ *   a          [B,T,H] fp64
+ *   cu_seqlens, num_seqs, B, T, H, chunk_size: as for kkt_oracle_solve
+ *   g_out      [B,T,H] fp64: for every chunk (t0, L) and head h,
+ *              g_out[t0 + i][h] = sum_{s=0..i} a[t0 + s][h]   (i < L),
+ *              summed left to right in fp64
+ * Returns 0, or a nonzero KKT_ORACLE_* code.
+ */
+int kkt_oracle_chunk_cumsum(const double* a, const int32_t* cu_seqlens, int64_t num_seqs,
+                            int64_t B, int64_t T, int64_t H, int64_t chunk_size, double* g_out)
+{
+    if (a == NULL || g_out == NULL) return KKT_ORACLE_BAD_ARGUMENT;
+    chunk_list ch;
+    int status = check_and_list_chunks(cu_seqlens, num_seqs, B, T, H, chunk_size, &ch);
+    if (status != KKT_ORACLE_OK) return status;
+    for (int64_t c = 0; c < ch.n; ++c) {
+        for (int64_t h = 0; h < H; ++h) {
+            double run = 0.0;
+            for (int64_t i = 0; i < ch.len[c]; ++i) {
+                const int64_t idx = (ch.b[c] * T + ch.t0[c] + i) * H + h;
+                run += a[idx];
+                g_out[idx] = run;
+            }
+        }
+    }
+    free_chunks(&ch);
     return KKT_ORACLE_OK;
 }
 

@@ -424,3 +424,68 @@ def split_pin_composition(solve, scaled_dot, solve_tril):
 
 
 SPLIT_PINS = [split_pin_golden_A, split_pin_solve_tril_library_inverse, split_pin_composition]
+
+
+# --------------------------------------------------------------------------
+# The gate from the per-token log-decay: g is its running sum restarted at
+# every chunk.  These pins take (solve, cumsum), cumsum with the signature of
+# oracle.chunk_cumsum_ref.
+# --------------------------------------------------------------------------
+def _local_index(T, cu, chunk):
+    """Row index inside its chunk, counted from each sequence start."""
+    starts = [0, T] if cu is None else [int(x) for x in cu]
+    local = np.zeros(T, dtype=np.int64)
+    for s in range(len(starts) - 1):
+        for t in range(starts[s], starts[s + 1]):
+            local[t] = (t - starts[s]) % chunk
+    return local
+
+
+def cumsum_pin_constant_closed_form(solve, cumsum):
+    """A constant decay c gives g = c (i + 1) at local row i (exact in fp64
+    for c = -0.25 and i < 64), per batch row and per packed sequence."""
+    c = -0.25
+    for B, T, cu in ((2, 150, None), (1, 143, np.array([0, 5, 75, 75, 78, 142, 143], dtype=np.int32))):
+        H = 3
+        g = cumsum(np.full((B, T, H), c), cu)
+        exp = c * (_local_index(T, cu, CH) + 1.0)
+        assert np.array_equal(g, np.broadcast_to(exp[None, :, None], g.shape)), (B, T)
+
+
+def cumsum_pin_bruteforce(solve, cumsum):
+    """Random decays, small chunk sizes: every g[t] equals the explicit sum of
+    the decays from its chunk's first row to t."""
+    rng = np.random.default_rng(50)
+    for B, T, H, chunk, cu in ((2, 13, 2, 4, None),
+                               (1, 11, 3, 3, np.array([0, 2, 2, 9, 11], dtype=np.int32))):
+        a = rng.uniform(-1.0, 0.0, (B, T, H))
+        g = cumsum(a, cu, chunk)
+        local = _local_index(T, cu, chunk)
+        for b in range(B):
+            for t in range(T):
+                for h in range(H):
+                    ref = 0.0
+                    for s in range(t - local[t], t + 1):
+                        ref += a[b, s, h]
+                    assert abs(g[b, t, h] - ref) <= 1e-15 * max(1.0, abs(ref)), (b, t, h)
+
+
+def cumsum_pin_first_row_irrelevant(solve, cumsum):
+    """Only the differences g_i - g_j (i > j) enter A, and they sum the decays
+    of rows j+1 .. i: the decay of each chunk's first row changes nothing,
+    the decay of any other row does."""
+    rng = np.random.default_rng(51)
+    B, T, H, K = 1, 150, 2, 16
+    k = _unit_keys(rng, B, T, H, K)
+    beta = rng.uniform(0.1, 0.9, (B, T, H))
+    a = rng.uniform(-0.2, 0.0, (B, T, H))
+    base = solve(k, cumsum(a), beta, None)
+    first = a.copy()
+    first[:, ::CH] = rng.uniform(-3.0, 3.0, first[:, ::CH].shape)
+    assert np.allclose(solve(k, cumsum(first), beta, None), base, rtol=1e-12, atol=1e-13)
+    other = a.copy()
+    other[:, 1::CH] -= 0.5
+    assert not np.allclose(solve(k, cumsum(other), beta, None), base, rtol=1e-6, atol=1e-8)
+
+
+CUMSUM_PINS = [cumsum_pin_constant_closed_form, cumsum_pin_bruteforce, cumsum_pin_first_row_irrelevant]

@@ -46,6 +46,16 @@ MUTANTS = [
     ("solve_tril_reads_upper", "M[i * L + j] = (i == j) ? 1.0 : ((j < i) ? arow[j] : 0.0);",
      "M[i * L + j] = (i == j) ? 1.0 : arow[j];"),
     ("key_of_previous_token", "const double* kj = k + tj * K;", "const double* kj = k + (tj >= H ? tj - H : tj) * K;"),
+    # the gate from per-token decays: exclusive instead of inclusive sum; the
+    # sum not restarted at chunk starts inside a sequence; head 0's decays for
+    # every head
+    ("cumsum_exclusive", "run += a[idx];\n                g_out[idx] = run;",
+     "g_out[idx] = run;\n                run += a[idx];"),
+    ("cumsum_restarts_per_sequence_only", "            double run = 0.0;\n            for (int64_t i = 0; i < ch.len[c]",
+     "            double run = (c > 0 && ch.b[c - 1] == ch.b[c] && ch.len[c - 1] == chunk_size)"
+     " ? g_out[(ch.b[c] * T + ch.t0[c] - 1) * H + h] : 0.0;\n"
+     "            for (int64_t i = 0; i < ch.len[c]"),
+    ("cumsum_head_zero", "                run += a[idx];", "                run += a[idx - h];"),
 ]
 
 
@@ -67,6 +77,9 @@ def _build(src_text, tmpdir, name):
     lib.kkt_oracle_solve_tril.argtypes = [dp, ip, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                           ctypes.c_int64, ctypes.c_int64, dp]
     lib.kkt_oracle_solve_tril.restype = ctypes.c_int
+    lib.kkt_oracle_chunk_cumsum.argtypes = [dp, ip, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                            ctypes.c_int64, ctypes.c_int64, dp]
+    lib.kkt_oracle_chunk_cumsum.restype = ctypes.c_int
     return lib
 
 
@@ -104,6 +117,21 @@ def _split(lib):
     return scaled_dot, solve_tril
 
 
+def _cumsum(lib):
+    def cumsum(a, cu=None, chunk_size=64):
+        a = np.ascontiguousarray(a, dtype=np.float64)
+        B, T, H = a.shape
+        cu = None if cu is None else np.ascontiguousarray(cu, dtype=np.int32)
+        out = np.zeros_like(a)
+        rc = lib.kkt_oracle_chunk_cumsum(_ptr(a, ctypes.c_double), _ptr(cu, ctypes.c_int32),
+                                         0 if cu is None else len(cu) - 1, B, T, H, chunk_size,
+                                         _ptr(out, ctypes.c_double))
+        if rc != 0:
+            raise ValueError(rc)
+        return out
+    return cumsum
+
+
 def _solver(lib):
     ptr = _ptr
 
@@ -137,6 +165,8 @@ def test_unmutated_copy_passes(tmpdir):
         pin(solve)
     for pin in oracle_pins.SPLIT_PINS:
         pin(solve, *_split(lib))
+    for pin in oracle_pins.CUMSUM_PINS:
+        pin(solve, _cumsum(lib))
 
 
 @pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
@@ -156,6 +186,12 @@ def test_mutant_is_caught(tmpdir, name, old, new):
     for pin in oracle_pins.SPLIT_PINS:
         try:
             pin(solve, scaled_dot, solve_tril)
+        except (AssertionError, ValueError, IndexError, FloatingPointError):
+            caught.append(pin.__name__)
+    cumsum = _cumsum(lib)
+    for pin in oracle_pins.CUMSUM_PINS:
+        try:
+            pin(solve, cumsum)
         except (AssertionError, ValueError, IndexError, FloatingPointError):
             caught.append(pin.__name__)
     assert caught, f"mutant {name} passed every pin"

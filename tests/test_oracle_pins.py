@@ -22,6 +22,23 @@ def test_split_pin(pin):
         lambda A, cu=None: oracle.solve_tril_ref(A, cu))
 
 
+@pytest.mark.parametrize("pin", oracle_pins.CUMSUM_PINS, ids=lambda f: f.__name__)
+def test_cumsum_pin(pin):
+    pin(_solve, lambda a, cu=None, chunk=64: oracle.chunk_cumsum_ref(a, cu, chunk))
+
+
+@pytest.mark.parametrize("name", ["T2000_H8_bf16_bf16"])
+def test_cumsum_agrees_with_the_input_recipe(name):
+    """The recipe's gate (summed in fp64, then rounded to fp32) and the
+    oracle's chunk-local sum of the recipe's fp32 decays agree to the fp32
+    rounding of both; packed sequences restart the sum too."""
+    for lengths in (None, [70, 1, 0, 129, 300]):
+        inp = workloads.generate(name, T=None if lengths else 300, H=3, lengths=lengths)
+        g = oracle.chunk_cumsum_ref(inp.g_raw, inp.cu_seqlens)
+        prefix_abs = oracle.chunk_cumsum_ref(np.abs(inp.g_raw.astype(np.float64)), inp.cu_seqlens)
+        assert np.all(np.abs(g - inp.g) <= 2.0 ** -23 * (np.abs(g) + prefix_abs) + 1e-30)
+
+
 def test_clamp_flag_is_the_pure_definition_when_off():
     # with the clamp off, a gate difference of 60 is exp(60)
     k = np.ones((1, 2, 1, 1))
