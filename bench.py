@@ -41,8 +41,10 @@ MALL_BYTES = 256 << 20
 KERNEL_SRC = os.path.join(ROOT, "chunked_gated_delta_token_amd", "csrc", "kkt_solve.hip")
 # the kernel each op launches (chain: both of the unfused steps)
 KERNELS = {"fused": "kkt_solve_kernel", "scaled_dot": "kkt_scaled_dot_kernel",
-           "solve_tril": "kkt_solve_tril_kernel", "chain": "kkt_scaled_dot_kernel+kkt_solve_tril_kernel"}
-ENTRY = {"fused": "kkt_solve", "scaled_dot": "kkt_scaled_dot", "solve_tril": "kkt_solve_tril"}
+           "solve_tril": "kkt_solve_tril_kernel", "chain": "kkt_scaled_dot_kernel+kkt_solve_tril_kernel",
+           "gate_cumsum": "kkt_solve_kernel"}
+ENTRY = {"fused": "kkt_solve", "scaled_dot": "kkt_scaled_dot", "solve_tril": "kkt_solve_tril",
+         "gate_cumsum": "kkt_solve_gate_cumsum"}
 
 
 def traffic_file(op: str, workload: str) -> str:
@@ -67,7 +69,8 @@ def chunk_lengths(w, cu_seqlens):
 def algorithmic_bytes(w, n_tokens: int, op: str = "fused", cu_seqlens=None) -> int:
     """Minimum bytes one step must move.  fused and chain: k once, g and beta
     once (when given), the output once (the chain's A round trip is its own
-    overhead, not the step's work).  scaled_dot: k, g, beta, and A in fp32.
+    overhead, not the step's work).  gate_cumsum: as fused, plus the summed
+    gate written back.  scaled_dot: k, g, beta, and A in fp32.
     solve_tril: the strictly lower entries of A (L (L-1) / 2 fp32 values per
     chunk and head) and the output.  (cu_seqlens, a few bytes, is ignored.)"""
     H, K = w.H, w.K
@@ -75,6 +78,8 @@ def algorithmic_bytes(w, n_tokens: int, op: str = "fused", cu_seqlens=None) -> i
     out = H * 64 * ESIZE[w.out_dtype]
     if op in ("fused", "chain"):
         return (k_gb + out) * n_tokens
+    if op == "gate_cumsum":
+        return (k_gb + out + H * 4) * n_tokens
     if op == "scaled_dot":
         return (k_gb + H * 64 * 4) * n_tokens
     lower = sum(L * (L - 1) // 2 for L in chunk_lengths(w, cu_seqlens)) * 4 * H
@@ -120,6 +125,8 @@ def cpu_baseline(inp, nbytes: int, budget_s: float, op: str = "fused"):
     while True:
         if op == "fused":
             oracle.kkt_solve_ref(k64, g64, b64, cu)
+        elif op == "gate_cumsum":
+            oracle.kkt_solve_gate_cumsum_ref(k64, inp.g_raw, b64, cu)
         elif op == "scaled_dot":
             oracle.scaled_dot_ref(k64, g64, b64, cu)
         elif op == "solve_tril":
@@ -131,7 +138,7 @@ def cpu_baseline(inp, nbytes: int, budget_s: float, op: str = "fused"):
         if el >= budget_s:
             break
     what = {"fused": "the fused op", "scaled_dot": "A alone", "solve_tril": "the solve of a given A",
-            "chain": "A, then its solve"}[op]
+            "chain": "A, then its solve", "gate_cumsum": "gate sum, then the fused op"}[op]
     return {"value": nbytes * reps / el / 1e9, "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
             "sample": f"the whole workload ({what}), {reps} calls in {el:.1f} s (fp64, OpenMP over chunk-head tiles)"}
 
@@ -174,7 +181,7 @@ def summarize_traffic(dirs, copy_bytes: int, op: str, workload: str):
     if copy_bytes <= 0:
         raise SystemExit("--copy-bytes is required")
     if op == "chain":
-        raise SystemExit("traffic is summarized per kernel: use --op fused, scaled_dot or solve_tril")
+        raise SystemExit("traffic is summarized per kernel: use --op fused, gate_cumsum, scaled_dot or solve_tril")
     kname = KERNELS[op]
     op_fetch = statistics.median(_counter_values(dirs[0], "FETCH_SIZE", kname))
     op_write = statistics.median(_counter_values(dirs[1], "WRITE_SIZE", kname))
@@ -217,7 +224,7 @@ def main():
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=None)
-    ap.add_argument("--op", choices=["fused", "scaled_dot", "solve_tril", "chain"], default="fused",
+    ap.add_argument("--op", choices=["fused", "gate_cumsum", "scaled_dot", "solve_tril", "chain"], default="fused",
                     help="what one step runs (default: the fused op)")
     ap.add_argument("--timing", choices=["graph", "eager"], default="graph")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -269,6 +276,10 @@ def main():
     cu0 = None if inp.cu_seqlens is None else torch.from_numpy(inp.cu_seqlens).to(dev)
     n_tokens = w.B * w.T
     op = args.op
+    if op == "gate_cumsum":
+        if inp.g_raw is None:
+            raise SystemExit(f"--op gate_cumsum needs a workload with a gate ({name} has none)")
+        g0 = torch.from_numpy(inp.g_raw).to(dev)  # per-token log-decays, summed by the kernel
     nbytes = algorithmic_bytes(w, n_tokens, op, inp.cu_seqlens)
     num_seqs = 0 if inp.cu_seqlens is None else len(inp.cu_seqlens) - 1
     stream = torch.cuda.Stream(dev)
@@ -285,7 +296,7 @@ def main():
     # bytes one buffer set occupies (every tensor a step touches)
     a_bytes = int(np.prod(shape)) * 4
     out_bytes = int(np.prod(shape)) * ESIZE[w.out_dtype]
-    set_bytes = {"fused": nbytes, "scaled_dot": nbytes, "chain": nbytes + a_bytes,
+    set_bytes = {"fused": nbytes, "gate_cumsum": nbytes, "scaled_dot": nbytes, "chain": nbytes + a_bytes,
                  "solve_tril": a_bytes + out_bytes}[op]
     R = max(2, -(-2 * MALL_BYTES // set_bytes))
     sets = []
@@ -299,6 +310,8 @@ def main():
             s_["A"] = A0.clone()
         if op != "scaled_dot":
             s_["out"] = torch.empty(shape, dtype=tdt[w.out_dtype], device=dev)
+        if op == "gate_cumsum":
+            s_["g_out"] = torch.empty(shape[:3], dtype=torch.float32, device=dev)
         sets.append(s_)
     del k0, g0, b0
     if op == "solve_tril":
@@ -315,6 +328,8 @@ def main():
                  kdt[w.in_dtype])
         if op == "fused":
             return [(lib.kkt_solve, kargs + (kdt[w.out_dtype], ptr(s_["out"]), sp))]
+        if op == "gate_cumsum":
+            return [(lib.kkt_solve_gate_cumsum, kargs + (kdt[w.out_dtype], ptr(s_["out"]), ptr(s_["g_out"]), sp))]
         tril = (lib.kkt_solve_tril, (ptr(s_["A"]), ptr(s_["cu"]), num_seqs, w.B, w.T, w.H, 64, kdt[w.out_dtype],
                                      ptr(s_.get("out")), sp))
         dot = (lib.kkt_scaled_dot, kargs + (ptr(s_["A"]), sp))
@@ -389,6 +404,7 @@ def main():
                          for s in range(num_seqs)) if num_seqs else w.B * (-(-w.T // 64)))
     value = nbytes / (ms_per_step * 1e-3) / 1e9
     metric = METRIC if op == "fused" else {
+        "gate_cumsum": "fused KKT+solve with the chunk-local gate sum in the kernel ms/iter & achieved HBM GB/s, 1 GPU",
         "scaled_dot": "KKT A alone (first step of the unfused chain) ms/iter & achieved HBM GB/s, 1 GPU",
         "solve_tril": "solve of a given A (second step of the unfused chain) ms/iter & achieved HBM GB/s, 1 GPU",
         "chain": "unfused two-step chain (A through HBM) ms/iter & GB/s of the fused op's bytes, 1 GPU"}[op]

@@ -54,7 +54,7 @@
 
 #include "kkt_solve.h"
 
-#define KKT_VERSION_NUMBER 300  // 0.3.0
+#define KKT_VERSION_NUMBER 400  // 0.4.0
 
 namespace {
 
@@ -171,6 +171,17 @@ template <> __device__ __forceinline__ f32x4 gram_step<Elt::F32>(u32x4 a, u32x4 
 }
 
 // ---------------------------------------------------------------- launch arguments
+// How workgroups map to tiles.  The hardware hands workgroups to the 8 XCDs
+// round-robin (workgroup w runs on XCD w % 8), and each XCD has its own L2.
+//   kHardwareOrder:   tile group = workgroup index.
+//   kContiguous:      each XCD takes one contiguous range of tile groups.
+//   kChunkRoundRobin: the groups_per_chunk workgroups that cover all heads of
+//                     one chunk run on one XCD, one after another, and chunks
+//                     go round-robin over the XCDs.  The heads of a token
+//                     share cache lines of g, beta (and the summed gate), so
+//                     each such line is then fetched and written by one L2.
+enum XcdOrder { kHardwareOrder = 0, kContiguous = 1, kChunkRoundRobin = 2 };
+
 struct KernelArgs {
     const void* k;
     const float* g;
@@ -184,7 +195,10 @@ struct KernelArgs {
     int32_t n_tiles;            // tiles in the grid (an upper bound for varlen)
     uint32_t k_row_bytes;       // bytes between consecutive tokens of one head in k
     uint32_t o_row_bytes;       // bytes between consecutive tokens of one head in out
-    int32_t xcd_remap;          // 1: give each XCD one contiguous range of tiles
+    int32_t xcd_order;          // workgroup -> tile order, one of the XcdOrder values
+    int32_t groups_per_chunk;   // workgroups that cover the heads of one chunk (order kChunkRoundRobin)
+    int32_t gate_cumsum;        // 1: g holds per-token log-decays, summed per chunk in the kernel
+    float* g_out;               // with gate_cumsum: where the summed gate goes, or nullptr
 };
 
 // ---------------------------------------------------------------- tile map (a1)
@@ -251,15 +265,19 @@ __device__ __forceinline__ void run_tile(const KernelArgs& args, WaveLds* lds_al
     const int m = lane % 16;   // row inside a 16-row block (A operand) / column (D layout)
     WaveLds& lds = lds_all[wave];
 
-    // Workgroup order.  Workgroups are dispatched round-robin over the 8 XCDs;
-    // with xcd_remap each XCD gets one contiguous range of tiles instead.
+    // Workgroup order (see XcdOrder); both remaps are permutations of
+    // [0, n_groups).
     const uint32_t n_groups = gridDim.x;
     const uint32_t hw = blockIdx.x;
+    const uint32_t xcd = hw % 8, slot = hw / 8;
     uint32_t group = hw;
-    if (args.xcd_remap) {
-        const uint32_t xcd = hw % 8, slot = hw / 8;
+    if (args.xcd_order == kContiguous) {
         const uint32_t per = n_groups / 8, extra = n_groups % 8;
         group = (xcd < extra) ? xcd * (per + 1) + slot : extra * (per + 1) + (xcd - extra) * per + slot;
+    } else if (args.xcd_order == kChunkRoundRobin) {
+        // whole rounds of 8 chunks; the remainder keeps the hardware order
+        const uint32_t G = (uint32_t)args.groups_per_chunk;
+        if (hw < (n_groups / (8u * G)) * (8u * G)) group = ((slot / G) * 8u + xcd) * G + slot % G;
     }
     const uint32_t tile_id = group * kWavesPerGroup + wave;
     if (tile_id >= (uint32_t)args.n_tiles) return;  // wave-uniform
@@ -348,6 +366,24 @@ __device__ __forceinline__ void run_tile(const KernelArgs& args, WaveLds* lds_al
             }
         }
         __builtin_amdgcn_sched_barrier(0);
+
+        // ---- gate from per-token log-decays (kkt_solve_gate_cumsum): the
+        // gate is their running sum from the chunk's first row, an inclusive
+        // scan across the wave (rows >= L hold 0 and come after every valid
+        // row).  It needs only g, the first load issued, so it runs while the
+        // K tile is still arriving.
+        if (has_g && args.gate_cumsum) {
+#pragma unroll
+            for (int d = 1; d < kWave; d <<= 1) {
+                const float up = __shfl_up(gv, d, kWave);
+                if (lane >= d) gv += up;
+            }
+            if (args.g_out != nullptr) {
+                const uint32_t span = (uint32_t)(L - 1) * (uint32_t)H * 4u + 4u;
+                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, gv), make_rsrc(args.g_out + tok, span),
+                                                      (uint32_t)lane * (uint32_t)H * 4u, 0, 0);
+            }
+        }
 
         // ---- a4: Gram blocks.  Block (i, j): lane (q, n=m) holds rows 16i + 4q + r, column 16j + n.
         auto gram = [&](int i, int j) -> f32x4 {
@@ -685,9 +721,12 @@ bool valid_dtype(int d) { return d == KKT_DTYPE_F32 || d == KKT_DTYPE_BF16 || d 
 int64_t dtype_bytes(kkt_dtype_t d) { return d == KKT_DTYPE_F32 ? 4 : 2; }
 
 // Grids up to this many workgroups use the XCD-contiguous tile order; larger
-// ones keep the hardware's round-robin order, which spreads each XCD's
-// concurrent accesses over the whole tensor.
+// ones keep chunks in round-robin order over the XCDs (each XCD's concurrent
+// accesses spread over the whole tensor), with all heads of a chunk on one XCD.
 constexpr int64_t kRemapMaxGroups = 1024;
+#ifndef KKT_LARGE_GRID_ORDER
+#define KKT_LARGE_GRID_ORDER kChunkRoundRobin
+#endif
 
 // Checks shared by every entry point and the launch geometry.  in_row_bytes
 // and out_row_bytes are the strides between consecutive tokens of one head.
@@ -740,7 +779,10 @@ kkt_status_t setup(KernelArgs& a, const void* in, const float* g, const float* b
     a.k_row_bytes = (uint32_t)in_row_bytes;
     a.o_row_bytes = (uint32_t)out_row_bytes;
     const int64_t groups = (n_tiles + kWavesPerGroup - 1) / kWavesPerGroup;
-    a.xcd_remap = groups <= kRemapMaxGroups ? 1 : 0;
+    a.xcd_order = groups <= kRemapMaxGroups ? kContiguous : KKT_LARGE_GRID_ORDER;
+    a.groups_per_chunk = (int32_t)((H + kWavesPerGroup - 1) / kWavesPerGroup);
+    a.gate_cumsum = 0;
+    a.g_out = nullptr;
     return KKT_OK;
 }
 
@@ -774,6 +816,37 @@ extern "C" kkt_status_t kkt_solve(const void* k, const float* g, const float* be
     st = setup(a, k, g, beta, cu_seqlens, num_seqs, B, T, H, H * K * dtype_bytes(in_dtype),
                H * kChunk * dtype_bytes(out_dtype), out, stream);
     if (st != KKT_OK) return st;
+
+    hipError_t e;
+    switch (in_dtype) {
+    case KKT_DTYPE_F32: e = launch_fused_out<Elt::F32>(out_dtype, K, a, stream); break;
+    case KKT_DTYPE_BF16: e = launch_fused_out<Elt::BF16>(out_dtype, K, a, stream); break;
+    default: e = launch_fused_out<Elt::F16>(out_dtype, K, a, stream); break;
+    }
+    if (e != hipSuccess) return fail(KKT_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(e));
+    return KKT_OK;
+}
+
+extern "C" kkt_status_t kkt_solve_gate_cumsum(const void* k, const float* g_decay, const float* beta,
+                                              const int32_t* cu_seqlens, int64_t num_seqs,
+                                              int64_t B, int64_t T, int64_t H, int64_t K,
+                                              int64_t chunk_size, kkt_dtype_t in_dtype, kkt_dtype_t out_dtype,
+                                              void* out, float* g_out, hipStream_t stream)
+{
+    g_last_error.clear();
+    if (chunk_size != kChunk) return fail(KKT_ERR_UNSUPPORTED, "chunk_size must be 64");
+    if (!valid_dtype((int)in_dtype) || !valid_dtype((int)out_dtype)) return fail(KKT_ERR_INVALID_ARGUMENT, "unknown dtype");
+    kkt_status_t st = check_k_sizes(B, T, H, K, num_seqs, cu_seqlens);
+    if (st != KKT_OK) return st;
+    if (T == 0) return KKT_OK;
+    if (g_decay == nullptr) return fail(KKT_ERR_INVALID_ARGUMENT, "g_decay must not be NULL");
+    if ((reinterpret_cast<uintptr_t>(g_out) & 3u) != 0) return fail(KKT_ERR_INVALID_ARGUMENT, "g_out must be 4-byte aligned");
+    KernelArgs a;
+    st = setup(a, k, g_decay, beta, cu_seqlens, num_seqs, B, T, H, H * K * dtype_bytes(in_dtype),
+               H * kChunk * dtype_bytes(out_dtype), out, stream);
+    if (st != KKT_OK) return st;
+    a.gate_cumsum = 1;
+    a.g_out = g_out;
 
     hipError_t e;
     switch (in_dtype) {

@@ -26,6 +26,10 @@ SIGNATURES = {
                                  ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                  ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
                                  ctypes.c_void_p, ctypes.c_void_p]),
+    "kkt_solve_gate_cumsum": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                             ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                             ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "kkt_scaled_dot": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                       ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                       ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
@@ -155,6 +159,37 @@ def kkt_solve(k: torch.Tensor, g: Optional[torch.Tensor] = None, beta: Optional[
     if st != KKT_OK:
         raise KKTError(st, last_error())
     return out
+
+
+def kkt_solve_gate_cumsum(k: torch.Tensor, g_decay: torch.Tensor, beta: Optional[torch.Tensor] = None,
+                          cu_seqlens: Optional[torch.Tensor] = None, chunk_size: int = 64,
+                          output_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None,
+                          g_out: Optional[torch.Tensor] = None, return_gate: bool = False,
+                          stream: Optional[torch.cuda.Stream] = None):
+    """``kkt_solve`` fed with the per-token log-decay ``g_decay`` [B,T,H]
+    fp32: the kernel sums it within every chunk (the gate ``kkt_solve``
+    takes) before using it.  With ``return_gate`` (or a given ``g_out``) the
+    summed gate is written too and ``(out, g)`` is returned; ``g_out`` may be
+    ``g_decay`` itself (in-place sum)."""
+    if g_decay is None:
+        raise ValueError("g_decay is required (use kkt_solve without a gate)")
+    k, g_decay, beta, cu_seqlens, num_seqs = _k_inputs(k, g_decay, beta, cu_seqlens, chunk_size)
+    B, T, H, K = k.shape
+    odt = k.dtype if output_dtype is None else output_dtype
+    if odt not in _TORCH_TO_KKT:
+        raise TypeError(f"unsupported output dtype {odt}")
+    out = _out_tensor(out, (B, T, H, 64), odt, k.device)
+    if g_out is None and return_gate:
+        g_out = torch.empty((B, T, H), dtype=torch.float32, device=k.device)
+    elif g_out is not None:
+        g_out = _out_tensor(g_out, (B, T, H), torch.float32, k.device)
+    with torch.cuda.device(k.device):
+        st = load_library().kkt_solve_gate_cumsum(_ptr(k), _ptr(g_decay), _ptr(beta), _ptr(cu_seqlens), num_seqs,
+                                                  B, T, H, K, chunk_size, _TORCH_TO_KKT[k.dtype], _TORCH_TO_KKT[odt],
+                                                  _ptr(out), _ptr(g_out), _stream_ptr(stream, k.device))
+    if st != KKT_OK:
+        raise KKTError(st, last_error())
+    return (out, g_out) if g_out is not None else out
 
 
 def kkt_scaled_dot(k: torch.Tensor, g: Optional[torch.Tensor] = None, beta: Optional[torch.Tensor] = None,

@@ -97,6 +97,34 @@ kkt_status_t kkt_solve(const void* k, const float* g, const float* beta,
                        void* out, hipStream_t stream);
 
 /*
+ * kkt_solve_gate_cumsum: kkt_solve fed with the per-token log-decay instead
+ * of its chunk-local sum.  The gate g that kkt_solve takes is the running sum
+ * of a per-token log-decay a_t, restarted at every chunk (PR #135 page,
+ * user-facing-change section: g is the op's gate argument; this library
+ * reads it as that chunk-local sum).  Here the kernel forms the sum itself:
+ *
+ *   g[t0 + i] = a[t0] + a[t0 + 1] + ... + a[t0 + i]     (i < L, fp32)
+ *
+ * and then computes exactly what kkt_solve computes with that g.
+ *
+ *   g_decay    device, [B,T,H] fp32 per-token log-decay; must not be NULL.
+ *   g_out      device, [B,T,H] fp32, or NULL: receives the summed gate g of
+ *              every covered row (the later steps of the forward pass use
+ *              it).  It may be the same pointer as g_decay (the sum is then
+ *              done in place); it must not overlap any other argument.
+ *   The sum is a 6-level tree (a parallel inclusive scan over the 64 rows) in
+ *   fp32; its result differs from a left-to-right sum by rounding only.
+ *   kkt_solve(k, g_out, ...) on the g_out this call wrote gives bit-identical
+ *   output.  Everything else (arguments, alignment, errors) as for kkt_solve;
+ *   g_out must be 4-byte aligned.
+ */
+kkt_status_t kkt_solve_gate_cumsum(const void* k, const float* g_decay, const float* beta,
+                                   const int32_t* cu_seqlens, int64_t num_seqs,
+                                   int64_t B, int64_t T, int64_t H, int64_t K,
+                                   int64_t chunk_size, kkt_dtype_t in_dtype, kkt_dtype_t out_dtype,
+                                   void* out, float* g_out, hipStream_t stream);
+
+/*
  * kkt_scaled_dot: the first step of the unfused two-step path on its own
  * (PR #135 page, PR description: the fused op replaces
  * chunk_scaled_dot_kkt_fwd followed by solve_tril; the first of those forms A).

@@ -33,8 +33,8 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["kkt_last_error", "kkt_scaled_dot", "kkt_solve", "kkt_solve_tril",
-                                    "kkt_version"]
+    assert declared_functions() == ["kkt_last_error", "kkt_scaled_dot", "kkt_solve", "kkt_solve_gate_cumsum",
+                                    "kkt_solve_tril", "kkt_version"]
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -48,7 +48,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version(lib):
-    assert lib.kkt_version() == 300
+    assert lib.kkt_version() == 400
 
 
 def _call(lib, **over):
@@ -112,6 +112,32 @@ def test_scaled_dot_invalid_arguments(lib, over, status, msg):
     assert msg in kkt.last_error()
 
 
+def _call_gate_cumsum(lib, **over):
+    args = dict(k=16, g=32, beta=None, cu=None, num_seqs=0, B=1, T=64, H=1, K=128, chunk_size=64,
+                in_dtype=1, out_dtype=0, out=16, g_out=None, stream=None)
+    args.update(over)
+    return lib.kkt_solve_gate_cumsum(args["k"], args["g"], args["beta"], args["cu"], args["num_seqs"], args["B"],
+                                     args["T"], args["H"], args["K"], args["chunk_size"], args["in_dtype"],
+                                     args["out_dtype"], args["out"], args["g_out"], args["stream"])
+
+
+@pytest.mark.parametrize("over,status,msg", [
+    (dict(chunk_size=32), 2, "chunk_size"),
+    (dict(out_dtype=9), 1, "dtype"),
+    (dict(K=48), 2, "K must be"),
+    (dict(T=-1), 1, ">= 1"),
+    (dict(g=None), 1, "g_decay"),
+    (dict(k=None), 1, "NULL"),
+    (dict(out=16 + 4), 1, "16-byte aligned"),
+    (dict(g=32 + 2), 1, "4-byte aligned"),
+    (dict(g_out=64 + 1), 1, "4-byte aligned"),
+])
+def test_gate_cumsum_invalid_arguments(lib, over, status, msg):
+    from chunked_gated_delta_token_amd import kkt
+    assert _call_gate_cumsum(lib, **over) == status
+    assert msg in kkt.last_error()
+
+
 def _call_solve_tril(lib, **over):
     args = dict(A=16, cu=None, num_seqs=0, B=1, T=64, H=1, chunk_size=64, out_dtype=0, out=16, stream=None)
     args.update(over)
@@ -141,6 +167,8 @@ def test_split_entry_points_empty_is_a_no_op(lib):
     assert _call_scaled_dot(lib, T=0, k=None, A=None) == 0
     assert kkt.last_error() == ""
     assert _call_solve_tril(lib, T=0, A=None, out=None) == 0
+    assert kkt.last_error() == ""
+    assert _call_gate_cumsum(lib, T=0, k=None, g=None, out=None) == 0
     assert kkt.last_error() == ""
 
 

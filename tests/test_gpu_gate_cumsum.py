@@ -1,0 +1,122 @@
+"""GPU parity of ``kkt_solve_gate_cumsum``: the fused op fed with per-token
+log-decays, the chunk-local sum formed in the kernel.
+
+Against the oracle: the summed gate within 8 2^-24 of the running sum of
+|decay| (a 6-level fp32 tree sum has first-order error at most 6 2^-24 times
+that sum; 8 leaves room for the higher-order terms), and the output rows by
+the criteria of the fused op.  Against the library itself: ``kkt_solve`` on
+the gate this call wrote gives bit-identical rows.
+"""
+from __future__ import annotations
+
+import json
+
+import numpy as np
+import pytest
+
+import oracle
+from chunked_gated_delta_token_amd import workloads as W
+from tests._compare import compare
+from tests._gpu_util import TORCH_DT, from_device, load_kkt, say, to_device
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+GATE_BOUND_ULPS = 8
+
+
+@pytest.fixture(scope="module")
+def kkt():
+    return load_kkt()
+
+
+def run(kkt, inp: W.Inputs, out_dtype: str, with_gate_out=True, in_place=False):
+    k, _g, b, cu = to_device(inp)
+    a = torch.from_numpy(inp.g_raw).to(k.device)
+    B, T, H, _ = k.shape
+    out = torch.full((B, T, H, 64), float("nan"), dtype=TORCH_DT[out_dtype], device=k.device)
+    g_out = None
+    if in_place:
+        g_out = a
+    elif with_gate_out:
+        g_out = torch.full((B, T, H), float("nan"), dtype=torch.float32, device=k.device)
+    kkt.kkt_solve_gate_cumsum(k, a, b, cu, output_dtype=TORCH_DT[out_dtype], out=out, g_out=g_out)
+    torch.cuda.synchronize()
+    return from_device(out, out_dtype), (None if g_out is None else g_out.cpu().numpy())
+
+
+def check(kkt, inp: W.Inputs, out_dtype: str, label: str):
+    w = inp.workload
+    say(f"[case] gate_cumsum {label}: B={w.B} T={w.T} H={w.H} K={w.K} in={w.in_dtype} out={out_dtype} "
+        f"beta={inp.beta is not None} seqs={0 if inp.cu_seqlens is None else len(inp.cu_seqlens) - 1}")
+    got, g = run(kkt, inp, out_dtype)
+    X_ref, g_ref = oracle.kkt_solve_gate_cumsum_ref(inp.k64(), inp.g_raw, inp.beta, inp.cu_seqlens)
+    prefix_abs = oracle.chunk_cumsum_ref(np.abs(inp.g_raw.astype(np.float64)), inp.cu_seqlens)
+    err = np.abs(g.astype(np.float64) - g_ref)
+    bound = GATE_BOUND_ULPS * 2.0 ** -24 * prefix_abs
+    assert not np.any(np.isnan(g)), f"{label}: unwritten gate rows"
+    assert np.all(err <= bound), f"{label}: gate sum error {float(np.max(err / np.maximum(bound, 1e-300))):.2f} x bound"
+    stats = compare(got, X_ref, out_dtype, inp.cu_seqlens, label)
+    stats["gate_err_over_bound"] = float(np.max(err / np.maximum(bound, 1e-300)))
+    say("[ok] " + json.dumps(stats))
+    # the same gate through kkt_solve gives the same rows, bit for bit
+    k, _g, b, cu = to_device(inp)
+    B, T, H, _ = k.shape
+    out2 = torch.full((B, T, H, 64), float("nan"), dtype=TORCH_DT[out_dtype], device=k.device)
+    kkt.kkt_solve(k, torch.from_numpy(g).to(k.device), b, cu, output_dtype=TORCH_DT[out_dtype], out=out2)
+    torch.cuda.synchronize()
+    view = np.uint32 if out_dtype == "f32" else np.uint16
+    assert np.array_equal(from_device(out2, out_dtype).view(view), got.view(view)), f"{label}: kkt_solve differs"
+
+
+GATED = [n for n, w in W.WORKLOADS.items() if w.gate]
+
+
+@pytest.mark.parametrize("name", GATED)
+def test_gate_cumsum_full_parity(kkt, name):
+    inp = W.generate(name)
+    check(kkt, inp, inp.workload.out_dtype, name)
+
+
+def test_gate_cumsum_varlen_workload_with_gate(kkt):
+    """The packed 12-sequence workload, drawn with a gate and beta."""
+    inp = W.generate("varlen12_T16384_H7_f32_f32", gate=True, beta=True)
+    check(kkt, inp, "f32", "varlen12 gated")
+
+
+@pytest.mark.parametrize("T", [1, 2, 63, 64, 65, 129])
+def test_gate_cumsum_lengths(kkt, T):
+    inp = W.generate("T256_H8_bf16_f32", B=2, T=T, H=3, seed=2000 + T, beta=bool(T % 2))
+    check(kkt, inp, "f32", f"T={T}")
+
+
+def test_gate_cumsum_varlen_short(kkt):
+    inp = W.generate("T256_H8_bf16_f32", lengths=[1, 2, 3, 0, 64, 65, 0, 130, 5] + [1, 3] * 40, H=3, seed=2100)
+    check(kkt, inp, "bf16", "varlen short")
+
+
+def test_gate_cumsum_strong_decay_takes_the_clamp(kkt):
+    """Decays of up to -3 per token: within-chunk gate differences reach
+    about -96, beyond the clamp."""
+    inp = W.generate("T256_H8_bf16_f32", T=200, H=2, seed=2200)
+    rng = np.random.default_rng(2201)
+    inp.g_raw = (-rng.uniform(0.0, 3.0, inp.g_raw.shape)).astype(np.float32)
+    check(kkt, inp, "f32", "strong decay")
+
+
+@pytest.mark.parametrize("in_dtype,out_dtype", [("f16", "f16"), ("f32", "bf16")])
+def test_gate_cumsum_dtypes(kkt, in_dtype, out_dtype):
+    inp = W.generate("T256_H8_bf16_f32", B=2, T=150, H=3, in_dtype=in_dtype, seed=2300)
+    check(kkt, inp, out_dtype, f"{in_dtype}->{out_dtype}")
+
+
+def test_gate_cumsum_in_place_and_without_gate_output(kkt):
+    """g_out == g_decay sums in place; leaving g_out NULL changes no row."""
+    inp = W.generate("T256_H8_bf16_f32", B=2, T=300, H=5, seed=2400)
+    say("[case] gate_cumsum in place / no gate output: B=2 T=300 H=5")
+    ref_X, ref_g = run(kkt, inp, "f32")
+    X_in, g_in = run(kkt, inp, "f32", in_place=True)
+    X_none, _ = run(kkt, inp, "f32", with_gate_out=False)
+    assert np.array_equal(g_in.view(np.uint32), ref_g.view(np.uint32))
+    assert np.array_equal(X_in.view(np.uint32), ref_X.view(np.uint32))
+    assert np.array_equal(X_none.view(np.uint32), ref_X.view(np.uint32))

@@ -102,6 +102,15 @@ def test_large_gate_spread(kkt):
     check(kkt, inp, "f32", "gate spread ~ -96")
 
 
+@pytest.mark.parametrize("T,H", [(38481, 8), (40000, 7)])
+def test_large_grid_tile_order(kkt, T, H):
+    """Grids above 1024 workgroups take the chunk-grouped XCD order: these
+    sizes leave a remainder of workgroups outside whole rounds, and with H=7
+    the workgroups straddle chunks."""
+    inp = W.generate("T256_H8_bf16_f32", T=T, H=H, seed=460 + H)
+    check(kkt, inp, "bf16", f"large grid T={T} H={H}")
+
+
 # ---------------------------------------------------------------- varlen
 VARLEN_CASES = {
     "tiny_and_empty": [1, 2, 3, 0, 64, 65, 0, 130, 5],
