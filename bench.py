@@ -42,7 +42,7 @@ KERNEL_SRC = os.path.join(ROOT, "chunked_gated_delta_token_amd", "csrc", "kkt_so
 # the kernel each op launches (chain: both of the unfused steps)
 KERNELS = {"fused": "kkt_solve_kernel", "scaled_dot": "kkt_scaled_dot_kernel",
            "solve_tril": "kkt_solve_tril_kernel", "chain": "kkt_scaled_dot_kernel+kkt_solve_tril_kernel",
-           "gate_cumsum": "kkt_solve_kernel"}
+           "gate_cumsum": "kkt_solve_gate_cumsum_kernel"}
 ENTRY = {"fused": "kkt_solve", "scaled_dot": "kkt_scaled_dot", "solve_tril": "kkt_solve_tril",
          "gate_cumsum": "kkt_solve_gate_cumsum"}
 
@@ -218,6 +218,79 @@ def summarize_traffic(dirs, copy_bytes: int, op: str, workload: str):
     print("\n".join(lines))
 
 
+def summarize_trace(directory: str, op: str, workload: str, run_log: str = None, plain_log: str = None):
+    """Write profiles/<entry>_<workload>.kernel_trace.txt from a rocprofv3
+    --kernel-trace --stats CSV directory: the op kernel's duration statistics
+    and launch resources, next to bench.py's own event time of the profiled
+    run (run_log) and of an unprofiled run (plain_log), when given."""
+    import csv
+    import glob
+    from chunked_gated_delta_token_amd import workloads as W
+    if op == "chain":
+        raise SystemExit("kernel traces are summarized per kernel: use --op fused, gate_cumsum, scaled_dot or solve_tril")
+    kname = KERNELS[op]
+    stats = [r for path in glob.glob(os.path.join(directory, "**", "*kernel_stats.csv"), recursive=True)
+             for r in csv.DictReader(open(path, newline="")) if f"::{kname}<" in r["Name"]]
+    if len(stats) != 1:
+        raise SystemExit(f"expected one kernel matching {kname} in {directory}, found {len(stats)}")
+    st = stats[0]
+    disp = None
+    for path in glob.glob(os.path.join(directory, "**", "*kernel_trace.csv"), recursive=True):
+        for r in csv.DictReader(open(path, newline="")):
+            if r["Kernel_Name"] == st["Name"]:
+                disp = r
+                break
+    w = W.WORKLOADS[workload]
+    cu = W.generate(workload).cu_seqlens if w.n_seqs else None
+    nbytes = algorithmic_bytes(w, w.B * w.T, op, cu)
+    avg = float(st["AverageNs"])
+
+    def event_us(log):
+        if not log or not os.path.exists(log):
+            return None
+        for line in open(log):
+            if line.startswith("{"):
+                d = json.loads(line)
+                return 1e3 * d["roofline"]["event_ms_per_step"]
+        return None
+
+    ev_prof, ev_plain = event_us(run_log), event_us(plain_log)
+    sel = f"--op {op} --workload {workload}"
+    lines = [
+        f"# rocprofv3 kernel trace: {kname}, workload {workload} ({w.B},{w.T},{w.H},{w.K}) "
+        f"{w.in_dtype} -> {w.out_dtype}; {nbytes} algorithmic bytes per launch",
+        "# commands (from /tmp, repository at $R; the last one wrote this file):",
+        f"#   rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o kt -- python -u $R/bench.py {sel} "
+        "--steps 200 --warmup 20 --no-cpu-baseline > <run_log>",
+        f"#   python -u $R/bench.py {sel} --no-cpu-baseline > <plain_log>",
+        f"#   python $R/bench.py --summarize-trace <dir> {sel} --run-log <run_log> --plain-log <plain_log>",
+        f"kernel_source_sha256_16: {source_digest()}",
+        f"kernel: {st['Name']}",
+        f"calls: {st['Calls']}",
+        f"average_ns: {avg:.1f}",
+        f"min_ns: {st['MinNs']}",
+        f"max_ns: {st['MaxNs']}",
+        f"stddev_ns: {float(st['StdDev']):.1f}",
+        f"share_of_gpu_time_percent: {st['Percentage']}",
+    ]
+    if disp is not None:
+        lines += [f"grid_x: {disp['Grid_Size_X']}", f"workgroup_x: {disp['Workgroup_Size_X']}",
+                  f"lds_bytes_per_workgroup: {disp['LDS_Block_Size']}", f"scratch_bytes: {disp['Scratch_Size']}",
+                  f"vgpr_count: {disp['VGPR_Count']}", f"sgpr_count: {disp['SGPR_Count']}"]
+    lines.append(f"algorithmic_GBs_at_average: {nbytes / avg:.1f}")
+    lines.append("# durations are device-side (dispatch start to end), eager warmup launches included")
+    if ev_prof is not None:
+        lines.append(f"bench_event_us_per_step_under_profiler: {ev_prof:.3f}")
+    if ev_plain is not None:
+        lines.append(f"bench_event_us_per_step_unprofiled: {ev_plain:.3f}")
+        lines.append(f"trace_average_vs_unprofiled_event: {avg / 1e3 / ev_plain - 1.0:+.3%}")
+    path = os.path.join(ROOT, "profiles", f"{ENTRY[op]}_{workload}.kernel_trace.txt")
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -236,7 +309,17 @@ def main():
     ap.add_argument("--summarize-traffic", nargs=4, metavar=("OP_FETCH", "OP_WRITE", "COPY_FETCH", "COPY_WRITE"),
                     help="write the HBM-traffic summary from four rocprofv3 --pmc output directories")
     ap.add_argument("--copy-bytes", type=int, default=0, help="size used by the copy-calibration runs")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="write the kernel-trace summary of --op from a rocprofv3 --kernel-trace --stats directory")
+    ap.add_argument("--run-log", help="bench.py output of the profiled run (with --summarize-trace)")
+    ap.add_argument("--plain-log", help="bench.py output of an unprofiled run (with --summarize-trace)")
     args = ap.parse_args()
+
+    if args.summarize_trace:
+        from chunked_gated_delta_token_amd import workloads as W
+        summarize_trace(args.summarize_trace, args.op, args.workload or W.BENCH_WORKLOAD, args.run_log,
+                        args.plain_log)
+        return
 
     if args.summarize_traffic:
         from chunked_gated_delta_token_amd import workloads as W

@@ -175,11 +175,13 @@ template <> __device__ __forceinline__ f32x4 gram_step<Elt::F32>(u32x4 a, u32x4 
 // round-robin (workgroup w runs on XCD w % 8), and each XCD has its own L2.
 //   kHardwareOrder:   tile group = workgroup index.
 //   kContiguous:      each XCD takes one contiguous range of tile groups.
-//   kChunkRoundRobin: the groups_per_chunk workgroups that cover all heads of
-//                     one chunk run on one XCD, one after another, and chunks
-//                     go round-robin over the XCDs.  The heads of a token
-//                     share cache lines of g, beta (and the summed gate), so
-//                     each such line is then fetched and written by one L2.
+//   kChunkRoundRobin: runs of 2^log2_group_run consecutive workgroups (the
+//                     ones that cover the heads of one chunk, when that count
+//                     is a power of two) run on one XCD, one after another,
+//                     and the runs go round-robin over the XCDs.  The heads of
+//                     a token share cache lines of g, beta (and the summed
+//                     gate), so each such line is then fetched and written by
+//                     one L2.
 enum XcdOrder { kHardwareOrder = 0, kContiguous = 1, kChunkRoundRobin = 2 };
 
 struct KernelArgs {
@@ -193,12 +195,13 @@ struct KernelArgs {
     int32_t H;
     int32_t chunks_per_row;
     int32_t n_tiles;            // tiles in the grid (an upper bound for varlen)
+    uint32_t n_groups;          // workgroups in the grid
     uint32_t k_row_bytes;       // bytes between consecutive tokens of one head in k
     uint32_t o_row_bytes;       // bytes between consecutive tokens of one head in out
     int32_t xcd_order;          // workgroup -> tile order, one of the XcdOrder values
-    int32_t groups_per_chunk;   // workgroups that cover the heads of one chunk (order kChunkRoundRobin)
-    int32_t gate_cumsum;        // 1: g holds per-token log-decays, summed per chunk in the kernel
-    float* g_out;               // with gate_cumsum: where the summed gate goes, or nullptr
+    int32_t log2_group_run;     // kChunkRoundRobin: log2 of the workgroups kept together on one XCD
+    uint32_t remap_groups;      // kChunkRoundRobin: workgroups in whole rounds (the rest keep their order)
+    float* g_out;               // gate-sum kernel: where the summed gate goes, or nullptr
 };
 
 // ---------------------------------------------------------------- tile map (a1)
@@ -248,7 +251,9 @@ __device__ Tile varlen_tile(const int32_t* __restrict__ cu, int32_t num_seqs, in
 }
 
 // ---------------------------------------------------------------- the kernel
-template <Mode MODE, Elt IN, Elt OUT, int K>
+// GATE_SUM: g holds per-token log-decays that the tile sums itself (a
+// separate instantiation, so the plain fused kernel carries none of it).
+template <Mode MODE, Elt IN, Elt OUT, int K, bool GATE_SUM = false>
 __device__ __forceinline__ void run_tile(const KernelArgs& args, WaveLds* lds_all)
 {
     constexpr int kInBytes = EltInfo<IN>::bytes;
@@ -266,19 +271,22 @@ __device__ __forceinline__ void run_tile(const KernelArgs& args, WaveLds* lds_al
     WaveLds& lds = lds_all[wave];
 
     // Workgroup order (see XcdOrder); both remaps are permutations of
-    // [0, n_groups).
-    const uint32_t n_groups = gridDim.x;
+    // [0, n_groups).  Computed without branches from kernel arguments only, so
+    // the argument loads are issued together.
+    // (the empty statement makes the tensor pointers live here, so that their
+    // loads are issued with the ones the order needs, in one round trip)
+    asm volatile("" ::"s"(args.k), "s"(args.out), "s"(args.g), "s"(args.beta));
+    const uint32_t n_groups = args.n_groups;
     const uint32_t hw = blockIdx.x;
     const uint32_t xcd = hw % 8, slot = hw / 8;
-    uint32_t group = hw;
-    if (args.xcd_order == kContiguous) {
-        const uint32_t per = n_groups / 8, extra = n_groups % 8;
-        group = (xcd < extra) ? xcd * (per + 1) + slot : extra * (per + 1) + (xcd - extra) * per + slot;
-    } else if (args.xcd_order == kChunkRoundRobin) {
-        // whole rounds of 8 chunks; the remainder keeps the hardware order
-        const uint32_t G = (uint32_t)args.groups_per_chunk;
-        if (hw < (n_groups / (8u * G)) * (8u * G)) group = ((slot / G) * 8u + xcd) * G + slot % G;
-    }
+    const uint32_t per = n_groups / 8, extra = n_groups % 8;
+    const uint32_t g_contiguous =
+        (xcd < extra) ? xcd * (per + 1) + slot : extra * (per + 1) + (xcd - extra) * per + slot;
+    const int lg = args.log2_group_run;
+    const uint32_t g_runs = (hw < args.remap_groups)
+        ? ((((slot >> lg) << 3) + xcd) << lg) | (slot & ((1u << lg) - 1u)) : hw;
+    const uint32_t group = (args.xcd_order == kContiguous) ? g_contiguous
+                         : (args.xcd_order == kChunkRoundRobin) ? g_runs : hw;
     const uint32_t tile_id = group * kWavesPerGroup + wave;
     if (tile_id >= (uint32_t)args.n_tiles) return;  // wave-uniform
 
@@ -372,7 +380,7 @@ __device__ __forceinline__ void run_tile(const KernelArgs& args, WaveLds* lds_al
         // scan across the wave (rows >= L hold 0 and come after every valid
         // row).  It needs only g, the first load issued, so it runs while the
         // K tile is still arriving.
-        if (has_g && args.gate_cumsum) {
+        if (GATE_SUM && has_g) {
 #pragma unroll
             for (int d = 1; d < kWave; d <<= 1) {
                 const float up = __shfl_up(gv, d, kWave);
@@ -617,6 +625,14 @@ void kkt_solve_kernel(const KernelArgs args)
     run_tile<Mode::Fused, IN, OUT, K>(args, lds_all);
 }
 
+template <Elt IN, Elt OUT, int K>
+__global__ __launch_bounds__(kWave * kWavesPerGroup)
+void kkt_solve_gate_cumsum_kernel(const KernelArgs args)
+{
+    __shared__ WaveLds lds_all[kWavesPerGroup];
+    run_tile<Mode::Fused, IN, OUT, K, true>(args, lds_all);
+}
+
 template <Elt IN, int K>
 __global__ __launch_bounds__(kWave * kWavesPerGroup)
 void kkt_scaled_dot_kernel(const KernelArgs args)
@@ -687,23 +703,31 @@ hipError_t launch(void (*kernel)(KernelArgs), const KernelArgs& a, hipStream_t s
     return hipGetLastError();
 }
 
-template <Elt IN, Elt OUT>
+template <Elt IN, Elt OUT, bool GATE_SUM>
 hipError_t launch_fused(int64_t K, const KernelArgs& a, hipStream_t stream)
 {
-    switch (K) {
-    case 64: return launch(kkt_solve_kernel<IN, OUT, 64>, a, stream);
-    case 128: return launch(kkt_solve_kernel<IN, OUT, 128>, a, stream);
-    default: return launch(kkt_solve_kernel<IN, OUT, 256>, a, stream);
+    if constexpr (GATE_SUM) {
+        switch (K) {
+        case 64: return launch(kkt_solve_gate_cumsum_kernel<IN, OUT, 64>, a, stream);
+        case 128: return launch(kkt_solve_gate_cumsum_kernel<IN, OUT, 128>, a, stream);
+        default: return launch(kkt_solve_gate_cumsum_kernel<IN, OUT, 256>, a, stream);
+        }
+    } else {
+        switch (K) {
+        case 64: return launch(kkt_solve_kernel<IN, OUT, 64>, a, stream);
+        case 128: return launch(kkt_solve_kernel<IN, OUT, 128>, a, stream);
+        default: return launch(kkt_solve_kernel<IN, OUT, 256>, a, stream);
+        }
     }
 }
 
-template <Elt IN>
+template <Elt IN, bool GATE_SUM = false>
 hipError_t launch_fused_out(kkt_dtype_t od, int64_t K, const KernelArgs& a, hipStream_t stream)
 {
     switch (od) {
-    case KKT_DTYPE_F32: return launch_fused<IN, Elt::F32>(K, a, stream);
-    case KKT_DTYPE_BF16: return launch_fused<IN, Elt::BF16>(K, a, stream);
-    default: return launch_fused<IN, Elt::F16>(K, a, stream);
+    case KKT_DTYPE_F32: return launch_fused<IN, Elt::F32, GATE_SUM>(K, a, stream);
+    case KKT_DTYPE_BF16: return launch_fused<IN, Elt::BF16, GATE_SUM>(K, a, stream);
+    default: return launch_fused<IN, Elt::F16, GATE_SUM>(K, a, stream);
     }
 }
 
@@ -779,9 +803,14 @@ kkt_status_t setup(KernelArgs& a, const void* in, const float* g, const float* b
     a.k_row_bytes = (uint32_t)in_row_bytes;
     a.o_row_bytes = (uint32_t)out_row_bytes;
     const int64_t groups = (n_tiles + kWavesPerGroup - 1) / kWavesPerGroup;
+    a.n_groups = (uint32_t)groups;
     a.xcd_order = groups <= kRemapMaxGroups ? kContiguous : KKT_LARGE_GRID_ORDER;
-    a.groups_per_chunk = (int32_t)((H + kWavesPerGroup - 1) / kWavesPerGroup);
-    a.gate_cumsum = 0;
+    // runs of the largest power of two <= the workgroups per chunk
+    const int64_t per_chunk = (H + kWavesPerGroup - 1) / kWavesPerGroup;
+    int lg = 0;
+    while ((2LL << lg) <= per_chunk && lg < 16) ++lg;
+    a.log2_group_run = lg;
+    a.remap_groups = (uint32_t)((groups >> (lg + 3)) << (lg + 3));
     a.g_out = nullptr;
     return KKT_OK;
 }
@@ -845,14 +874,13 @@ extern "C" kkt_status_t kkt_solve_gate_cumsum(const void* k, const float* g_deca
     st = setup(a, k, g_decay, beta, cu_seqlens, num_seqs, B, T, H, H * K * dtype_bytes(in_dtype),
                H * kChunk * dtype_bytes(out_dtype), out, stream);
     if (st != KKT_OK) return st;
-    a.gate_cumsum = 1;
     a.g_out = g_out;
 
     hipError_t e;
     switch (in_dtype) {
-    case KKT_DTYPE_F32: e = launch_fused_out<Elt::F32>(out_dtype, K, a, stream); break;
-    case KKT_DTYPE_BF16: e = launch_fused_out<Elt::BF16>(out_dtype, K, a, stream); break;
-    default: e = launch_fused_out<Elt::F16>(out_dtype, K, a, stream); break;
+    case KKT_DTYPE_F32: e = launch_fused_out<Elt::F32, true>(out_dtype, K, a, stream); break;
+    case KKT_DTYPE_BF16: e = launch_fused_out<Elt::BF16, true>(out_dtype, K, a, stream); break;
+    default: e = launch_fused_out<Elt::F16, true>(out_dtype, K, a, stream); break;
     }
     if (e != hipSuccess) return fail(KKT_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(e));
     return KKT_OK;
