@@ -193,12 +193,12 @@ def summarize_traffic(dirs, copy_bytes: int, op: str, workload: str):
     sel = f"--op {op} --workload {workload}"
     lines = [
         f"# HBM traffic of {kname}, workload {workload}",
-        "# commands (run from the repository root, then summarized by the last one):",
-        f"#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d <op_fetch> -- python bench.py {sel} --timing eager --steps 20 --warmup 2 --no-cpu-baseline",
-        f"#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d <op_write> -- python bench.py {sel} --timing eager --steps 20 --warmup 2 --no-cpu-baseline",
-        f"#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d <copy_fetch> -- python bench.py --copy-calibration {copy_bytes} --steps 20",
-        f"#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d <copy_write> -- python bench.py --copy-calibration {copy_bytes} --steps 20",
-        f"#   python bench.py --summarize-traffic <op_fetch> <op_write> <copy_fetch> <copy_write> --copy-bytes {copy_bytes} {sel}",
+        "# commands (from /tmp, repository at $R; each --pmc pass alone, the last command wrote this file):",
+        f"#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d <op_fetch> -o p -- python -u $R/bench.py {sel} --timing eager --steps 20 --warmup 2 --no-cpu-baseline",
+        f"#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d <op_write> -o p -- python -u $R/bench.py {sel} --timing eager --steps 20 --warmup 2 --no-cpu-baseline",
+        f"#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d <copy_fetch> -o p -- python -u $R/bench.py --copy-calibration {copy_bytes} --steps 20",
+        f"#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d <copy_write> -o p -- python -u $R/bench.py --copy-calibration {copy_bytes} --steps 20",
+        f"#   python $R/bench.py --summarize-traffic <op_fetch> <op_write> <copy_fetch> <copy_write> --copy-bytes {copy_bytes} {sel}",
         f"kernel_source_sha256_16: {source_digest()}",
         f"op_fetch_size_kib_median: {op_fetch:.1f}",
         f"op_write_size_kib_median: {op_write:.1f}",
@@ -234,12 +234,13 @@ def summarize_trace(directory: str, op: str, workload: str, run_log: str = None,
     if len(stats) != 1:
         raise SystemExit(f"expected one kernel matching {kname} in {directory}, found {len(stats)}")
     st = stats[0]
-    disp = None
+    disp, durations = None, []
     for path in glob.glob(os.path.join(directory, "**", "*kernel_trace.csv"), recursive=True):
         for r in csv.DictReader(open(path, newline="")):
             if r["Kernel_Name"] == st["Name"]:
-                disp = r
-                break
+                disp = disp or r
+                durations.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    durations = [d for _, d in sorted(durations)]
     w = W.WORKLOADS[workload]
     cu = W.generate(workload).cu_seqlens if w.n_seqs else None
     nbytes = algorithmic_bytes(w, w.B * w.T, op, cu)
@@ -279,11 +280,19 @@ def summarize_trace(directory: str, op: str, workload: str, run_log: str = None,
                   f"vgpr_count: {disp['VGPR_Count']}", f"sgpr_count: {disp['SGPR_Count']}"]
     lines.append(f"algorithmic_GBs_at_average: {nbytes / avg:.1f}")
     lines.append("# durations are device-side (dispatch start to end), eager warmup launches included")
+    if len(durations) >= 200:
+        import statistics
+        last = durations[-200:]
+        lines.append(f"median_ns: {statistics.median(durations):.1f}")
+        lines.append(f"timed_graph_replay_average_ns: {statistics.mean(last):.1f}  # the last 200 dispatches")
     if ev_prof is not None:
         lines.append(f"bench_event_us_per_step_under_profiler: {ev_prof:.3f}")
     if ev_plain is not None:
         lines.append(f"bench_event_us_per_step_unprofiled: {ev_plain:.3f}")
         lines.append(f"trace_average_vs_unprofiled_event: {avg / 1e3 / ev_plain - 1.0:+.3%}")
+        if len(durations) >= 200:
+            lines.append(f"timed_replay_average_vs_unprofiled_event: "
+                         f"{statistics.mean(durations[-200:]) / 1e3 / ev_plain - 1.0:+.3%}")
     path = os.path.join(ROOT, "profiles", f"{ENTRY[op]}_{workload}.kernel_trace.txt")
     os.makedirs(os.path.dirname(path), exist_ok=True)
     with open(path, "w") as f:
