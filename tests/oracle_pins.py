@@ -489,3 +489,85 @@ def cumsum_pin_first_row_irrelevant(solve, cumsum):
 
 
 CUMSUM_PINS = [cumsum_pin_constant_closed_form, cumsum_pin_bruteforce, cumsum_pin_first_row_irrelevant]
+
+
+# --------------------------------------------------------------------------
+# Chunks of 128 tokens (the chunk size of the GDR case page's tiling).  These
+# pins take solve (with a chunk_size keyword) and hold the 128-token result to
+# the 64-token one, which the pins above fix.
+# --------------------------------------------------------------------------
+def _A_block(k, g, beta, rows, cols):
+    """beta_i (k_i . k_j) exp(clamp(g_i - g_j)) for token rows x token cols
+    (one batch row, one head)."""
+    G = np.clip(g[rows][:, None] - g[cols][None, :], -50.0, 50.0)
+    return beta[rows][:, None] * (k[rows] @ k[cols].T) * np.exp(G)
+
+
+def chunk128_pin_block_inverse(solve):
+    """Split a 128-token chunk into halves: the diagonal blocks of its inverse
+    are the 64-token results of each half, the upper block is zero, and the
+    lower block is -X22 A21 X11 (the inverse of a block lower-triangular
+    matrix).  Covers a full chunk and a partial one (T = 2*128 + 100)."""
+    rng = np.random.default_rng(60)
+    B, T, H, K = 1, 356, 2, 16
+    k = _unit_keys(rng, B, T, H, K)
+    beta = rng.uniform(0.1, 0.9, (B, T, H))
+    g = np.empty((B, T, H))
+    for t0 in range(0, T, 128):
+        g[:, t0:t0 + 128] = np.cumsum(-rng.uniform(0.0, 0.1, g[:, t0:t0 + 128].shape), axis=1)
+    X = solve(k, g, beta, None, chunk_size=128)
+    assert X.shape == (B, T, H, 128)
+    for t0 in range(0, T, 128):
+        L = min(128, T - t0)
+        L2 = L - 64
+        top = solve(k[:, t0:t0 + 64], g[:, t0:t0 + 64], beta[:, t0:t0 + 64], None)
+        bot = solve(k[:, t0 + 64:t0 + L], g[:, t0 + 64:t0 + L], beta[:, t0 + 64:t0 + L], None)
+        for h in range(H):
+            X11 = top[0, :, h, :64]
+            X22 = bot[0, :, h, :L2]
+            A21 = _A_block(k[0, :, h], g[0, :, h], beta[0, :, h],
+                           np.arange(t0 + 64, t0 + L), np.arange(t0, t0 + 64))
+            X21 = -X22 @ A21 @ X11
+            got = X[0, t0:t0 + L, h]
+            tol = 1e-12 * max(1.0, np.max(np.abs(X21)))
+            assert np.max(np.abs(got[:64, :64] - X11)) <= tol
+            assert np.all(got[:64, 64:] == 0.0)
+            assert np.max(np.abs(got[64:, 64:L] - X22)) <= tol
+            assert np.max(np.abs(got[64:, :64] - X21)) <= tol
+            assert np.all(got[:, L:] == 0.0)
+
+
+def chunk128_pin_library_inverse(solve):
+    """No gate, no beta: each 128-token chunk is numpy.linalg.inv(I + strict
+    lower part of K K^T)."""
+    rng = np.random.default_rng(61)
+    B, T, H, K = 2, 200, 1, 32
+    k = _unit_keys(rng, B, T, H, K)
+    X = solve(k, None, None, None, chunk_size=128)
+    for b in range(B):
+        for t0 in range(0, T, 128):
+            L = min(128, T - t0)
+            kk = k[b, t0:t0 + L, 0]
+            ref = np.linalg.inv(np.eye(L) + np.tril(kk @ kk.T, -1))
+            assert np.max(np.abs(X[b, t0:t0 + L, 0, :L] - ref)) <= 1e-11 * max(1.0, np.max(np.abs(ref)))
+
+
+def chunk128_pin_varlen_is_concat(solve):
+    """Packed sequences at chunk 128 equal one call per sequence; chunks
+    restart at every sequence start."""
+    rng = np.random.default_rng(62)
+    lens = [130, 1, 0, 128, 257, 64]
+    T, H, K = sum(lens), 2, 16
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    k = _unit_keys(rng, 1, T, H, K)
+    beta = rng.uniform(0.1, 0.9, (1, T, H))
+    g = -np.cumsum(rng.uniform(0.0, 0.05, (1, T, H)), axis=1)
+    out = solve(k, g, beta, cu, chunk_size=128)
+    for s in range(len(lens)):
+        a, b = cu[s], cu[s + 1]
+        if b > a:
+            ref = solve(k[:, a:b], g[:, a:b], beta[:, a:b], None, chunk_size=128)
+            assert np.array_equal(out[:, a:b], ref), s
+
+
+CHUNK128_PINS = [chunk128_pin_block_inverse, chunk128_pin_library_inverse, chunk128_pin_varlen_is_concat]

@@ -56,6 +56,9 @@ MUTANTS = [
      " ? g_out[(ch.b[c] * T + ch.t0[c] - 1) * H + h] : 0.0;\n"
      "            for (int64_t i = 0; i < ch.len[c]"),
     ("cumsum_head_zero", "                run += a[idx];", "                run += a[idx - h];"),
+    # chunks of 128: the chunk length capped at 64 whatever chunk_size says
+    ("chunk_len_capped_at_64", "out->len[n] = (eos - t0 < chunk_size) ? (eos - t0) : chunk_size;",
+     "out->len[n] = (eos - t0 < chunk_size) ? (eos - t0) : (chunk_size > 64 ? 64 : chunk_size);"),
 ]
 
 
@@ -167,6 +170,8 @@ def test_unmutated_copy_passes(tmpdir):
         pin(solve, *_split(lib))
     for pin in oracle_pins.CUMSUM_PINS:
         pin(solve, _cumsum(lib))
+    for pin in oracle_pins.CHUNK128_PINS:
+        pin(solve)
 
 
 @pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
@@ -192,6 +197,11 @@ def test_mutant_is_caught(tmpdir, name, old, new):
     for pin in oracle_pins.CUMSUM_PINS:
         try:
             pin(solve, cumsum)
+        except (AssertionError, ValueError, IndexError, FloatingPointError):
+            caught.append(pin.__name__)
+    for pin in oracle_pins.CHUNK128_PINS:
+        try:
+            pin(solve)
         except (AssertionError, ValueError, IndexError, FloatingPointError):
             caught.append(pin.__name__)
     assert caught, f"mutant {name} passed every pin"

@@ -22,6 +22,11 @@ def test_split_pin(pin):
         lambda A, cu=None: oracle.solve_tril_ref(A, cu))
 
 
+@pytest.mark.parametrize("pin", oracle_pins.CHUNK128_PINS, ids=lambda f: f.__name__)
+def test_chunk128_pin(pin):
+    pin(_solve)
+
+
 @pytest.mark.parametrize("pin", oracle_pins.CUMSUM_PINS, ids=lambda f: f.__name__)
 def test_cumsum_pin(pin):
     pin(_solve, lambda a, cu=None, chunk=64: oracle.chunk_cumsum_ref(a, cu, chunk))
