@@ -42,9 +42,14 @@ KERNEL_SRC = os.path.join(ROOT, "chunked_gated_delta_token_amd", "csrc", "kkt_so
 # the kernel each op launches (chain: both of the unfused steps)
 KERNELS = {"fused": "kkt_solve_kernel", "scaled_dot": "kkt_scaled_dot_kernel",
            "solve_tril": "kkt_solve_tril_kernel", "chain": "kkt_scaled_dot_kernel+kkt_solve_tril_kernel",
-           "gate_cumsum": "kkt_solve_gate_cumsum_kernel"}
+           "gate_cumsum": "kkt_solve_gate_cumsum_kernel", "fused128": "kkt_solve128_kernel"}
+# names of the profile files (fused128: kkt_solve with 128-token chunks)
 ENTRY = {"fused": "kkt_solve", "scaled_dot": "kkt_scaled_dot", "solve_tril": "kkt_solve_tril",
-         "gate_cumsum": "kkt_solve_gate_cumsum"}
+         "gate_cumsum": "kkt_solve_gate_cumsum", "fused128": "kkt_solve128"}
+
+
+def op_key(op: str, chunk: int) -> str:
+    return "fused128" if (op == "fused" and chunk == 128) else op
 
 
 def traffic_file(op: str, workload: str) -> str:
@@ -66,16 +71,17 @@ def chunk_lengths(w, cu_seqlens):
     return out
 
 
-def algorithmic_bytes(w, n_tokens: int, op: str = "fused", cu_seqlens=None) -> int:
+def algorithmic_bytes(w, n_tokens: int, op: str = "fused", cu_seqlens=None, chunk: int = 64) -> int:
     """Minimum bytes one step must move.  fused and chain: k once, g and beta
     once (when given), the output once (the chain's A round trip is its own
-    overhead, not the step's work).  gate_cumsum: as fused, plus the summed
+    overhead, not the step's work); with 128-token chunks the output rows are
+    128 wide.  gate_cumsum: as fused, plus the summed
     gate written back.  scaled_dot: k, g, beta, and A in fp32.
     solve_tril: the strictly lower entries of A (L (L-1) / 2 fp32 values per
     chunk and head) and the output.  (cu_seqlens, a few bytes, is ignored.)"""
     H, K = w.H, w.K
     k_gb = H * K * ESIZE[w.in_dtype] + H * 4 * (int(w.gate) + int(w.beta))
-    out = H * 64 * ESIZE[w.out_dtype]
+    out = H * chunk * ESIZE[w.out_dtype]
     if op in ("fused", "chain"):
         return (k_gb + out) * n_tokens
     if op == "gate_cumsum":
@@ -174,7 +180,7 @@ def _counter_values(directory: str, counter: str, kernel_substr: str):
     return vals
 
 
-def summarize_traffic(dirs, copy_bytes: int, op: str, workload: str):
+def summarize_traffic(dirs, copy_bytes: int, op: str, workload: str, chunk: int = 64):
     """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the op's kernel, each
     scaled by the bytes-per-KiB ratio the same counter shows for a plain copy."""
     import statistics
@@ -182,7 +188,8 @@ def summarize_traffic(dirs, copy_bytes: int, op: str, workload: str):
         raise SystemExit("--copy-bytes is required")
     if op == "chain":
         raise SystemExit("traffic is summarized per kernel: use --op fused, gate_cumsum, scaled_dot or solve_tril")
-    kname = KERNELS[op]
+    key = op_key(op, chunk)
+    kname = KERNELS[key]
     op_fetch = statistics.median(_counter_values(dirs[0], "FETCH_SIZE", kname))
     op_write = statistics.median(_counter_values(dirs[1], "WRITE_SIZE", kname))
     cp_fetch = statistics.median(_counter_values(dirs[2], "FETCH_SIZE", "copy"))
@@ -190,7 +197,7 @@ def summarize_traffic(dirs, copy_bytes: int, op: str, workload: str):
     f_scale = copy_bytes / cp_fetch
     w_scale = copy_bytes / cp_write
     fetch_b, write_b = op_fetch * f_scale, op_write * w_scale
-    sel = f"--op {op} --workload {workload}"
+    sel = f"--op {op} --workload {workload}" + (f" --chunk {chunk}" if chunk != 64 else "")
     lines = [
         f"# HBM traffic of {kname}, workload {workload}",
         "# commands (from /tmp, repository at $R; each --pmc pass alone, the last command wrote this file):",
@@ -211,14 +218,15 @@ def summarize_traffic(dirs, copy_bytes: int, op: str, workload: str):
         f"write_bytes_per_launch: {write_b:.0f}",
         f"hbm_bytes_per_launch: {fetch_b + write_b:.0f}",
     ]
-    path = traffic_file(op, workload)
+    path = traffic_file(key, workload)
     os.makedirs(os.path.dirname(path), exist_ok=True)
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
 
-def summarize_trace(directory: str, op: str, workload: str, run_log: str = None, plain_log: str = None):
+def summarize_trace(directory: str, op: str, workload: str, run_log: str = None, plain_log: str = None,
+                    chunk: int = 64):
     """Write profiles/<entry>_<workload>.kernel_trace.txt from a rocprofv3
     --kernel-trace --stats CSV directory: the op kernel's duration statistics
     and launch resources, next to bench.py's own event time of the profiled
@@ -228,7 +236,8 @@ def summarize_trace(directory: str, op: str, workload: str, run_log: str = None,
     from chunked_gated_delta_token_amd import workloads as W
     if op == "chain":
         raise SystemExit("kernel traces are summarized per kernel: use --op fused, gate_cumsum, scaled_dot or solve_tril")
-    kname = KERNELS[op]
+    key = op_key(op, chunk)
+    kname = KERNELS[key]
     stats = [r for path in glob.glob(os.path.join(directory, "**", "*kernel_stats.csv"), recursive=True)
              for r in csv.DictReader(open(path, newline="")) if f"::{kname}<" in r["Name"]]
     if len(stats) != 1:
@@ -243,7 +252,7 @@ def summarize_trace(directory: str, op: str, workload: str, run_log: str = None,
     durations = [d for _, d in sorted(durations)]
     w = W.WORKLOADS[workload]
     cu = W.generate(workload).cu_seqlens if w.n_seqs else None
-    nbytes = algorithmic_bytes(w, w.B * w.T, op, cu)
+    nbytes = algorithmic_bytes(w, w.B * w.T, op, cu, chunk)
     avg = float(st["AverageNs"])
 
     def event_us(log):
@@ -256,7 +265,7 @@ def summarize_trace(directory: str, op: str, workload: str, run_log: str = None,
         return None
 
     ev_prof, ev_plain = event_us(run_log), event_us(plain_log)
-    sel = f"--op {op} --workload {workload}"
+    sel = f"--op {op} --workload {workload}" + (f" --chunk {chunk}" if chunk != 64 else "")
     lines = [
         f"# rocprofv3 kernel trace: {kname}, workload {workload} ({w.B},{w.T},{w.H},{w.K}) "
         f"{w.in_dtype} -> {w.out_dtype}; {nbytes} algorithmic bytes per launch",
@@ -293,7 +302,7 @@ def summarize_trace(directory: str, op: str, workload: str, run_log: str = None,
         if len(durations) >= 200:
             lines.append(f"timed_replay_average_vs_unprofiled_event: "
                          f"{statistics.mean(durations[-200:]) / 1e3 / ev_plain - 1.0:+.3%}")
-    path = os.path.join(ROOT, "profiles", f"{ENTRY[op]}_{workload}.kernel_trace.txt")
+    path = os.path.join(ROOT, "profiles", f"{ENTRY[key]}_{workload}.kernel_trace.txt")
     os.makedirs(os.path.dirname(path), exist_ok=True)
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
@@ -308,6 +317,8 @@ def main():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--op", choices=["fused", "gate_cumsum", "scaled_dot", "solve_tril", "chain"], default="fused",
                     help="what one step runs (default: the fused op)")
+    ap.add_argument("--chunk", type=int, choices=[64, 128], default=64,
+                    help="chunk size of the fused op (128: the 128-token variant)")
     ap.add_argument("--timing", choices=["graph", "eager"], default="graph")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -327,12 +338,13 @@ def main():
     if args.summarize_trace:
         from chunked_gated_delta_token_amd import workloads as W
         summarize_trace(args.summarize_trace, args.op, args.workload or W.BENCH_WORKLOAD, args.run_log,
-                        args.plain_log)
+                        args.plain_log, args.chunk)
         return
 
     if args.summarize_traffic:
         from chunked_gated_delta_token_amd import workloads as W
-        summarize_traffic(args.summarize_traffic, args.copy_bytes, args.op, args.workload or W.BENCH_WORKLOAD)
+        summarize_traffic(args.summarize_traffic, args.copy_bytes, args.op, args.workload or W.BENCH_WORKLOAD,
+                          args.chunk)
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -372,7 +384,10 @@ def main():
         if inp.g_raw is None:
             raise SystemExit(f"--op gate_cumsum needs a workload with a gate ({name} has none)")
         g0 = torch.from_numpy(inp.g_raw).to(dev)  # per-token log-decays, summed by the kernel
-    nbytes = algorithmic_bytes(w, n_tokens, op, inp.cu_seqlens)
+    chunk = args.chunk
+    if chunk != 64 and op != "fused":
+        raise SystemExit("--chunk 128 applies to the fused op only")
+    nbytes = algorithmic_bytes(w, n_tokens, op, inp.cu_seqlens, chunk)
     num_seqs = 0 if inp.cu_seqlens is None else len(inp.cu_seqlens) - 1
     stream = torch.cuda.Stream(dev)
     shape = (w.B, w.T, w.H, 64)
@@ -401,7 +416,7 @@ def main():
         if op == "solve_tril":
             s_["A"] = A0.clone()
         if op != "scaled_dot":
-            s_["out"] = torch.empty(shape, dtype=tdt[w.out_dtype], device=dev)
+            s_["out"] = torch.empty(shape[:3] + (chunk,), dtype=tdt[w.out_dtype], device=dev)
         if op == "gate_cumsum":
             s_["g_out"] = torch.empty(shape[:3], dtype=torch.float32, device=dev)
         sets.append(s_)
@@ -419,7 +434,8 @@ def main():
         kargs = (ptr(s_.get("k")), ptr(s_.get("g")), ptr(s_.get("b")), ptr(s_["cu"]), num_seqs, w.B, w.T, w.H, w.K, 64,
                  kdt[w.in_dtype])
         if op == "fused":
-            return [(lib.kkt_solve, kargs + (kdt[w.out_dtype], ptr(s_["out"]), sp))]
+            kargs_c = kargs[:9] + (chunk,) + kargs[10:]
+            return [(lib.kkt_solve, kargs_c + (kdt[w.out_dtype], ptr(s_["out"]), sp))]
         if op == "gate_cumsum":
             return [(lib.kkt_solve_gate_cumsum, kargs + (kdt[w.out_dtype], ptr(s_["out"]), ptr(s_["g_out"]), sp))]
         tril = (lib.kkt_solve_tril, (ptr(s_["A"]), ptr(s_["cu"]), num_seqs, w.B, w.T, w.H, 64, kdt[w.out_dtype],
@@ -491,16 +507,18 @@ def main():
 
     achieved = nbytes / (ev_ms * 1e-3) / 1e9
     digest = source_digest()
-    traffic = None if op == "chain" else read_traffic(digest, traffic_file(op, name))
-    n_tiles = w.H * (sum(-(-(int(inp.cu_seqlens[s + 1]) - int(inp.cu_seqlens[s])) // 64)
-                         for s in range(num_seqs)) if num_seqs else w.B * (-(-w.T // 64)))
+    key = op_key(op, chunk)
+    traffic = None if op == "chain" else read_traffic(digest, traffic_file(key, name))
+    n_tiles = w.H * (sum(-(-(int(inp.cu_seqlens[s + 1]) - int(inp.cu_seqlens[s])) // chunk)
+                         for s in range(num_seqs)) if num_seqs else w.B * (-(-w.T // chunk)))
     value = nbytes / (ms_per_step * 1e-3) / 1e9
-    metric = METRIC if op == "fused" else {
+    metric = METRIC if (op == "fused" and chunk == 64) else {
+        "fused": "fused KKT+solve with 128-token chunks ms/iter & achieved HBM GB/s, 1 GPU",
         "gate_cumsum": "fused KKT+solve with the chunk-local gate sum in the kernel ms/iter & achieved HBM GB/s, 1 GPU",
         "scaled_dot": "KKT A alone (first step of the unfused chain) ms/iter & achieved HBM GB/s, 1 GPU",
         "solve_tril": "solve of a given A (second step of the unfused chain) ms/iter & achieved HBM GB/s, 1 GPU",
         "chain": "unfused two-step chain (A through HBM) ms/iter & GB/s of the fused op's bytes, 1 GPU"}[op]
-    pages_ms = {"fused": PAGES_FUSED_MS, "chain": PAGES_TWO_OP_MS}.get(op)
+    pages_ms = {"fused": PAGES_FUSED_MS, "chain": PAGES_TWO_OP_MS}.get(op) if chunk == 64 else None
     line = {
         "metric": metric,
         "value": round(value, 2),
@@ -514,12 +532,12 @@ def main():
         "vs_baseline": round(pages_ms / ms_per_step, 3) if (pages_ms and name == W.BENCH_WORKLOAD) else None,
         "dtype": w.in_dtype,
         "data": "synthetic",
-        "config": {"workload": name, "op": op, "B": w.B, "T": w.T, "H": w.H, "K": w.K, "in_dtype": w.in_dtype,
+        "config": {"workload": name, "op": op, "chunk": chunk, "B": w.B, "T": w.T, "H": w.H, "K": w.K, "in_dtype": w.in_dtype,
                    "out_dtype": w.out_dtype, "gate": w.gate, "beta": w.beta, "tiles": n_tiles,
                    "algorithmic_bytes": nbytes, "buffer_sets": R, "timing": args.timing,
                    "chunks_per_s": round(n_tiles / (ms_per_step * 1e-3), 1)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": KERNELS[op],
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": KERNELS[key],
                      "event_ms_per_step": round(ev_ms, 6), "launches_per_step": len(calls[0]),
                      "kernel_source_sha256_16": digest},
     }

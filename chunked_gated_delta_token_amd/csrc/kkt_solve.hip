@@ -54,7 +54,7 @@
 
 #include "kkt_solve.h"
 
-#define KKT_VERSION_NUMBER 400  // 0.4.0
+#define KKT_VERSION_NUMBER 500  // 0.5.0
 
 namespace {
 
@@ -210,9 +210,11 @@ struct Tile {
     int len;       // valid rows L in [1, 64]; 0: no tile
 };
 
-// Packed sequences: the chunk with global index c (chunks numbered sequence
-// by sequence) is found with a wave-wide inclusive scan of per-sequence chunk
-// counts, 64 sequences per pass.  Offsets are clamped into [0, T].
+// Packed sequences: the chunk with global index c (chunks of CH tokens,
+// numbered sequence by sequence) is found with a wave-wide inclusive scan of
+// per-sequence chunk counts, 64 sequences per pass.  Offsets are clamped into
+// [0, T].
+template <int CH>
 __device__ Tile varlen_tile(const int32_t* __restrict__ cu, int32_t num_seqs, int64_t T, int32_t c, int lane)
 {
     Tile t{0, 0};
@@ -225,7 +227,7 @@ __device__ Tile varlen_tile(const int32_t* __restrict__ cu, int32_t num_seqs, in
             bos = a < 0 ? 0 : (a > T ? T : a);
             eos = e < bos ? bos : (e > T ? T : e);
         }
-        const int32_t n = (int32_t)((eos - bos + kChunk - 1) / kChunk);
+        const int32_t n = (int32_t)((eos - bos + CH - 1) / CH);
         int32_t incl = n;
 #pragma unroll
         for (int d = 1; d < kWave; d <<= 1) {
@@ -239,10 +241,10 @@ __device__ Tile varlen_tile(const int32_t* __restrict__ cu, int32_t num_seqs, in
             const int32_t sel_excl = __shfl(incl - n, src, kWave);
             const int64_t sel_bos = __shfl(bos, src, kWave);
             const int64_t sel_eos = __shfl(eos, src, kWave);
-            const int64_t t0 = sel_bos + (int64_t)(c - before - sel_excl) * kChunk;
+            const int64_t t0 = sel_bos + (int64_t)(c - before - sel_excl) * CH;
             const int64_t rem = sel_eos - t0;
             t.row0 = t0;
-            t.len = (int)(rem < kChunk ? rem : kChunk);
+            t.len = (int)(rem < CH ? rem : CH);
             return t;
         }
         before += __shfl(incl, kWave - 1, kWave);
@@ -250,29 +252,11 @@ __device__ Tile varlen_tile(const int32_t* __restrict__ cu, int32_t num_seqs, in
     return t;
 }
 
-// ---------------------------------------------------------------- the kernel
-// GATE_SUM: g holds per-token log-decays that the tile sums itself (a
-// separate instantiation, so the plain fused kernel carries none of it).
-template <Mode MODE, Elt IN, Elt OUT, int K, bool GATE_SUM = false>
-__device__ __forceinline__ void run_tile(const KernelArgs& args, WaveLds* lds_all)
+// Workgroup order (see XcdOrder); both remaps are permutations of
+// [0, n_groups).  Computed without branches from kernel arguments only, so the
+// argument loads are issued together.
+__device__ __forceinline__ uint32_t workgroup_order(const KernelArgs& args)
 {
-    constexpr int kInBytes = EltInfo<IN>::bytes;
-    constexpr int kOutBytes = EltInfo<OUT>::bytes;
-    constexpr int kElemsPer16B = 16 / kInBytes;            // 8 (16-bit) or 4 (fp32)
-    constexpr int kSteps = K / (4 * kElemsPer16B);          // 16-byte fragments per row per lane
-    static_assert(K % (4 * kElemsPer16B) == 0, "K must fill whole fragments");
-
-    const int lane = threadIdx.x % kWave;
-    // wave-uniform values are pinned to scalar registers so that the buffer
-    // resources built from them are scalar too
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int q = lane / 16;   // lane group (k-slot group of an MFMA operand)
-    const int m = lane % 16;   // row inside a 16-row block (A operand) / column (D layout)
-    WaveLds& lds = lds_all[wave];
-
-    // Workgroup order (see XcdOrder); both remaps are permutations of
-    // [0, n_groups).  Computed without branches from kernel arguments only, so
-    // the argument loads are issued together.
     // (the empty statement makes the tensor pointers live here, so that their
     // loads are issued with the ones the order needs, in one round trip)
     asm volatile("" ::"s"(args.k), "s"(args.out), "s"(args.g), "s"(args.beta));
@@ -285,35 +269,80 @@ __device__ __forceinline__ void run_tile(const KernelArgs& args, WaveLds* lds_al
     const int lg = args.log2_group_run;
     const uint32_t g_runs = (hw < args.remap_groups)
         ? ((((slot >> lg) << 3) + xcd) << lg) | (slot & ((1u << lg) - 1u)) : hw;
-    const uint32_t group = (args.xcd_order == kContiguous) ? g_contiguous
-                         : (args.xcd_order == kChunkRoundRobin) ? g_runs : hw;
-    const uint32_t tile_id = group * kWavesPerGroup + wave;
-    if (tile_id >= (uint32_t)args.n_tiles) return;  // wave-uniform
+    return (args.xcd_order == kContiguous) ? g_contiguous
+         : (args.xcd_order == kChunkRoundRobin) ? g_runs : hw;
+}
 
-    // ---- a1: tile map
-    const int H = args.H;
-    const int h = (int)(tile_id % (uint32_t)H);
-    const uint32_t chunk = tile_id / (uint32_t)H;
+// Chunk c of CH tokens of one head -> (first row, valid rows); the result is
+// wave-uniform and lives in scalar registers.
+template <int CH>
+__device__ __forceinline__ Tile chunk_tile(const KernelArgs& args, uint32_t chunk, int lane)
+{
     Tile tile;
     if (args.cu_seqlens == nullptr) {
         const uint32_t b = chunk / (uint32_t)args.chunks_per_row;
         const uint32_t c = chunk % (uint32_t)args.chunks_per_row;
-        const int64_t t0 = (int64_t)c * kChunk;
+        const int64_t t0 = (int64_t)c * CH;
         tile.row0 = (int64_t)b * args.T + t0;
-        tile.len = (int)((args.T - t0) < kChunk ? (args.T - t0) : kChunk);
+        tile.len = (int)((args.T - t0) < CH ? (args.T - t0) : CH);
     } else {
-        tile = varlen_tile(args.cu_seqlens, args.num_seqs, args.T, (int32_t)chunk, lane);
+        tile = varlen_tile<CH>(args.cu_seqlens, args.num_seqs, args.T, (int32_t)chunk, lane);
     }
-    const int L = __builtin_amdgcn_readfirstlane(tile.len);
-    if (L <= 0) return;  // wave-uniform
-    const int64_t row0 = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(tile.row0 >> 32)) << 32) |
-                                   (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)tile.row0));
+    tile.len = __builtin_amdgcn_readfirstlane(tile.len);
+    tile.row0 = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(tile.row0 >> 32)) << 32) |
+                          (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)tile.row0));
+    return tile;
+}
 
-    // Buffer resources spanning exactly rows 0 .. L-1 of this tile.
-    const int64_t tok = row0 * H + h;  // flat (token, head) index of row 0
+// LDS of one 128-token tile (one workgroup): the four waves' own areas, then
+// what the halves of the chunk exchange.
+struct Chunk128Lds {
+    WaveLds wave[kWavesPerGroup];
+    float x22t[10][16][kBlockLd];          // X22 blocks, transposed: x22t[b][col][row]
+    struct Cross {
+        f32x4 x11[10][kWave];              // X11 blocks, result-layout register images
+        f32x4 a21[16][kWave];              // A21 blocks (left-operand layout), then P blocks (result layout)
+    };
+    union {
+        Cross cross;
+        float x21[kChunk][kStageLd];       // X21 rows staged for the store
+    };
+};
+
+// Index of lower block (i, j), j <= i, of a 4x4 block-triangular matrix.
+__host__ __device__ constexpr int tri(int i, int j) { return i * (i + 1) / 2 + j; }
+
+// ---------------------------------------------------------------- the kernel
+// Steps a2-a8 for 64 rows of one chunk of CH tokens, on one wave.  CH = 64:
+// the whole chunk (half = 0).  CH = 128: rows 64*half .. 64*half+63, the
+// half's own diagonal 64x64 block of the inverse; its columns go to
+// 64*half .. 64*half+63 of the 128-wide output rows (half 0 also writes the
+// zeros of columns 64..127), and the block is left in ex for the rest of the
+// workgroup.  tok: flat (token, head) index of the chunk's first row; L: valid
+// rows of the chunk.
+// GATE_SUM: g holds per-token log-decays that the tile sums itself (a
+// separate instantiation, so the plain fused kernel carries none of it).
+template <Mode MODE, Elt IN, Elt OUT, int K, bool GATE_SUM, int CH>
+__device__ __forceinline__ void chunk_rows(const KernelArgs& args, WaveLds& lds, int lane, int64_t tok, int L,
+                                           int half, Chunk128Lds* ex)
+{
+    constexpr int kInBytes = EltInfo<IN>::bytes;
+    constexpr int kOutBytes = EltInfo<OUT>::bytes;
+    constexpr int kElemsPer16B = 16 / kInBytes;            // 8 (16-bit) or 4 (fp32)
+    constexpr int kSteps = K / (4 * kElemsPer16B);          // 16-byte fragments per row per lane
+    static_assert(K % (4 * kElemsPer16B) == 0, "K must fill whole fragments");
+    static_assert(CH == 64 || (CH == 128 && MODE == Mode::Fused && !GATE_SUM), "128-token chunks: fused op only");
+    const int q = lane / 16;   // lane group (k-slot group of an MFMA operand)
+    const int m = lane % 16;   // row inside a 16-row block (A operand) / column (D layout)
+    const int H = args.H;
+    // first row and first output column of this wave's 64 rows
+    const uint32_t row_base = (CH == 128) ? 64u * (uint32_t)half : 0u;
+    const uint32_t col_base = row_base;
+
+    // Buffer resources spanning exactly rows 0 .. L-1 of the chunk.
     const __amdgpu_buffer_rsrc_t o_rsrc = make_rsrc(
-        static_cast<char*>(args.out) + tok * (int64_t)(kChunk * kOutBytes),
-        (uint32_t)(L - 1) * args.o_row_bytes + kChunk * kOutBytes);
+        static_cast<char*>(args.out) + tok * (int64_t)(CH * kOutBytes),
+        (uint32_t)(L - 1) * args.o_row_bytes + CH * kOutBytes);
 
     // The 10 lower 16x16 blocks of A, result layout: A[i][j] lane (q, n)
     // holds A_ij[4q .. 4q+3][n] (rows 16i + 4q + r, column 16j + n).  The
@@ -322,8 +351,8 @@ __device__ __forceinline__ void run_tile(const KernelArgs& args, WaveLds* lds_al
     if constexpr (MODE == Mode::SolveTril) {
         // ---- A from memory (fp32 rows of 64; the kernel argument k carries A)
         const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(
-            static_cast<const char*>(args.k) + tok * (int64_t)(kChunk * 4),
-            (uint32_t)(L - 1) * args.k_row_bytes + kChunk * 4);
+            static_cast<const char*>(args.k) + tok * (int64_t)(CH * 4),
+            (uint32_t)(L - 1) * args.k_row_bytes + CH * 4);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -344,10 +373,10 @@ __device__ __forceinline__ void run_tile(const KernelArgs& args, WaveLds* lds_al
         // before the K tile: loads complete in order, so waiting for these two
         // does not wait for the whole tile.
         const bool has_g = args.g != nullptr;
-        const bool valid = lane < L;
+        const bool valid = lane < L - (int)row_base;
         float gv = 0.0f, bv = 1.0f;
         {
-            const uint32_t voff = (uint32_t)lane * (uint32_t)H * 4u;
+            const uint32_t voff = (row_base + (uint32_t)lane) * (uint32_t)H * 4u;
             const uint32_t span = (uint32_t)(L - 1) * (uint32_t)H * 4u + 4u;
             // the loads return raw 32-bit words: reinterpret, do not convert
             if (has_g) {
@@ -367,7 +396,7 @@ __device__ __forceinline__ void run_tile(const KernelArgs& args, WaveLds* lds_al
         u32x4 frag[4][kSteps];
 #pragma unroll
         for (int bi = 0; bi < 4; ++bi) {
-            const uint32_t voff = (uint32_t)(16 * bi + m) * args.k_row_bytes + q * 16;
+            const uint32_t voff = (row_base + (uint32_t)(16 * bi + m)) * args.k_row_bytes + q * 16;
 #pragma unroll
             for (int s = 0; s < kSteps; ++s) {
                 frag[bi][s] = __builtin_amdgcn_raw_buffer_load_b128(k_rsrc, voff + s * 64, 0, 0);
@@ -488,8 +517,11 @@ __device__ __forceinline__ void run_tile(const KernelArgs& args, WaveLds* lds_al
             for (int it = 0; it < 4; ++it) {
                 const int rr = 4 * it + rsub;
                 const f32x4 v = *reinterpret_cast<const f32x4*>(&lds.stage[rr][c4]);
-                const uint32_t voff = (uint32_t)(16 * i + rr) * args.o_row_bytes + c4 * 4;
+                const uint32_t voff = (row_base + (uint32_t)(16 * i + rr)) * args.o_row_bytes + (col_base + c4) * 4;
                 __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), o_rsrc, voff, 0, kNonTemporal);
+                if (CH == 128 && half == 0) {  // columns 64..127 of the first half's rows
+                    __builtin_amdgcn_raw_buffer_store_b128(u32x4{0u, 0u, 0u, 0u}, o_rsrc, voff + 64 * 4, 0, kNonTemporal);
+                }
             }
         } else {
             // 8 lanes per 128-byte row, 8 rows per pass
@@ -504,8 +536,11 @@ __device__ __forceinline__ void run_tile(const KernelArgs& args, WaveLds* lds_al
                 p[1] = pack2<OUT>(v0[2], v0[3]);
                 p[2] = pack2<OUT>(v1[0], v1[1]);
                 p[3] = pack2<OUT>(v1[2], v1[3]);
-                const uint32_t voff = (uint32_t)(16 * i + rr) * args.o_row_bytes + c8 * 2;
+                const uint32_t voff = (row_base + (uint32_t)(16 * i + rr)) * args.o_row_bytes + (col_base + c8) * 2;
                 __builtin_amdgcn_raw_buffer_store_b128(p, o_rsrc, voff, 0, kNonTemporal);
+                if (CH == 128 && half == 0) {
+                    __builtin_amdgcn_raw_buffer_store_b128(u32x4{0u, 0u, 0u, 0u}, o_rsrc, voff + 64 * 2, 0, kNonTemporal);
+                }
             }
         }
     };
@@ -614,6 +649,142 @@ __device__ __forceinline__ void run_tile(const KernelArgs& args, WaveLds* lds_al
 
     const f32x4 x30 = zero4 - mm16(wt32, x20, p30);
     store_block_row(3, x30, x31, x32, xd[3]);
+
+    if constexpr (CH == 128) {
+        // hand the block to the workgroup: X11 as result-layout register
+        // images, X22 transposed (its rows are read as left operands)
+        const f32x4 blocks[10] = {xd[0], x10, xd[1], x20, x21, xd[2], x30, x31, x32, xd[3]};
+        if (half == 0) {
+#pragma unroll
+            for (int b = 0; b < 10; ++b) ex->cross.x11[b][lane] = blocks[b];
+        } else {
+#pragma unroll
+            for (int b = 0; b < 10; ++b) *reinterpret_cast<f32x4*>(&ex->x22t[b][m][4 * q]) = blocks[b];
+        }
+    }
+}
+
+
+// One 64-token chunk per wave, four waves per workgroup.
+template <Mode MODE, Elt IN, Elt OUT, int K, bool GATE_SUM = false>
+__device__ __forceinline__ void run_tile(const KernelArgs& args, WaveLds* lds_all)
+{
+    const int lane = threadIdx.x % kWave;
+    // wave-uniform values are pinned to scalar registers so that the buffer
+    // resources built from them are scalar too
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const uint32_t tile_id = workgroup_order(args) * kWavesPerGroup + wave;
+    if (tile_id >= (uint32_t)args.n_tiles) return;  // wave-uniform
+
+    // ---- a1: tile map
+    const int H = args.H;
+    const int h = (int)(tile_id % (uint32_t)H);
+    const Tile tile = chunk_tile<kChunk>(args, tile_id / (uint32_t)H, lane);
+    if (tile.len <= 0) return;  // wave-uniform
+    chunk_rows<MODE, IN, OUT, K, GATE_SUM, kChunk>(args, lds_all[wave], lane, tile.row0 * H + h, tile.len, 0, nullptr);
+}
+
+// 128-token chunks: the 64x64 block A21 of A (rows 64..127, columns 0..63)
+// for two of its four 16-row block rows (w2 = 0: rows 64..95, 1: rows
+// 96..127), left in the workgroup's LDS as left-operand-layout images.
+// A21[i][j] = beta_i (k_i . k_j) exp(clamp(g_i - g_j)): every element takes
+// its own clamped exponential (rows and columns come from different halves).
+template <Elt IN, int K>
+__device__ __forceinline__ void cross_block_rows(const KernelArgs& args, Chunk128Lds& ex, WaveLds& lds, int lane,
+                                                 int64_t tok, int L, int w2)
+{
+    constexpr int kInBytes = EltInfo<IN>::bytes;
+    constexpr int kElemsPer16B = 16 / kInBytes;
+    constexpr int kSteps = K / (4 * kElemsPer16B);
+    constexpr int kPass = kSteps < 4 ? kSteps : 4;  // fragments per row and pass (register budget)
+    static_assert(kSteps % kPass == 0, "whole passes");
+    const int q = lane / 16;
+    const int m = lane % 16;
+    const int H = args.H;
+    const __amdgpu_buffer_rsrc_t k_rsrc = make_rsrc(
+        static_cast<const char*>(args.k) + tok * (int64_t)(K * kInBytes),
+        (uint32_t)(L - 1) * args.k_row_bytes + K * kInBytes);
+
+    // gate and beta: lane holds the column gate of first-half row `lane` and
+    // the row gate and beta of second-half row 64 + lane (rows >= L read 0)
+    const bool has_g = args.g != nullptr;
+    float g_lo = 0.0f, g_hi = 0.0f, b_hi = 1.0f;
+    {
+        const uint32_t span = (uint32_t)(L - 1) * (uint32_t)H * 4u + 4u;
+        const uint32_t lo = (uint32_t)lane * (uint32_t)H * 4u, hi = (64u + (uint32_t)lane) * (uint32_t)H * 4u;
+        if (has_g) {
+            const __amdgpu_buffer_rsrc_t g_rsrc = make_rsrc(args.g + tok, span);
+            g_lo = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(g_rsrc, lo, 0, 0));
+            g_hi = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(g_rsrc, hi, 0, 0));
+        }
+        if (args.beta != nullptr) {
+            b_hi = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(args.beta + tok, span), hi, 0, 0));
+        }
+    }
+
+    // S21 blocks, transposed Gram: gram_step(first-half fragment, second-half
+    // fragment) gives K1_j K2_i^T in result layout, which is S21_ij in
+    // left-operand layout.  Keys stream in passes of kPass fragments.
+    f32x4 acc[2][4];
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi) {
+#pragma unroll
+        for (int bj = 0; bj < 4; ++bj) acc[bi][bj] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+#pragma unroll
+    for (int p0 = 0; p0 < kSteps; p0 += kPass) {
+        u32x4 fr[2][kPass], fc[4][kPass];
+#pragma unroll
+        for (int bi = 0; bi < 2; ++bi) {
+            const uint32_t voff = (uint32_t)(64 + 32 * w2 + 16 * bi + m) * args.k_row_bytes + q * 16;
+#pragma unroll
+            for (int s = 0; s < kPass; ++s) fr[bi][s] = __builtin_amdgcn_raw_buffer_load_b128(k_rsrc, voff + (p0 + s) * 64, 0, 0);
+        }
+#pragma unroll
+        for (int bj = 0; bj < 4; ++bj) {
+            const uint32_t voff = (uint32_t)(16 * bj + m) * args.k_row_bytes + q * 16;
+#pragma unroll
+            for (int s = 0; s < kPass; ++s) fc[bj][s] = __builtin_amdgcn_raw_buffer_load_b128(k_rsrc, voff + (p0 + s) * 64, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int bi = 0; bi < 2; ++bi) {
+#pragma unroll
+            for (int bj = 0; bj < 4; ++bj) {
+#pragma unroll
+                for (int s = 0; s < kPass; ++s) acc[bi][bj] = gram_step<IN>(fc[bj][s], fr[bi][s], acc[bi][bj]);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // epilogue: lane (q, m) of block (bi, bj) holds S21[m][4q + r], second-half
+    // row 32 w2 + 16 bi + m, first-half column 16 bj + 4q + r
+    lds.row_scale[lane] = b_hi;
+    lds.gate[lane] = g_hi;
+    lds.col_scale[lane] = g_lo;
+    wave_lds_sync();
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi) {
+        const int row = 32 * w2 + 16 * bi + m;
+        const float br = lds.row_scale[row];
+        const float gr = lds.gate[row];
+#pragma unroll
+        for (int bj = 0; bj < 4; ++bj) {
+            f32x4 a;
+            if (has_g) {
+                const f32x4 gc = *reinterpret_cast<const f32x4*>(&lds.col_scale[16 * bj + 4 * q]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float d = fminf(fmaxf(gr - gc[r], -kGateClamp), kGateClamp);
+                    a[r] = br * (acc[bi][bj][r] * __expf(d));
+                }
+            } else {
+                a = br * acc[bi][bj];
+            }
+            ex.cross.a21[4 * (2 * w2 + bi) + bj][lane] = a;
+        }
+    }
 }
 
 // One kernel per entry point, so that profiles name the operation.
@@ -648,6 +819,118 @@ void kkt_solve_tril_kernel(const KernelArgs args)
 {
     __shared__ WaveLds lds_all[kWavesPerGroup];
     run_tile<Mode::SolveTril, Elt::F32, OUT, 64>(args, lds_all);
+}
+
+// 128-token chunks (the GDR case page's chunk size), one workgroup per
+// (chunk, head).  With X11 = (I + A11)^{-1}, X22 = (I + A22)^{-1} for the two
+// 64-row halves, the inverse is [[X11, 0], [X21, X22]] with
+// X21 = -X22 (A21 X11):
+//   waves 0, 1: a2-a8 on their half (X11, X22 and their output columns);
+//   waves 2, 3: A21, two block rows each;
+//   then P = A21 X11 (wave i: block row i), X21 = -X22 P (wave j: block
+//   column j), X21 staged in LDS and stored as 256/128-byte row pieces.
+template <Elt IN, Elt OUT, int K>
+__global__ __launch_bounds__(kWave * kWavesPerGroup)
+void kkt_solve128_kernel(const KernelArgs args)
+{
+    constexpr int kOutBytes = EltInfo<OUT>::bytes;
+    __shared__ Chunk128Lds ex;
+    const int lane = threadIdx.x % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int q = lane / 16;
+    const int m = lane % 16;
+    const uint32_t tile_id = workgroup_order(args);
+    if (tile_id >= (uint32_t)args.n_tiles) return;  // workgroup-uniform
+    const int H = args.H;
+    const int h = (int)(tile_id % (uint32_t)H);
+    const Tile tile = chunk_tile<2 * kChunk>(args, tile_id / (uint32_t)H, lane);
+    if (tile.len <= 0) return;  // workgroup-uniform
+    const int L = tile.len;
+    const int64_t tok = tile.row0 * H + h;
+
+    if (wave < 2) {
+        chunk_rows<Mode::Fused, IN, OUT, K, false, 2 * kChunk>(args, ex.wave[wave], lane, tok, L, wave, &ex);
+    } else {
+        cross_block_rows<IN, K>(args, ex, ex.wave[wave], lane, tok, L, wave - 2);
+    }
+    __syncthreads();
+
+    const f32x4 zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
+    // P = A21 X11, block row i = wave: P_ij = sum_{k=j..3} A21_ik X11_kj
+    {
+        const int i = wave;
+        f32x4 a[4], p[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) a[k] = ex.cross.a21[4 * i + k][lane];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            p[j] = zero4;
+#pragma unroll
+            for (int k = j; k < 4; ++k) p[j] = mm16(a[k], ex.cross.x11[tri(k, j)][lane], p[j]);
+        }
+        wave_lds_sync();  // this wave's reads of its A21 row precede the overwrite
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ex.cross.a21[4 * i + j][lane] = p[j];
+    }
+    __syncthreads();
+
+    // X21 = -X22 P, block column j = wave: X21_ij = -sum_{k=0..i} X22_ik P_kj
+    f32x4 x21[4];
+    {
+        const int j = wave;
+        f32x4 pc[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) pc[k] = ex.cross.a21[4 * k + j][lane];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f32x4 sum = zero4;
+#pragma unroll
+            for (int k = 0; k <= i; ++k) {
+                f32x4 xa;  // X22_ik in left-operand layout: row m, columns 4q .. 4q+3
+#pragma unroll
+                for (int r = 0; r < 4; ++r) xa[r] = ex.x22t[tri(i, k)][4 * q + r][m];
+                sum = mm16(xa, pc[k], sum);
+            }
+            x21[i] = zero4 - sum;
+        }
+    }
+    __syncthreads();  // every read of the exchange area is done: X21 may overwrite it
+
+    // stage block column j = wave of X21 as rows, then store rows 64 + 16 wave ..
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ex.x21[16 * i + 4 * q + r][16 * wave + m] = x21[i][r];
+    }
+    __syncthreads();
+    const __amdgpu_buffer_rsrc_t o_rsrc = make_rsrc(
+        static_cast<char*>(args.out) + tok * (int64_t)(2 * kChunk * kOutBytes),
+        (uint32_t)(L - 1) * args.o_row_bytes + 2 * kChunk * kOutBytes);
+    if constexpr (OUT == Elt::F32) {
+        const int rsub = lane / 16, c4 = (lane % 16) * 4;
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            const int rr = 16 * wave + 4 * it + rsub;
+            const f32x4 v = *reinterpret_cast<const f32x4*>(&ex.x21[rr][c4]);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), o_rsrc,
+                                                   (uint32_t)(64 + rr) * args.o_row_bytes + c4 * 4, 0, kNonTemporal);
+        }
+    } else {
+        const int rsub = lane / 8, c8 = (lane % 8) * 8;
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+            const int rr = 16 * wave + 8 * it + rsub;
+            const f32x4 v0 = *reinterpret_cast<const f32x4*>(&ex.x21[rr][c8]);
+            const f32x4 v1 = *reinterpret_cast<const f32x4*>(&ex.x21[rr][c8 + 4]);
+            u32x4 p;
+            p[0] = pack2<OUT>(v0[0], v0[1]);
+            p[1] = pack2<OUT>(v0[2], v0[3]);
+            p[2] = pack2<OUT>(v1[0], v1[1]);
+            p[3] = pack2<OUT>(v1[2], v1[3]);
+            __builtin_amdgcn_raw_buffer_store_b128(p, o_rsrc, (uint32_t)(64 + rr) * args.o_row_bytes + c8 * 2, 0,
+                                                   kNonTemporal);
+        }
+    }
 }
 
 // ---------------------------------------------------------------- host side
@@ -698,8 +981,7 @@ kkt_status_t validate_cu_seqlens(const int32_t* cu, int64_t num_seqs, int64_t T,
 
 hipError_t launch(void (*kernel)(KernelArgs), const KernelArgs& a, hipStream_t stream)
 {
-    const int64_t groups = ((int64_t)a.n_tiles + kWavesPerGroup - 1) / kWavesPerGroup;
-    hipLaunchKernelGGL(kernel, dim3((unsigned)groups), dim3(kWave * kWavesPerGroup), 0, stream, a);
+    hipLaunchKernelGGL(kernel, dim3(a.n_groups), dim3(kWave * kWavesPerGroup), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -721,9 +1003,26 @@ hipError_t launch_fused(int64_t K, const KernelArgs& a, hipStream_t stream)
     }
 }
 
-template <Elt IN, bool GATE_SUM = false>
-hipError_t launch_fused_out(kkt_dtype_t od, int64_t K, const KernelArgs& a, hipStream_t stream)
+template <Elt IN, Elt OUT>
+hipError_t launch_fused128(int64_t K, const KernelArgs& a, hipStream_t stream)
 {
+    switch (K) {
+    case 64: return launch(kkt_solve128_kernel<IN, OUT, 64>, a, stream);
+    case 128: return launch(kkt_solve128_kernel<IN, OUT, 128>, a, stream);
+    default: return launch(kkt_solve128_kernel<IN, OUT, 256>, a, stream);
+    }
+}
+
+template <Elt IN, bool GATE_SUM = false>
+hipError_t launch_fused_out(kkt_dtype_t od, int64_t K, int64_t chunk, const KernelArgs& a, hipStream_t stream)
+{
+    if (chunk == 2 * kChunk) {
+        switch (od) {
+        case KKT_DTYPE_F32: return launch_fused128<IN, Elt::F32>(K, a, stream);
+        case KKT_DTYPE_BF16: return launch_fused128<IN, Elt::BF16>(K, a, stream);
+        default: return launch_fused128<IN, Elt::F16>(K, a, stream);
+        }
+    }
     switch (od) {
     case KKT_DTYPE_F32: return launch_fused<IN, Elt::F32, GATE_SUM>(K, a, stream);
     case KKT_DTYPE_BF16: return launch_fused<IN, Elt::BF16, GATE_SUM>(K, a, stream);
@@ -753,11 +1052,13 @@ constexpr int64_t kRemapMaxGroups = 1024;
 #endif
 
 // Checks shared by every entry point and the launch geometry.  in_row_bytes
-// and out_row_bytes are the strides between consecutive tokens of one head.
+// and out_row_bytes are the strides between consecutive tokens of one head;
+// chunk is 64 (one tile per wave) or 128 (one tile per workgroup).
 // Returns KKT_OK with a filled in; makes no HIP call unless the arguments pass.
 kkt_status_t setup(KernelArgs& a, const void* in, const float* g, const float* beta,
                    const int32_t* cu_seqlens, int64_t num_seqs, int64_t B, int64_t T, int64_t H,
-                   int64_t in_row_bytes, int64_t out_row_bytes, void* out, hipStream_t stream)
+                   int64_t in_row_bytes, int64_t out_row_bytes, void* out, hipStream_t stream,
+                   int64_t chunk = kChunk)
 {
     if (in == nullptr || out == nullptr) return fail(KKT_ERR_INVALID_ARGUMENT, "input and output must not be NULL");
     // the kernel moves the row tensors in 16-byte vectors, g / beta / cu_seqlens in 4-byte words
@@ -768,14 +1069,15 @@ kkt_status_t setup(KernelArgs& a, const void* in, const float* g, const float* b
         (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0) {
         return fail(KKT_ERR_INVALID_ARGUMENT, "g, beta and cu_seqlens must be 4-byte aligned");
     }
-    // 32-bit in-tile offsets: 64 rows of one head must span < 2 GiB
-    if (kChunk * in_row_bytes >= (1LL << 31) || kChunk * out_row_bytes >= (1LL << 31)) {
+    // 32-bit in-tile offsets: the rows of one chunk of one head must span < 2 GiB
+    if (chunk * in_row_bytes >= (1LL << 31) || chunk * out_row_bytes >= (1LL << 31)) {
         return fail(KKT_ERR_UNSUPPORTED, "H * K too large for one launch");
     }
-    const int64_t chunks_per_row = (T + kChunk - 1) / kChunk;
-    // Packed sequences: at most floor(T/64) + num_seqs chunks; surplus waves exit.
-    const int64_t n_chunks = (cu_seqlens == nullptr) ? B * chunks_per_row : T / kChunk + num_seqs;
+    const int64_t chunks_per_row = (T + chunk - 1) / chunk;
+    // Packed sequences: at most floor(T/chunk) + num_seqs chunks; surplus tiles exit.
+    const int64_t n_chunks = (cu_seqlens == nullptr) ? B * chunks_per_row : T / chunk + num_seqs;
     const int64_t n_tiles = n_chunks * H;
+    const int64_t tiles_per_group = (chunk == kChunk) ? kWavesPerGroup : 1;
     if (n_tiles >= (1LL << 31) - kWavesPerGroup || num_seqs >= (1LL << 31) - 1) {
         return fail(KKT_ERR_UNSUPPORTED, "problem too large for one launch");
     }
@@ -802,11 +1104,11 @@ kkt_status_t setup(KernelArgs& a, const void* in, const float* g, const float* b
     a.n_tiles = (int32_t)n_tiles;
     a.k_row_bytes = (uint32_t)in_row_bytes;
     a.o_row_bytes = (uint32_t)out_row_bytes;
-    const int64_t groups = (n_tiles + kWavesPerGroup - 1) / kWavesPerGroup;
+    const int64_t groups = (n_tiles + tiles_per_group - 1) / tiles_per_group;
     a.n_groups = (uint32_t)groups;
     a.xcd_order = groups <= kRemapMaxGroups ? kContiguous : KKT_LARGE_GRID_ORDER;
     // runs of the largest power of two <= the workgroups per chunk
-    const int64_t per_chunk = (H + kWavesPerGroup - 1) / kWavesPerGroup;
+    const int64_t per_chunk = (H + tiles_per_group - 1) / tiles_per_group;
     int lg = 0;
     while ((2LL << lg) <= per_chunk && lg < 16) ++lg;
     a.log2_group_run = lg;
@@ -836,21 +1138,21 @@ extern "C" kkt_status_t kkt_solve(const void* k, const float* g, const float* be
 {
     g_last_error.clear();
     // ---- argument checks: no HIP call before they pass
-    if (chunk_size != kChunk) return fail(KKT_ERR_UNSUPPORTED, "chunk_size must be 64");
+    if (chunk_size != kChunk && chunk_size != 2 * kChunk) return fail(KKT_ERR_UNSUPPORTED, "chunk_size must be 64 or 128");
     if (!valid_dtype((int)in_dtype) || !valid_dtype((int)out_dtype)) return fail(KKT_ERR_INVALID_ARGUMENT, "unknown dtype");
     kkt_status_t st = check_k_sizes(B, T, H, K, num_seqs, cu_seqlens);
     if (st != KKT_OK) return st;
     if (T == 0) return KKT_OK;
     KernelArgs a;
     st = setup(a, k, g, beta, cu_seqlens, num_seqs, B, T, H, H * K * dtype_bytes(in_dtype),
-               H * kChunk * dtype_bytes(out_dtype), out, stream);
+               H * chunk_size * dtype_bytes(out_dtype), out, stream, chunk_size);
     if (st != KKT_OK) return st;
 
     hipError_t e;
     switch (in_dtype) {
-    case KKT_DTYPE_F32: e = launch_fused_out<Elt::F32>(out_dtype, K, a, stream); break;
-    case KKT_DTYPE_BF16: e = launch_fused_out<Elt::BF16>(out_dtype, K, a, stream); break;
-    default: e = launch_fused_out<Elt::F16>(out_dtype, K, a, stream); break;
+    case KKT_DTYPE_F32: e = launch_fused_out<Elt::F32>(out_dtype, K, chunk_size, a, stream); break;
+    case KKT_DTYPE_BF16: e = launch_fused_out<Elt::BF16>(out_dtype, K, chunk_size, a, stream); break;
+    default: e = launch_fused_out<Elt::F16>(out_dtype, K, chunk_size, a, stream); break;
     }
     if (e != hipSuccess) return fail(KKT_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(e));
     return KKT_OK;
@@ -878,9 +1180,9 @@ extern "C" kkt_status_t kkt_solve_gate_cumsum(const void* k, const float* g_deca
 
     hipError_t e;
     switch (in_dtype) {
-    case KKT_DTYPE_F32: e = launch_fused_out<Elt::F32, true>(out_dtype, K, a, stream); break;
-    case KKT_DTYPE_BF16: e = launch_fused_out<Elt::BF16, true>(out_dtype, K, a, stream); break;
-    default: e = launch_fused_out<Elt::F16, true>(out_dtype, K, a, stream); break;
+    case KKT_DTYPE_F32: e = launch_fused_out<Elt::F32, true>(out_dtype, K, kChunk, a, stream); break;
+    case KKT_DTYPE_BF16: e = launch_fused_out<Elt::BF16, true>(out_dtype, K, kChunk, a, stream); break;
+    default: e = launch_fused_out<Elt::F16, true>(out_dtype, K, kChunk, a, stream); break;
     }
     if (e != hipSuccess) return fail(KKT_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(e));
     return KKT_OK;

@@ -89,11 +89,11 @@ def version() -> int:
     return int(load_library().kkt_version())
 
 
-def _k_inputs(k, g, beta, cu_seqlens, chunk_size):
+def _k_inputs(k, g, beta, cu_seqlens, chunk_size, chunk_sizes=(64,)):
     """Shared checks of the entry points that take k; returns contiguous
     tensors and the number of sequences."""
-    if chunk_size != 64:
-        raise ValueError("chunk_size must be 64")
+    if chunk_size not in chunk_sizes:
+        raise ValueError(f"chunk_size must be {' or '.join(str(c) for c in chunk_sizes)}")
     if k.dim() != 4:
         raise ValueError("k must be [B, T, H, K]")
     if k.dtype not in _TORCH_TO_KKT:
@@ -137,22 +137,23 @@ def kkt_solve(k: torch.Tensor, g: Optional[torch.Tensor] = None, beta: Optional[
               cu_seqlens: Optional[torch.Tensor] = None, chunk_size: int = 64,
               output_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None,
               stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
-    """Rows of (I + A)^{-1} per 64-token chunk, shape [B, T, H, 64].
+    """Rows of (I + A)^{-1} per chunk, shape [B, T, H, chunk_size].
 
     Mirrors the fused API of MindSpeed-Ops PR #135 (user-facing-change
     section): ``k`` [B,T,H,K] (bf16 / fp16 / fp32), ``g`` and ``beta``
     [B,T,H] fp32 or None, ``cu_seqlens`` int32 [N+1] or None (then B == 1),
-    ``chunk_size`` must be 64 (ValueError otherwise), ``output_dtype``
-    defaults to k's dtype.  ``out`` may be given (contiguous, [B,T,H,64]);
-    otherwise it is allocated uninitialised, since the kernel writes every
-    element.
+    ``output_dtype`` defaults to k's dtype.  ``chunk_size`` is 64, the API's
+    value, or 128 (the chunk size of the GDR case page's tiling); anything
+    else raises ValueError.  ``out`` may be given (contiguous,
+    [B,T,H,chunk_size]); otherwise it is allocated uninitialised, since the
+    kernel writes every element.
     """
-    k, g, beta, cu_seqlens, num_seqs = _k_inputs(k, g, beta, cu_seqlens, chunk_size)
+    k, g, beta, cu_seqlens, num_seqs = _k_inputs(k, g, beta, cu_seqlens, chunk_size, (64, 128))
     B, T, H, K = k.shape
     odt = k.dtype if output_dtype is None else output_dtype
     if odt not in _TORCH_TO_KKT:
         raise TypeError(f"unsupported output dtype {odt}")
-    out = _out_tensor(out, (B, T, H, 64), odt, k.device)
+    out = _out_tensor(out, (B, T, H, chunk_size), odt, k.device)
     with torch.cuda.device(k.device):
         st = kkt_solve_raw(_ptr(k), _ptr(g), _ptr(beta), _ptr(cu_seqlens), num_seqs, B, T, H, K, chunk_size,
                            _TORCH_TO_KKT[k.dtype], _TORCH_TO_KKT[odt], _ptr(out), _stream_ptr(stream, k.device))

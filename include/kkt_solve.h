@@ -52,7 +52,10 @@ typedef enum {
 /*
  * kkt_solve: the fused op (PR #135 page: the fused API takes k, g, beta,
  * cu_seqlens, chunk_size and an output dtype and returns (I+A)^{-1} of shape
- * [B,T,H,64]; only chunk_size 64 is served, other values are an error).
+ * [B,T,H,64]).  chunk_size 64 is the API's value; 128 is also served (the
+ * chunk size of the PyPTO GatedDeltaRule case page's tiling, section 3.2):
+ * everything above then holds with chunks of 128 tokens and 128-wide output
+ * rows, out [B,T,H,128].  Other values are an error.
  *
  *   k          device, [B,T,H,K] of in_dtype, contiguous (H*K elements per token).
  *   g          device, [B,T,H] fp32 chunk-local cumulative log-decay, or NULL
@@ -71,11 +74,11 @@ typedef enum {
  *   num_seqs   number of sequences; ignored when cu_seqlens is NULL.
  *   B, T, H, K sizes.  T may be 0 (nothing is launched).
  *              K must be 64, 128 or 256.
- *   chunk_size must be 64.
+ *   chunk_size 64 or 128 (the chunk length; also the width of an output row).
  *   in_dtype   element type of k.
  *   out_dtype  element type of out.  bf16 / f16 results are rounded to nearest
  *              even from the fp32 value.
- *   out        device, [B,T,H,64] of out_dtype, contiguous; every element is
+ *   out        device, [B,T,H,chunk_size] of out_dtype, contiguous; every element is
  *              written (for varlen: every element of the rows covered by the
  *              sequences).  Must not overlap any input.
  *   stream     HIP stream the kernel is enqueued on (NULL: the null stream).
@@ -115,8 +118,8 @@ kkt_status_t kkt_solve(const void* k, const float* g, const float* beta,
  *   The sum is a 6-level tree (a parallel inclusive scan over the 64 rows) in
  *   fp32; its result differs from a left-to-right sum by rounding only.
  *   kkt_solve(k, g_out, ...) on the g_out this call wrote gives bit-identical
- *   output.  Everything else (arguments, alignment, errors) as for kkt_solve;
- *   g_out must be 4-byte aligned.
+ *   output.  Everything else (arguments, alignment, errors) as for kkt_solve,
+ *   except that chunk_size must be 64; g_out must be 4-byte aligned.
  */
 kkt_status_t kkt_solve_gate_cumsum(const void* k, const float* g_decay, const float* beta,
                                    const int32_t* cu_seqlens, int64_t num_seqs,
@@ -135,7 +138,8 @@ kkt_status_t kkt_solve_gate_cumsum(const void* k, const float* g_decay, const fl
  *   in fp32, shape [B,T,H,64], every element of every covered row written.
  *
  *   k, g, beta, cu_seqlens, num_seqs, B, T, H, K, chunk_size, in_dtype, stream:
- *   as for kkt_solve (same alignment rules, same errors).  A_out: device,
+ *   as for kkt_solve (same alignment rules, same errors), except that
+ *   chunk_size must be 64.  A_out: device,
  *   [B,T,H,64] fp32, contiguous, 16-byte aligned, must not overlap any input.
  *   The A it writes is bit-identical to the A that kkt_solve inverts.
  */
@@ -153,7 +157,8 @@ kkt_status_t kkt_scaled_dot(const void* k, const float* g, const float* beta,
  *              chunk (cut as above) only the strictly lower entries A[i][j],
  *              j < i < L, are read; the diagonal, the upper part and the
  *              columns j >= L are ignored (they may hold anything).
- *   cu_seqlens, num_seqs, B, T, H, chunk_size, stream: as for kkt_solve.
+ *   cu_seqlens, num_seqs, B, T, H, stream: as for kkt_solve; chunk_size must
+ *              be 64.
  *   out_dtype, out: as for kkt_solve: rows of (I + strict_lower(A))^{-1},
  *              [B,T,H,64], upper zeros written.  out must not overlap A.
  *

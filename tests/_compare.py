@@ -41,19 +41,20 @@ def decode(got: np.ndarray, out_dtype: str) -> np.ndarray:
     return got.view(np.float16).astype(np.float64)
 
 
-def structural_masks(T: int, cu_seqlens=None):
-    """[T, 64] masks: diagonal, strictly upper (incl. columns >= L), strictly lower."""
-    local, _length = workloads.chunk_geometry(T, cu_seqlens)
-    j = np.arange(64)[None, :]
+def structural_masks(T: int, cu_seqlens=None, chunk: int = 64):
+    """[T, chunk] masks: diagonal, strictly upper (incl. columns >= L), strictly lower."""
+    local, _length = workloads.chunk_geometry(T, cu_seqlens, chunk)
+    j = np.arange(chunk)[None, :]
     i = local[:, None]
     return (j == i), (j > i), (j < i)
 
 
 def compare(got: np.ndarray, ref: np.ndarray, out_dtype: str, cu_seqlens=None, label: str = "") -> dict:
-    """Assert the criteria above; return the measured figures."""
+    """Assert the criteria above; return the measured figures.  The chunk
+    size is the width of the rows (64 or 128)."""
     B, T, H, C = ref.shape
     assert got.shape == ref.shape, (got.shape, ref.shape)
-    diag, upper, lower = (m[None, :, None, :] for m in structural_masks(T, cu_seqlens))
+    diag, upper, lower = (m[None, :, None, :] for m in structural_masks(T, cu_seqlens, C))
     diag = np.broadcast_to(diag, ref.shape)
     upper = np.broadcast_to(upper, ref.shape)
     lower = np.broadcast_to(lower, ref.shape)

@@ -1,0 +1,140 @@
+"""GPU parity of 128-token chunks (``kkt_solve`` with chunk_size=128): every
+output element against the fp64 oracle at chunk size 128, by the criteria of
+the 64-token op, plus the block structure of the result against the library's
+own 64-token results.
+
+Every case prints what it runs before touching the GPU.
+"""
+from __future__ import annotations
+
+import json
+
+import numpy as np
+import pytest
+
+import oracle
+from chunked_gated_delta_token_amd import workloads as W
+from tests._compare import compare
+from tests._gpu_util import TORCH_DT, from_device, load_kkt, say, to_device
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+CH = 128
+
+
+@pytest.fixture(scope="module")
+def kkt():
+    return load_kkt()
+
+
+def run(kkt, inp: W.Inputs, out_dtype: str, chunk: int = CH, tensors=None) -> np.ndarray:
+    k, g, b, cu = tensors if tensors is not None else to_device(inp)
+    B, T, H, _ = k.shape
+    out = torch.full((B, T, H, chunk), float("nan"), dtype=TORCH_DT[out_dtype], device=k.device)
+    kkt.kkt_solve(k, g, b, cu, chunk_size=chunk, output_dtype=TORCH_DT[out_dtype], out=out)
+    torch.cuda.synchronize()
+    return from_device(out, out_dtype)
+
+
+def check(kkt, inp: W.Inputs, out_dtype: str, label: str) -> dict:
+    w = inp.workload
+    say(f"[case] chunk128 {label}: B={w.B} T={w.T} H={w.H} K={w.K} in={w.in_dtype} out={out_dtype} "
+        f"g={inp.g is not None} beta={inp.beta is not None} "
+        f"seqs={0 if inp.cu_seqlens is None else len(inp.cu_seqlens) - 1}")
+    got = run(kkt, inp, out_dtype)
+    ref = oracle.kkt_solve_ref(inp.k64(), inp.g, inp.beta, inp.cu_seqlens, chunk_size=CH)
+    stats = compare(got, ref, out_dtype, inp.cu_seqlens, label)
+    say("[ok] " + json.dumps(stats))
+    return stats
+
+
+@pytest.mark.parametrize("name", list(W.WORKLOADS))
+def test_chunk128_full_parity(kkt, name):
+    inp = W.generate(name)
+    check(kkt, inp, inp.workload.out_dtype, name)
+
+
+@pytest.mark.parametrize("in_dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16", "f16"])
+def test_chunk128_dtypes(kkt, in_dtype, out_dtype):
+    inp = W.generate("T256_H8_bf16_f32", B=2, T=300, H=3, in_dtype=in_dtype, seed=3000)
+    check(kkt, inp, out_dtype, f"{in_dtype}->{out_dtype}")
+
+
+@pytest.mark.parametrize("T", [1, 2, 63, 64, 65, 127, 128, 129, 191, 255, 256])
+def test_chunk128_lengths(kkt, T):
+    gate, beta = bool(T % 2), bool((T // 2) % 2)
+    inp = W.generate("T256_H8_bf16_f32", B=2, T=T, H=3, seed=3100 + T, gate=gate, beta=beta)
+    check(kkt, inp, "f32", f"T={T}")
+
+
+@pytest.mark.parametrize("K,in_dtype", [(64, "bf16"), (256, "bf16"), (128, "f32"), (256, "f32"), (64, "f16")])
+def test_chunk128_head_dims(kkt, K, in_dtype):
+    inp = W.generate("T256_H8_bf16_f32", T=260, H=2, K=K, in_dtype=in_dtype, seed=3200 + K)
+    check(kkt, inp, "f32", f"K={K} {in_dtype}")
+
+
+@pytest.mark.parametrize("gate", [False, True])
+@pytest.mark.parametrize("beta", [False, True])
+def test_chunk128_gate_beta(kkt, gate, beta):
+    inp = W.generate("T256_H8_bf16_f32", T=300, H=5, seed=3300, gate=gate, beta=beta)
+    check(kkt, inp, "bf16", f"gate={gate} beta={beta}")
+
+
+def test_chunk128_gate_beyond_the_clamp(kkt):
+    """Decays of up to -1.5 per token: gate differences across the two halves
+    reach about -190, far beyond the clamp, inside one chunk as well."""
+    inp = W.generate("T256_H8_bf16_f32", T=256, H=2, seed=3400)
+    rng = np.random.default_rng(3401)
+    inc = -rng.uniform(0.0, 1.5, inp.g.shape)
+    g = np.empty_like(inc)
+    for t0 in range(0, 256, CH):
+        g[:, t0:t0 + CH] = np.cumsum(inc[:, t0:t0 + CH], axis=1)
+    inp.g = g.astype(np.float32)
+    check(kkt, inp, "f32", "gate spread ~ -190")
+
+
+VARLEN = {
+    "mixed": [1, 63, 64, 65, 0, 127, 128, 129, 300, 5],
+    "many_short": [3, 70] * 40,
+}
+
+
+@pytest.mark.parametrize("case", list(VARLEN))
+def test_chunk128_varlen(kkt, case):
+    inp = W.generate("T256_H8_bf16_f32", lengths=VARLEN[case], H=3, seed=3500)
+    check(kkt, inp, "f32", f"varlen {case}")
+
+
+@pytest.mark.parametrize("T,H", [(40000, 7), (30000, 8)])
+def test_chunk128_large_grid(kkt, T, H):
+    """Grids above 1024 workgroups (one per chunk and head): runs of heads on
+    one XCD, a remainder of workgroups, and H=7."""
+    inp = W.generate("T256_H8_bf16_f32", T=T, H=H, seed=3600 + H)
+    check(kkt, inp, "bf16", f"large grid T={T} H={H}")
+
+
+def test_chunk128_halves_equal_64_token_results(kkt):
+    """The diagonal 64x64 blocks of each 128-token chunk are bit-identical to
+    the 64-token op on each half (the same arithmetic on the same values), and
+    the upper block is +0.0."""
+    inp = W.generate("T256_H8_bf16_f32", B=2, T=512, H=3, seed=3700)
+    say("[case] chunk128 halves vs chunk64: B=2 T=512 H=3")
+    t = to_device(inp)
+    x128 = run(kkt, inp, "f32", tensors=t)
+    x64 = run(kkt, inp, "f32", chunk=64, tensors=t)
+    for t0 in range(0, 512, CH):
+        assert np.array_equal(x128[:, t0:t0 + 64, :, :64].view(np.uint32), x64[:, t0:t0 + 64].view(np.uint32))
+        assert np.array_equal(x128[:, t0 + 64:t0 + CH, :, 64:].view(np.uint32),
+                              x64[:, t0 + 64:t0 + CH].view(np.uint32))
+        assert np.all(x128[:, t0:t0 + 64, :, 64:].view(np.uint32) == 0)
+
+
+def test_chunk128_repeatable(kkt):
+    inp = W.generate("T8192_H8_bf16_f32")
+    say("[case] chunk128 repeatable: T8192_H8")
+    t = to_device(inp)
+    a = run(kkt, inp, "f32", tensors=t)
+    b = run(kkt, inp, "f32", tensors=t)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))

@@ -276,7 +276,7 @@ def test_error_paths(kkt):
     inp = W.generate("T256_H8_bf16_f32", T=64, H=1, seed=700)
     k, g, b, _ = to_device(inp)
     with pytest.raises(ValueError):
-        kkt.kkt_solve(k, g, b, chunk_size=128)
+        kkt.kkt_solve(k, g, b, chunk_size=256)
     out = torch.empty((1, 64, 1, 64), device=k.device)
     for kwargs, status in (
         (dict(chunk_size=32), kkt.KKT_ERR_UNSUPPORTED),
