@@ -69,7 +69,10 @@ def test_chunk128_lengths(kkt, T):
     check(kkt, inp, "f32", f"T={T}")
 
 
-@pytest.mark.parametrize("K,in_dtype", [(64, "bf16"), (256, "bf16"), (128, "f32"), (256, "f32"), (64, "f16")])
+# small grids stage the key tile in LDS when it holds at most 4 k-steps per
+# lane (16-bit K <= 128, fp32 K = 64); the others load keys per wave
+@pytest.mark.parametrize("K,in_dtype", [(64, "bf16"), (256, "bf16"), (64, "f32"), (128, "f32"), (256, "f32"),
+                                        (64, "f16")])
 def test_chunk128_head_dims(kkt, K, in_dtype):
     inp = W.generate("T256_H8_bf16_f32", T=260, H=2, K=K, in_dtype=in_dtype, seed=3200 + K)
     check(kkt, inp, "f32", f"K={K} {in_dtype}")
@@ -109,8 +112,9 @@ def test_chunk128_varlen(kkt, case):
 
 @pytest.mark.parametrize("T,H", [(40000, 7), (30000, 8)])
 def test_chunk128_large_grid(kkt, T, H):
-    """Grids above 1024 workgroups (one per chunk and head): runs of heads on
-    one XCD, a remainder of workgroups, and H=7."""
+    """Grids above 1024 workgroups (one per chunk and head; keys loaded per
+    wave, not staged): runs of heads on one XCD, a remainder of workgroups,
+    and H=7."""
     inp = W.generate("T256_H8_bf16_f32", T=T, H=H, seed=3600 + H)
     check(kkt, inp, "bf16", f"large grid T={T} H={H}")
 
