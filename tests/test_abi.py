@@ -182,6 +182,31 @@ def test_split_entry_points_empty_is_a_no_op(lib):
     assert kkt.last_error() == ""
 
 
+def test_last_error_is_per_thread(lib):
+    """Concurrent failing calls on several host threads: each thread reads
+    its own message (argument checks only; no GPU needed)."""
+    import threading
+    from chunked_gated_delta_token_amd import kkt
+    cases = [(dict(chunk_size=32), "chunk_size"), (dict(K=100), "K must be"), (dict(in_dtype=9), "dtype"),
+             (dict(B=0), ">= 1")]
+    errors = []
+
+    def worker(over, msg):
+        for _ in range(200):
+            st = _call(lib, **over)
+            text = kkt.last_error()
+            if st == 0 or msg not in text:
+                errors.append((over, st, text))
+                return
+
+    threads = [threading.Thread(target=worker, args=c) for c in cases]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors[:3]
+
+
 def test_empty_sequence_is_a_no_op(lib):
     from chunked_gated_delta_token_amd import kkt
     assert _call(lib, T=0, k=None, out=None) == 0

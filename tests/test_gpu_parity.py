@@ -245,6 +245,39 @@ def test_repeatable_and_stream(kkt):
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
 
 
+def test_graph_capture_replays(kkt):
+    """kkt_solve captured in a HIP graph (the library launches one kernel and
+    records no memset): every replay, with eager work and synchronisations in
+    between, equals the eager result bit for bit, also after the inputs
+    change in place."""
+    inp = W.generate("T2000_H8_bf16_bf16")
+    say("[case] graph capture: T2000_H8 bf16 -> bf16, 4 replays")
+    k, g, b, cu = to_device(inp)
+    B, T, H, _ = k.shape
+    out = torch.empty((B, T, H, 64), dtype=torch.bfloat16, device=k.device)
+    eager = torch.empty_like(out)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        kkt.kkt_solve(k, g, b, output_dtype=torch.bfloat16, out=eager, stream=s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        kkt.kkt_solve(k, g, b, output_dtype=torch.bfloat16, out=out, stream=s)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s):
+            graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), rep
+        if rep == 1:  # new values in the captured input buffers
+            k.mul_(-1.0)
+            with torch.cuda.stream(s):
+                kkt.kkt_solve(k, g, b, output_dtype=torch.bfloat16, out=eager, stream=s)
+            torch.cuda.synchronize()
+
+
 # ---------------------------------------------------------------- golden file on the GPU
 def test_hand_worked_golden_on_gpu(kkt):
     path = os.path.join(os.path.dirname(__file__), "golden", "hand_worked_chunks.json")
