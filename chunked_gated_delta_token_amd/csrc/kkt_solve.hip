@@ -43,6 +43,12 @@
 //       next product wants for its left operand; no shuffles are needed.
 //   a8  each 16-row block row is staged through LDS and written as full
 //       contiguous rows (256 B fp32 / 128 B bf16), upper zeros included.
+//
+// The same per-wave pipeline (chunk_rows) also serves the unfused chain's two
+// steps (ScaledDot: a1-a5 and A written in fp32; SolveTril: A read back, then
+// a6-a8), the gate formed from per-token log-decays (a wave scan before a4),
+// and 128-token chunks (kkt_solve128_kernel: the two 64-row halves plus the
+// block below the diagonal, one workgroup per chunk).
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>

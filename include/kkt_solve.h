@@ -81,7 +81,9 @@ typedef enum {
  *   out        device, [B,T,H,chunk_size] of out_dtype, contiguous; every element is
  *              written (for varlen: every element of the rows covered by the
  *              sequences).  Must not overlap any input.
- *   stream     HIP stream the kernel is enqueued on (NULL: the null stream).
+ *   stream     HIP stream the kernel is enqueued on (NULL: the null stream);
+ *              it must belong to the calling thread's current device, which
+ *              is the device checked to be gfx950.
  *
  * Alignment: k and out 16-byte aligned; g, beta and cu_seqlens 4-byte aligned
  * (KKT_ERR_INVALID_ARGUMENT otherwise).
