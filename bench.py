@@ -225,6 +225,64 @@ def summarize_traffic(dirs, copy_bytes: int, op: str, workload: str, chunk: int 
     print("\n".join(lines))
 
 
+MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F16",
+                 "SQ_INSTS_VALU_MFMA_MOPS_F32")
+N_SIMDS = 256 * 4               # MI355X: 256 CUs x 4 SIMDs
+CLOCK_HZ = 2.4e9                # MI355X peak engine clock
+
+
+def mfma_file(op: str, workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"mfma_{ENTRY[op]}_{workload}.txt")
+
+
+def summarize_mfma(directory: str, op: str, workload: str, chunk: int = 64):
+    """Matrix-core counters of the op's kernel from one rocprofv3 --pmc pass:
+    MFMA busy cycles (summed over SIMDs) and MFMA operations (units of 512
+    flop) per launch, medians over the launches."""
+    import statistics
+    key = op_key(op, chunk)
+    kname = KERNELS[key]
+    med = {c: statistics.median(_counter_values(directory, c, kname)) for c in MFMA_COUNTERS}
+    sel = f"--op {op} --workload {workload}" + (f" --chunk {chunk}" if chunk != 64 else "")
+    lines = [
+        f"# MFMA counters of {kname}, workload {workload} (medians per launch)",
+        "# commands (from /tmp, repository at $R; the last one wrote this file):",
+        f"#   rocprofv3 --pmc {' '.join(MFMA_COUNTERS)} --output-format csv -d <dir> -o p -- python -u $R/bench.py "
+        f"{sel} --timing eager --steps 10 --warmup 2 --no-cpu-baseline",
+        f"#   python $R/bench.py --summarize-mfma <dir> {sel}",
+        "# busy cycles are summed over the SIMDs; one MFMA operation (MOPS) is 512 flop",
+        f"kernel_source_sha256_16: {source_digest()}",
+        f"mfma_busy_cycles_per_launch: {med['SQ_VALU_MFMA_BUSY_CYCLES']:.0f}",
+        f"mfma_flop_bf16_per_launch: {512 * med['SQ_INSTS_VALU_MFMA_MOPS_BF16']:.0f}",
+        f"mfma_flop_f16_per_launch: {512 * med['SQ_INSTS_VALU_MFMA_MOPS_F16']:.0f}",
+        f"mfma_flop_f32_per_launch: {512 * med['SQ_INSTS_VALU_MFMA_MOPS_F32']:.0f}",
+    ]
+    path = mfma_file(key, workload)
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def read_mfma(digest: str, path: str):
+    """The counter summary's values, if taken on the current kernel source."""
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256_16") != digest:
+        return None
+    try:
+        return {k: float(vals[k]) for k in ("mfma_busy_cycles_per_launch", "mfma_flop_bf16_per_launch",
+                                            "mfma_flop_f16_per_launch", "mfma_flop_f32_per_launch")}
+    except (KeyError, ValueError):
+        return None
+
+
 def summarize_trace(directory: str, op: str, workload: str, run_log: str = None, plain_log: str = None,
                     chunk: int = 64):
     """Write profiles/<entry>_<workload>.kernel_trace.txt from a rocprofv3
@@ -331,9 +389,16 @@ def main():
     ap.add_argument("--copy-bytes", type=int, default=0, help="size used by the copy-calibration runs")
     ap.add_argument("--summarize-trace", metavar="DIR",
                     help="write the kernel-trace summary of --op from a rocprofv3 --kernel-trace --stats directory")
+    ap.add_argument("--summarize-mfma", metavar="DIR",
+                    help="write the MFMA-counter summary of --op from a rocprofv3 --pmc directory")
     ap.add_argument("--run-log", help="bench.py output of the profiled run (with --summarize-trace)")
     ap.add_argument("--plain-log", help="bench.py output of an unprofiled run (with --summarize-trace)")
     args = ap.parse_args()
+
+    if args.summarize_mfma:
+        from chunked_gated_delta_token_amd import workloads as W
+        summarize_mfma(args.summarize_mfma, args.op, args.workload or W.BENCH_WORKLOAD, args.chunk)
+        return
 
     if args.summarize_trace:
         from chunked_gated_delta_token_amd import workloads as W
@@ -541,6 +606,19 @@ def main():
                      "event_ms_per_step": round(ev_ms, 6), "launches_per_step": len(calls[0]),
                      "kernel_source_sha256_16": digest},
     }
+    mf = None if op == "chain" else read_mfma(digest, mfma_file(key, name))
+    if mf is not None:
+        # matrix-core use of the step, from the committed counter summary and
+        # this run's event time: busy share of all SIMD cycles, and the Gram's
+        # (16-bit) MFMA rate against the dense bf16/f16 peak
+        cycles = ev_ms * 1e-3 * CLOCK_HZ * N_SIMDS
+        gram = mf["mfma_flop_bf16_per_launch"] + mf["mfma_flop_f16_per_launch"]
+        line["roofline"]["mfma"] = {
+            "busy_frac": round(mf["mfma_busy_cycles_per_launch"] / cycles, 4),
+            "gram_tflops": round(gram / (ev_ms * 1e-3) / 1e12, 2) if gram else None,
+            "gram_frac_of_16bit_peak": round(gram / (ev_ms * 1e-3) / 2.5e15, 4) if gram else None,
+            "f32_tflops": round(mf["mfma_flop_f32_per_launch"] / (ev_ms * 1e-3) / 1e12, 2),
+        }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inp, nbytes, args.cpu_seconds, op)
     print(json.dumps(line), flush=True)
