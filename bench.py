@@ -577,8 +577,9 @@ def main():
     n_tiles = w.H * (sum(-(-(int(inp.cu_seqlens[s + 1]) - int(inp.cu_seqlens[s])) // chunk)
                          for s in range(num_seqs)) if num_seqs else w.B * (-(-w.T // chunk)))
     value = nbytes / (ms_per_step * 1e-3) / 1e9
-    metric = METRIC if (op == "fused" and chunk == 64) else {
-        "fused": "fused KKT+solve with 128-token chunks ms/iter & achieved HBM GB/s, 1 GPU",
+    metric = METRIC if (op == "fused" and chunk == 64 and name == W.BENCH_WORKLOAD) else {
+        "fused": f"fused KKT+solve{' with 128-token chunks' if chunk == 128 else ''} ms/iter & achieved HBM "
+                 f"GB/s on {name}, 1 GPU",
         "gate_cumsum": "fused KKT+solve with the chunk-local gate sum in the kernel ms/iter & achieved HBM GB/s, 1 GPU",
         "scaled_dot": "KKT A alone (first step of the unfused chain) ms/iter & achieved HBM GB/s, 1 GPU",
         "solve_tril": "solve of a given A (second step of the unfused chain) ms/iter & achieved HBM GB/s, 1 GPU",
