@@ -112,11 +112,24 @@ def test_large_grid_tile_order(kkt, T, H):
 
 
 # ---------------------------------------------------------------- varlen
+def _lengths(seed, n, lo, hi, empty_every=0):
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(lo, hi + 1, size=n)
+    if empty_every:
+        lens[::empty_every] = 0
+    return [int(x) for x in lens]
+
+
 VARLEN_CASES = {
     "tiny_and_empty": [1, 2, 3, 0, 64, 65, 0, 130, 5],
     "single": [777],
     "all_empty_but_one": [0, 0, 40, 0],
-    "many_short": [1, 3] * 70,  # 140 sequences: more than one 64-wide scan pass
+    "many_short": [1, 3] * 70,  # 140 sequences
+    # the chunk search reads 512 sequences per pass: exactly one pass, one
+    # more sequence, and many passes with empty sequences among them
+    "pass_512": _lengths(510, 512, 1, 70),
+    "pass_513": _lengths(511, 513, 1, 70),
+    "passes_3000": _lengths(512, 3000, 0, 40, empty_every=7),
 }
 
 
@@ -129,7 +142,8 @@ def test_varlen(kkt, case):
     # call per sequence, bit for bit
     packed = run_gpu(kkt, inp, "f32")
     cu = inp.cu_seqlens
-    for s in range(len(lens)):
+    picked = range(len(lens)) if len(lens) <= 200 else sorted(set(range(0, len(lens), 97)) | {len(lens) - 1})
+    for s in picked:
         a, b = int(cu[s]), int(cu[s + 1])
         if b == a:
             continue
