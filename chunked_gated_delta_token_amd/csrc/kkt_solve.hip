@@ -9,8 +9,8 @@
 //
 // One wave64 owns one (chunk, head) tile from load to store; nothing goes
 // back to HBM between the steps.
-//   a1  tile -> (b, t0, L, h); for packed sequences a wave-wide prefix scan
-//       over cu_seqlens (no host sync, no index tensor).  Every tensor of the
+//   a1  tile -> (b, t0, L, h); for packed sequences a 64-ary search over
+//       cu_seqlens (no host sync, no index tensor).  Every tensor of the
 //       tile is then addressed through a buffer resource whose base is the
 //       tile's first row and whose size ends after row L-1: loads of rows
 //       >= L return 0 and stores to them are dropped by the hardware range
@@ -60,7 +60,7 @@
 
 #include "kkt_solve.h"
 
-#define KKT_VERSION_NUMBER 500  // 0.5.0
+#define KKT_VERSION_NUMBER 501  // 0.5.1
 
 namespace {
 
@@ -219,46 +219,51 @@ struct Tile {
     int len;       // valid rows L in [1, 64]; 0: no tile
 };
 
-// Packed sequences: the chunk with global index c (chunks of CH tokens,
-// numbered sequence by sequence) is found with a wave-wide inclusive scan of
-// per-sequence chunk counts, 64 sequences per pass.  Offsets are clamped into
-// [0, T].
+// Packed sequences.  Chunk slots are numbered so that a slot can be found
+// from the offsets alone: sequence s (offsets clamped into [0, T]) owns the
+// slots [S(s), S(s) + ceil(len_s / CH)) with S(s) = floor(bos_s / CH) + s.
+// S is strictly increasing, no two ranges overlap and every slot is below
+// T / CH + num_seqs, the grid's bound; slots in no range are empty.  Slot w
+// belongs to the last sequence with S(s) <= w, found by a 64-ary search: each
+// level probes 64 evenly spaced sequences, one per lane, and keeps the span
+// after the last probe that is still <= w, so the search takes
+// ceil(log64(num_seqs)) dependent rounds of loads.
 template <int CH>
-__device__ Tile varlen_tile(const int32_t* __restrict__ cu, int32_t num_seqs, int64_t T, int32_t c, int lane)
+__device__ Tile varlen_tile(const int32_t* __restrict__ cu, int32_t num_seqs, int64_t T, int32_t w, int lane)
 {
+    // offsets are int32, so every clamped offset fits in 32 bits
+    const int32_t t_max = T < INT32_MAX ? (int32_t)T : INT32_MAX;
     Tile t{0, 0};
-    int32_t before = 0;  // chunks in the sequences already passed
-    for (int32_t base = 0; base < num_seqs; base += kWave) {
-        const int32_t s = base + lane;
-        int64_t bos = 0, eos = 0;
-        if (s < num_seqs) {
-            const int64_t a = cu[s], e = cu[s + 1];
-            bos = a < 0 ? 0 : (a > T ? T : a);
-            eos = e < bos ? bos : (e > T ? T : e);
+    int32_t lo = 0, span = num_seqs;  // the sequence sought lies in [lo, lo + span)
+    for (;;) {
+        const int32_t step = (span + kWave - 1) / kWave;
+        const int32_t s = lo + lane * step;
+        int32_t bos = 0, eos = 0;
+        bool le = false;
+        if (lane * step < span) {
+            const int32_t a = cu[s], e = cu[s + 1];
+            bos = a < 0 ? 0 : (a > t_max ? t_max : a);
+            eos = e < bos ? bos : (e > t_max ? t_max : e);
+            le = (int64_t)(bos / CH) + s <= w;
         }
-        const int32_t n = (int32_t)((eos - bos + CH - 1) / CH);
-        int32_t incl = n;
-#pragma unroll
-        for (int d = 1; d < kWave; d <<= 1) {
-            const int32_t up = __shfl_up(incl, d, kWave);
-            if (lane >= d) incl += up;
-        }
-        const bool hit = (s < num_seqs) && (before + incl > c);
-        const uint64_t mask = __ballot(hit);
-        if (mask != 0) {
-            const int src = __builtin_ctzll(mask);
-            const int32_t sel_excl = __shfl(incl - n, src, kWave);
-            const int64_t sel_bos = __shfl(bos, src, kWave);
-            const int64_t sel_eos = __shfl(eos, src, kWave);
-            const int64_t t0 = sel_bos + (int64_t)(c - before - sel_excl) * CH;
-            const int64_t rem = sel_eos - t0;
-            t.row0 = t0;
-            t.len = (int)(rem < CH ? rem : CH);
+        const uint64_t mask = __ballot(le);
+        if (mask == 0) return t;  // (only with offsets that do not start at 0)
+        const int src = 63 - __builtin_clzll(mask);
+        const int32_t end = lo + span;
+        lo += src * step;
+        span = (end - lo < step) ? end - lo : step;
+        if (span <= 1) {
+            const int32_t sel_bos = __shfl(bos, src, kWave);
+            const int32_t sel_eos = __shfl(eos, src, kWave);
+            const int64_t t0 = sel_bos + (int64_t)(w - sel_bos / CH - lo) * CH;
+            if (t0 < sel_eos) {
+                const int64_t rem = sel_eos - t0;
+                t.row0 = t0;
+                t.len = (int)(rem < CH ? rem : CH);
+            }
             return t;
         }
-        before += __shfl(incl, kWave - 1, kWave);
     }
-    return t;
 }
 
 // Workgroup order (see XcdOrder); both remaps are permutations of

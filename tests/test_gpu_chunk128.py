@@ -101,6 +101,9 @@ def test_chunk128_gate_beyond_the_clamp(kkt):
 VARLEN = {
     "mixed": [1, 63, 64, 65, 0, 127, 128, 129, 300, 5],
     "many_short": [3, 70] * 40,
+    # three levels of the chunk search, empty sequences among them
+    "three_levels_4097": [int(x) for x in np.where(np.arange(4097) % 9 == 0, 0,
+                                                   np.random.default_rng(3501).integers(1, 300, 4097))],
 }
 
 

@@ -125,11 +125,14 @@ VARLEN_CASES = {
     "single": [777],
     "all_empty_but_one": [0, 0, 40, 0],
     "many_short": [1, 3] * 70,  # 140 sequences
-    # the chunk search reads 512 sequences per pass: exactly one pass, one
-    # more sequence, and many passes with empty sequences among them
-    "pass_512": _lengths(510, 512, 1, 70),
-    "pass_513": _lengths(511, 513, 1, 70),
-    "passes_3000": _lengths(512, 3000, 0, 40, empty_every=7),
+    # the chunk search narrows 64-fold per level: one level up to 64
+    # sequences, two up to 4096, three beyond; cases on both sides of each
+    # step, with empty sequences among them
+    "one_level_64": _lengths(510, 64, 1, 70),
+    "two_levels_65": _lengths(511, 65, 0, 70, empty_every=5),
+    "two_levels_3000": _lengths(512, 3000, 0, 40, empty_every=7),
+    "two_levels_4096": _lengths(513, 4096, 1, 20),
+    "three_levels_4097": _lengths(514, 4097, 0, 20, empty_every=11),
 }
 
 
@@ -181,6 +184,32 @@ def test_varlen_offsets_are_clamped(kkt):
     assert torch.isnan(guard[:, 80:]).all()
     ref = reference(inp)
     compare(out.cpu().numpy(), ref, "f32", inp.cu_seqlens, "clamped offsets")
+
+
+@pytest.mark.parametrize("chunk", [64, 128])
+@pytest.mark.parametrize("offsets", [
+    [5, 3, 200, -7, 90, 80],     # decreasing, negative, beyond T
+    [-10, 40, 20, 60],
+    [30, 80],                    # not starting at 0: rows 0..29 belong to no sequence
+    [79, 1, 0],
+])
+def test_varlen_malformed_offsets_stay_in_bounds(kkt, offsets, chunk):
+    """Malformed offsets give unspecified rows but never a write outside the
+    output: guard rows on both sides stay NaN, written rows are finite."""
+    inp = W.generate("T256_H8_bf16_f32", T=80, H=2, seed=503)
+    k, g, b, _ = to_device(inp)
+    say(f"[case] malformed offsets {offsets} chunk={chunk}")
+    cu = torch.tensor(offsets, dtype=torch.int32, device=k.device)
+    guard = torch.full((1, 120, 2, chunk), float("nan"), device=k.device)
+    out = guard[:, 20:100]
+    kkt.kkt_solve(k, g, b, cu, chunk_size=chunk, output_dtype=torch.float32, out=out)
+    torch.cuda.synchronize()
+    assert torch.isnan(guard[:, :20]).all() and torch.isnan(guard[:, 100:]).all()
+    rows = out.cpu()
+    written = ~torch.isnan(rows).all(dim=-1)
+    assert torch.isfinite(rows[written]).all()
+    if offsets == [30, 80]:
+        assert not written[:, :30].any() and written[:, 30:].all()
 
 
 # ---------------------------------------------------------------- bit-exact pins

@@ -145,7 +145,11 @@ def test_split_lengths(kkt, T):
     check_chain_equals_fused(kkt, inp, "f32", f"T={T}")
 
 
-SPLIT_VARLEN = {"tiny_and_empty": [1, 2, 3, 0, 64, 65, 0, 130, 5], "many_short": [1, 3] * 70}
+SPLIT_VARLEN = {
+    "tiny_and_empty": [1, 2, 3, 0, 64, 65, 0, 130, 5],
+    "many_short": [1, 3] * 70,
+    "two_levels_1000": [0 if i % 6 == 0 else 1 + (i * 37) % 90 for i in range(1000)],
+}
 
 
 @pytest.mark.parametrize("case", list(SPLIT_VARLEN))
