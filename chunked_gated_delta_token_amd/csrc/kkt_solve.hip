@@ -9,8 +9,9 @@
 //
 // One wave64 owns one (chunk, head) tile from load to store; nothing goes
 // back to HBM between the steps.
-//   a1  tile -> (b, t0, L, h); for packed sequences a 64-ary search over
-//       cu_seqlens (no host sync, no index tensor).  Every tensor of the
+//   a1  tile -> (b, t0, L, h); for packed sequences a scan of (or, beyond
+//       64 sequences, a 64-ary search over) cu_seqlens (no host sync, no
+//       index tensor).  Every tensor of the
 //       tile is then addressed through a buffer resource whose base is the
 //       tile's first row and whose size ends after row L-1: loads of rows
 //       >= L return 0 and stores to them are dropped by the hardware range
@@ -60,7 +61,7 @@
 
 #include "kkt_solve.h"
 
-#define KKT_VERSION_NUMBER 501  // 0.5.1
+#define KKT_VERSION_NUMBER 502  // 0.5.2
 
 namespace {
 
@@ -219,21 +220,53 @@ struct Tile {
     int len;       // valid rows L in [1, 64]; 0: no tile
 };
 
-// Packed sequences.  Chunk slots are numbered so that a slot can be found
-// from the offsets alone: sequence s (offsets clamped into [0, T]) owns the
-// slots [S(s), S(s) + ceil(len_s / CH)) with S(s) = floor(bos_s / CH) + s.
-// S is strictly increasing, no two ranges overlap and every slot is below
-// T / CH + num_seqs, the grid's bound; slots in no range are empty.  Slot w
-// belongs to the last sequence with S(s) <= w, found by a 64-ary search: each
-// level probes 64 evenly spaced sequences, one per lane, and keeps the span
-// after the last probe that is still <= w, so the search takes
-// ceil(log64(num_seqs)) dependent rounds of loads.
+// Packed sequences: grid slot w -> (first row, valid rows).  The grid has
+// T / CH + num_seqs slots, an upper bound on the chunk count.
+//   Up to 64 sequences: slots are the chunks numbered sequence by sequence;
+//   one wave-wide inclusive scan of the per-sequence chunk counts finds the
+//   sequence.  Slots beyond the last chunk are empty.
+//   More sequences: slots are numbered so that a slot can be found from the
+//   offsets alone: sequence s owns [S(s), S(s) + ceil(len_s / CH)) with
+//   S(s) = floor(bos_s / CH) + s.  S is strictly increasing, the ranges do
+//   not overlap and end below T / CH + num_seqs; slots in no range are empty.
+//   Slot w belongs to the last sequence with S(s) <= w, found by a 64-ary
+//   search (each level probes 64 evenly spaced sequences, one per lane), so
+//   the search takes ceil(log64(num_seqs)) dependent rounds of loads instead
+//   of a scan over every sequence before the chunk.
+// Offsets are clamped into [0, T] (they are int32, so every clamped offset
+// fits in 32 bits).
 template <int CH>
 __device__ Tile varlen_tile(const int32_t* __restrict__ cu, int32_t num_seqs, int64_t T, int32_t w, int lane)
 {
-    // offsets are int32, so every clamped offset fits in 32 bits
     const int32_t t_max = T < INT32_MAX ? (int32_t)T : INT32_MAX;
     Tile t{0, 0};
+    auto clamped = [&](int32_t s, int32_t& bos, int32_t& eos) {
+        const int32_t a = cu[s], e = cu[s + 1];
+        bos = a < 0 ? 0 : (a > t_max ? t_max : a);
+        eos = e < bos ? bos : (e > t_max ? t_max : e);
+    };
+    if (num_seqs <= kWave) {
+        int32_t bos = 0, eos = 0;
+        if (lane < num_seqs) clamped(lane, bos, eos);
+        const int32_t n = (eos - bos + CH - 1) / CH;
+        int32_t incl = n;
+#pragma unroll
+        for (int d = 1; d < kWave; d <<= 1) {
+            const int32_t up = __shfl_up(incl, d, kWave);
+            if (lane >= d) incl += up;
+        }
+        const uint64_t mask = __ballot(lane < num_seqs && incl > w);
+        if (mask == 0) return t;
+        const int src = __builtin_ctzll(mask);
+        const int32_t sel_excl = __shfl(incl - n, src, kWave);
+        const int32_t sel_bos = __shfl(bos, src, kWave);
+        const int32_t sel_eos = __shfl(eos, src, kWave);
+        const int64_t t0 = sel_bos + (int64_t)(w - sel_excl) * CH;
+        const int64_t rem = sel_eos - t0;
+        t.row0 = t0;
+        t.len = (int)(rem < CH ? rem : CH);
+        return t;
+    }
     int32_t lo = 0, span = num_seqs;  // the sequence sought lies in [lo, lo + span)
     for (;;) {
         const int32_t step = (span + kWave - 1) / kWave;
@@ -241,9 +274,7 @@ __device__ Tile varlen_tile(const int32_t* __restrict__ cu, int32_t num_seqs, in
         int32_t bos = 0, eos = 0;
         bool le = false;
         if (lane * step < span) {
-            const int32_t a = cu[s], e = cu[s + 1];
-            bos = a < 0 ? 0 : (a > t_max ? t_max : a);
-            eos = e < bos ? bos : (e > t_max ? t_max : e);
+            clamped(s, bos, eos);
             le = (int64_t)(bos / CH) + s <= w;
         }
         const uint64_t mask = __ballot(le);
@@ -308,37 +339,34 @@ __device__ __forceinline__ Tile chunk_tile(const KernelArgs& args, uint32_t chun
     return tile;
 }
 
-// LDS of one 128-token tile (one workgroup): the four waves' own areas, then
-// the key tile staged once for all waves, whose space the halves of the chunk
-// reuse afterwards to exchange their blocks.
+// LDS of one 128-token tile (one workgroup), in two overlapping layouts.
+// Until the workgroup barrier that ends the first phase: the waves' own
+// areas and the first half's key fragments as wave 0 loaded them (for waves
+// 2 and 3).  After it: the blocks the waves exchange (X11, X22, A21, then P
+// and X21).  39,424 bytes: four workgroups fit in a CU's 160 KB.
 struct Chunk128Lds {
-    WaveLds half[2];                       // waves 0 and 1 (the 64-row pipelines)
-    GateLds cross_gate[2];                 // waves 2 and 3 (the A21 epilogue)
     union {
-        u32x4 kimg[8][4][kWave];           // key fragments (16-row block, k-step, lane), up to 4 k-steps
         struct {
-            float x22t[10][16][kBlockLd];  // X22 blocks, transposed: x22t[b][col][row]
+            WaveLds half[2];                   // waves 0 and 1 (the 64-row pipelines)
+            GateLds cross_gate[2];             // waves 2 and 3 (the A21 epilogue)
+            u32x4 kimg[4][4][kWave];           // rows 0..63: key fragments (16-row block, k-step, lane)
+        };
+        struct {
+            float x22t[10][16][kBlockLd];      // X22 blocks, transposed: x22t[b][col][row]
             union {
                 struct {
-                    f32x4 x11[10][kWave];  // X11 blocks, result-layout register images
-                    f32x4 a21[16][kWave];  // A21 blocks (left-operand layout), then P blocks (result layout)
+                    f32x4 x11[10][kWave];      // X11 blocks, result-layout register images
+                    f32x4 a21[16][kWave];      // A21 blocks (left-operand layout), then P blocks (result layout)
                 } cross;
-                float x21[kChunk][kStageLd];  // X21 rows staged for the store
+                float x21[kChunk][kStageLd];   // X21 rows staged for the store
             };
         };
     };
 };
+static_assert(sizeof(Chunk128Lds) * 4 <= 160 * 1024, "four 128-token workgroups per CU");
 
 // Index of lower block (i, j), j <= i, of a 4x4 block-triangular matrix.
 __host__ __device__ constexpr int tri(int i, int j) { return i * (i + 1) / 2 + j; }
-
-// Key fragments, gate and beta of 64 rows, loaded by the caller (the
-// 128-token kernel stages the key tile in LDS once for all its waves).
-template <int KSTEPS>
-struct RowsIn {
-    u32x4 frag[4][KSTEPS];
-    float gv, bv;
-};
 
 // ---------------------------------------------------------------- the kernel
 // Steps a2-a8 for 64 rows of one chunk of CH tokens, on one wave.  CH = 64:
@@ -350,10 +378,14 @@ struct RowsIn {
 // rows of the chunk.
 // GATE_SUM: g holds per-token log-decays that the tile sums itself (a
 // separate instantiation, so the plain fused kernel carries none of it).
-template <Mode MODE, Elt IN, Elt OUT, int K, bool GATE_SUM, int CH, bool STAGED = false>
+// CH = 128: before it leaves X11 / X22 in ex the wave waits at the workgroup
+// barrier that ends the first phase (the exchange area overlaps the
+// first-phase areas).  SHARE: after its Gram, wave 0 also writes its key
+// fragments to ex->kimg for the A21 waves, and both waves take part in the
+// barrier that makes them visible.
+template <Mode MODE, Elt IN, Elt OUT, int K, bool GATE_SUM, int CH, bool SHARE = false>
 __device__ __forceinline__ void chunk_rows(const KernelArgs& args, WaveLds& lds, int lane, int64_t tok, int L,
-                                           int half, Chunk128Lds* ex,
-                                           const RowsIn<K / (4 * (16 / EltInfo<IN>::bytes))>* in = nullptr)
+                                           int half, Chunk128Lds* ex)
 {
     constexpr int kInBytes = EltInfo<IN>::bytes;
     constexpr int kOutBytes = EltInfo<OUT>::bytes;
@@ -361,6 +393,7 @@ __device__ __forceinline__ void chunk_rows(const KernelArgs& args, WaveLds& lds,
     constexpr int kSteps = K / (4 * kElemsPer16B);          // 16-byte fragments per row per lane
     static_assert(K % (4 * kElemsPer16B) == 0, "K must fill whole fragments");
     static_assert(CH == 64 || (CH == 128 && MODE == Mode::Fused && !GATE_SUM), "128-token chunks: fused op only");
+    static_assert(!SHARE || (CH == 128 && kSteps <= 4), "shared key tile: 128-token kernel, at most 4 k-steps");
     const int q = lane / 16;   // lane group (k-slot group of an MFMA operand)
     const int m = lane % 16;   // row inside a 16-row block (A operand) / column (D layout)
     const int H = args.H;
@@ -398,50 +431,40 @@ __device__ __forceinline__ void chunk_rows(const KernelArgs& args, WaveLds& lds,
         const bool valid = lane < L - (int)row_base;
         float gv = 0.0f, bv = 1.0f;
         u32x4 frag[4][kSteps];
-        if constexpr (STAGED) {
-            gv = in->gv;
-            bv = in->bv;
-#pragma unroll
-            for (int bi = 0; bi < 4; ++bi) {
-#pragma unroll
-                for (int s = 0; s < kSteps; ++s) frag[bi][s] = in->frag[bi][s];
-            }
-        } else {
-            const __amdgpu_buffer_rsrc_t k_rsrc = make_rsrc(
-                static_cast<const char*>(args.k) + tok * (int64_t)(K * kInBytes),
-                (uint32_t)(L - 1) * args.k_row_bytes + K * kInBytes);
+        const __amdgpu_buffer_rsrc_t k_rsrc = make_rsrc(
+            static_cast<const char*>(args.k) + tok * (int64_t)(K * kInBytes),
+            (uint32_t)(L - 1) * args.k_row_bytes + K * kInBytes);
 
-            // ---- a3: g and beta, one row per lane (rows >= L read as 0).  Issued
-            // before the K tile: loads complete in order, so waiting for these two
-            // does not wait for the whole tile.
-            {
-                const uint32_t voff = (row_base + (uint32_t)lane) * (uint32_t)H * 4u;
-                const uint32_t span = (uint32_t)(L - 1) * (uint32_t)H * 4u + 4u;
-                // the loads return raw 32-bit words: reinterpret, do not convert
-                if (has_g) {
-                    gv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(args.g + tok, span), voff, 0, 0));
-                }
-                if (args.beta != nullptr) {
-                    bv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(args.beta + tok, span), voff, 0, 0));
-                }
+        // ---- a3: g and beta, one row per lane (rows >= L read as 0).  Issued
+        // before the K tile: loads complete in order, so waiting for these two
+        // does not wait for the whole tile.
+        {
+            const uint32_t voff = (row_base + (uint32_t)lane) * (uint32_t)H * 4u;
+            const uint32_t span = (uint32_t)(L - 1) * (uint32_t)H * 4u + 4u;
+            // the loads return raw 32-bit words: reinterpret, do not convert
+            if (has_g) {
+                gv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(args.g + tok, span), voff, 0, 0));
             }
+            if (args.beta != nullptr) {
+                bv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(args.beta + tok, span), voff, 0, 0));
+            }
+        }
 
-            // ---- a2: K fragments, all loads issued up front (rows >= L read as 0).
-            // Each load instruction reads 64 bytes of 16 rows; the next k-step reads
-            // the other half of the same 128-byte lines, so these loads are not
-            // marked streaming (the lines must survive in L2 until then).  The
-            // scheduling barrier keeps every load ahead of the first MFMA, so the
-            // whole tile is in flight at once.
+        // ---- a2: K fragments, all loads issued up front (rows >= L read as 0).
+        // Each load instruction reads 64 bytes of 16 rows; the next k-step reads
+        // the other half of the same 128-byte lines, so these loads are not
+        // marked streaming (the lines must survive in L2 until then).  The
+        // scheduling barrier keeps every load ahead of the first MFMA, so the
+        // whole tile is in flight at once.
 #pragma unroll
-            for (int bi = 0; bi < 4; ++bi) {
-                const uint32_t voff = (row_base + (uint32_t)(16 * bi + m)) * args.k_row_bytes + q * 16;
+        for (int bi = 0; bi < 4; ++bi) {
+            const uint32_t voff = (row_base + (uint32_t)(16 * bi + m)) * args.k_row_bytes + q * 16;
 #pragma unroll
-                for (int s = 0; s < kSteps; ++s) {
-                    frag[bi][s] = __builtin_amdgcn_raw_buffer_load_b128(k_rsrc, voff + s * 64, 0, 0);
-                }
+            for (int s = 0; s < kSteps; ++s) {
+                frag[bi][s] = __builtin_amdgcn_raw_buffer_load_b128(k_rsrc, voff + s * 64, 0, 0);
             }
-            __builtin_amdgcn_sched_barrier(0);
-        }  // !STAGED
+        }
+        __builtin_amdgcn_sched_barrier(0);
 
         // ---- gate from per-token log-decays (kkt_solve_gate_cumsum): the
         // gate is their running sum from the chunk's first row, an inclusive
@@ -473,6 +496,17 @@ __device__ __forceinline__ void chunk_rows(const KernelArgs& args, WaveLds& lds,
         for (int i = 0; i < 4; ++i) {
 #pragma unroll
             for (int j = 0; j <= i; ++j) S[i][j] = gram(i, j);
+        }
+        if constexpr (SHARE) {
+            if (half == 0) {
+                // rows >= L hold the zeros their out-of-range loads returned
+#pragma unroll
+                for (int bi = 0; bi < 4; ++bi) {
+#pragma unroll
+                    for (int s = 0; s < kSteps; ++s) ex->kimg[bi][s][lane] = frag[bi][s];
+                }
+            }
+            __syncthreads();  // the first half's key fragments are in LDS
         }
 
         // ---- a5: epilogue
@@ -690,6 +724,7 @@ __device__ __forceinline__ void chunk_rows(const KernelArgs& args, WaveLds& lds,
     store_block_row(3, x30, x31, x32, xd[3]);
 
     if constexpr (CH == 128) {
+        __syncthreads();  // end of the first phase: the exchange area overlaps its areas
         // hand the block to the workgroup: X11 as result-layout register
         // images, X22 transposed (its rows are read as left operands)
         const f32x4 blocks[10] = {xd[0], x10, xd[1], x20, x21, xd[2], x30, x31, x32, xd[3]};
@@ -753,9 +788,9 @@ __device__ __forceinline__ CrossIn cross_gate_beta(const KernelArgs& args, int l
 
 // acc[bi][bj]: S21 block (2 w2 + bi, bj) in left-operand layout, i.e. lane
 // (q, m) holds S21[m][4q + r]: second-half row 32 w2 + 16 bi + m, first-half
-// column 16 bj + 4q + r.
-__device__ __forceinline__ void cross_epilogue(const KernelArgs& args, Chunk128Lds& ex, GateLds& lds, int lane,
-                                               int w2, const CrossIn& in, const f32x4 (&acc)[2][4])
+// column 16 bj + 4q + r.  Turned into the A21 blocks in place.
+__device__ __forceinline__ void cross_scale(const KernelArgs& args, GateLds& lds, int lane, int w2, const CrossIn& in,
+                                            f32x4 (&acc)[2][4])
 {
     const int q = lane / 16;
     const int m = lane % 16;
@@ -781,8 +816,17 @@ __device__ __forceinline__ void cross_epilogue(const KernelArgs& args, Chunk128L
             } else {
                 a = br * acc[bi][bj];
             }
-            ex.cross.a21[4 * (2 * w2 + bi) + bj][lane] = a;
+            acc[bi][bj] = a;
         }
+    }
+}
+
+__device__ __forceinline__ void cross_store(Chunk128Lds& ex, int lane, int w2, const f32x4 (&a21)[2][4])
+{
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi) {
+#pragma unroll
+        for (int bj = 0; bj < 4; ++bj) ex.cross.a21[4 * (2 * w2 + bi) + bj][lane] = a21[bi][bj];
     }
 }
 
@@ -802,11 +846,12 @@ __device__ __forceinline__ void cross_gram(const u32x4 (&fr)[2][P], const u32x4 
     }
 }
 
-// A21 with the keys read from global memory in passes of at most 4
-// fragments per row (head dimensions whose key tile is not staged in LDS).
+// A21 blocks (the rows of w2; scaled, in registers) with the keys read from
+// global memory in passes of at most 4 fragments per row (head dimensions
+// whose key fragments do not fit the LDS image).
 template <Elt IN, int K>
-__device__ __forceinline__ void cross_block_rows(const KernelArgs& args, Chunk128Lds& ex, GateLds& lds, int lane,
-                                                 int64_t tok, int L, int w2)
+__device__ __forceinline__ void cross_block_rows(const KernelArgs& args, GateLds& lds, int lane, int64_t tok, int L,
+                                                 int w2, f32x4 (&acc)[2][4])
 {
     constexpr int kInBytes = EltInfo<IN>::bytes;
     constexpr int kElemsPer16B = 16 / kInBytes;
@@ -819,7 +864,6 @@ __device__ __forceinline__ void cross_block_rows(const KernelArgs& args, Chunk12
         static_cast<const char*>(args.k) + tok * (int64_t)(K * kInBytes),
         (uint32_t)(L - 1) * args.k_row_bytes + K * kInBytes);
     const CrossIn in = cross_gate_beta(args, lane, tok, L);
-    f32x4 acc[2][4];
 #pragma unroll
     for (int bi = 0; bi < 2; ++bi) {
 #pragma unroll
@@ -844,7 +888,7 @@ __device__ __forceinline__ void cross_block_rows(const KernelArgs& args, Chunk12
         cross_gram<IN, kPass>(fr, fc, acc);
         __builtin_amdgcn_sched_barrier(0);
     }
-    cross_epilogue(args, ex, lds, lane, w2, in, acc);
+    cross_scale(args, lds, lane, w2, in, acc);
 }
 
 // One kernel per entry point, so that profiles name the operation.
@@ -889,8 +933,25 @@ void kkt_solve_tril_kernel(const KernelArgs args)
 //   waves 2, 3: A21, two block rows each;
 //   then P = A21 X11 (wave i: block row i), X21 = -X22 P (wave j: block
 //   column j), X21 staged in LDS and stored as 256/128-byte row pieces.
-template <Elt IN, Elt OUT, int K, bool STAGE_K>
+// How the key tile reaches the waves (STAGE):
+//   kKeysShared: waves 0 and 1 load their halves into registers as the
+//                64-token pipeline does; after its Gram, wave 0 copies the
+//                first half's fragments to LDS, where waves 2 and 3 read them
+//                (their own 32 second-half rows they read after that barrier,
+//                from L2).  Waves 0 and 1 wait for no other wave before their
+//                Gram, and waves 2 and 3 are idle until then anyway.  The LDS
+//                image holds at most 4 k-steps (16-bit keys with K <= 128,
+//                fp32 keys with K = 64).
+//   kKeysGlobal: (larger K) every wave loads the key rows it needs; waves 2
+//                and 3 read the first half and their own rows again, in
+//                passes of 4 k-steps.
+enum KeyStage { kKeysGlobal = 0, kKeysShared = 1 };
+
+template <Elt IN, Elt OUT, int K, int STAGE>
 __global__ __launch_bounds__(kWave * kWavesPerGroup)
+// (shared keys: at most 128 VGPRs, so that registers, like the 39 KB of LDS,
+// leave room for four workgroups per CU)
+__attribute__((amdgpu_waves_per_eu(STAGE == kKeysShared ? 4 : 1)))
 void kkt_solve128_kernel(const KernelArgs args)
 {
     constexpr int kOutBytes = EltInfo<OUT>::bytes;
@@ -910,88 +971,49 @@ void kkt_solve128_kernel(const KernelArgs args)
 
     constexpr int kInBytes = EltInfo<IN>::bytes;
     constexpr int kSteps = K / (4 * (16 / kInBytes));
-    static_assert(!STAGE_K || kSteps <= 4, "the staged key tile holds at most 4 k-steps");
-    if constexpr (STAGE_K) {
-        // The key tile through LDS: each 16-row block is loaded once (wave w:
-        // blocks 2w, 2w+1), straight into LDS as lane-ordered images of its
-        // MFMA fragments, and every wave then reads the fragments it needs
-        // (waves 0, 1: their half; waves 2, 3: their A21 rows and the first
-        // half).  Gate and beta loads go first.  This costs two workgroup
-        // barriers before any compute; without staging, waves 2 and 3 read
-        // the keys they need from global memory themselves (2.5 times the
-        // tile through L2, no barrier).
-        const __amdgpu_buffer_rsrc_t k_rsrc = make_rsrc(
-            static_cast<const char*>(args.k) + tok * (int64_t)(K * kInBytes),
-            (uint32_t)(L - 1) * args.k_row_bytes + K * kInBytes);
-        RowsIn<kSteps> rin;
-        CrossIn cin;
-        if (wave < 2) {
-            rin.gv = 0.0f;
-            rin.bv = 1.0f;
-            const uint32_t voff = (64u * (uint32_t)wave + (uint32_t)lane) * (uint32_t)H * 4u;
-            const uint32_t span = (uint32_t)(L - 1) * (uint32_t)H * 4u + 4u;
-            if (args.g != nullptr) {
-                rin.gv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(args.g + tok, span), voff, 0, 0));
-            }
-            if (args.beta != nullptr) {
-                rin.bv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(args.beta + tok, span), voff, 0, 0));
-            }
-        } else {
-            cin = cross_gate_beta(args, lane, tok, L);
-        }
-#pragma unroll
-        for (int b2 = 0; b2 < 2; ++b2) {
-            const int bi = 2 * wave + b2;
-            const uint32_t voff = (uint32_t)(16 * bi + m) * args.k_row_bytes + q * 16;
-#pragma unroll
-            for (int s = 0; s < kSteps; ++s) {
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    k_rsrc, (__attribute__((address_space(3))) void*)&ex.kimg[bi][s][0], 16, voff + s * 64, 0, 0, 0);
-            }
-        }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's part of the tile is in LDS
-        __syncthreads();
-        // Lane (q, m) of block b holds row 16 b + m.  Rows >= L are set to
-        // zero here, whatever the out-of-range lanes of the direct loads left
-        // in LDS, so they contribute exact zeros as in the 64-token kernel.
-        const u32x4 zero_frag = {0u, 0u, 0u, 0u};
-        auto key_frag = [&](int b, int s) -> u32x4 { return (16 * b + m < L) ? ex.kimg[b][s][lane] : zero_frag; };
-        u32x4 fr[2][kSteps], fc[4][kSteps];
-        if (wave < 2) {
-#pragma unroll
-            for (int bi = 0; bi < 4; ++bi) {
-#pragma unroll
-                for (int s = 0; s < kSteps; ++s) rin.frag[bi][s] = key_frag(4 * wave + bi, s);
-            }
-        } else {
-#pragma unroll
-            for (int s = 0; s < kSteps; ++s) {
-#pragma unroll
-                for (int bi = 0; bi < 2; ++bi) fr[bi][s] = key_frag(4 + 2 * (wave - 2) + bi, s);
-#pragma unroll
-                for (int bj = 0; bj < 4; ++bj) fc[bj][s] = key_frag(bj, s);
-            }
-        }
-        __syncthreads();  // every read of the key tile is done: its space is reused below
-        if (wave < 2) {
-            chunk_rows<Mode::Fused, IN, OUT, K, false, 2 * kChunk, true>(args, ex.half[wave], lane, tok, L, wave, &ex,
-                                                                           &rin);
-        } else {
-            f32x4 acc[2][4];
+    static_assert(STAGE == kKeysGlobal || kSteps <= 4, "the LDS key image holds at most 4 k-steps");
+    if (wave < 2) {
+        chunk_rows<Mode::Fused, IN, OUT, K, false, 2 * kChunk, STAGE == kKeysShared>(args, ex.half[wave], lane, tok, L,
+                                                                                     wave, &ex);
+    } else {
+        const int w2 = wave - 2;
+        f32x4 acc[2][4];
+        if constexpr (STAGE == kKeysShared) {
+            // the first half's fragments from wave 0 via LDS; the own rows
+            // (64 + 32 w2 ..) from memory, but only after the barrier: wave 1
+            // has fetched them by then (L2 hits), and issued at the start
+            // they would queue in front of the loads of waves 0 and 1
+            const __amdgpu_buffer_rsrc_t k_rsrc = make_rsrc(
+                static_cast<const char*>(args.k) + tok * (int64_t)(K * kInBytes),
+                (uint32_t)(L - 1) * args.k_row_bytes + K * kInBytes);
+            const CrossIn cin = cross_gate_beta(args, lane, tok, L);
 #pragma unroll
             for (int bi = 0; bi < 2; ++bi) {
 #pragma unroll
                 for (int bj = 0; bj < 4; ++bj) acc[bi][bj] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
             }
-            cross_gram<IN, kSteps>(fr, fc, acc);
-            cross_epilogue(args, ex, ex.cross_gate[wave - 2], lane, wave - 2, cin, acc);
-        }
-    } else {
-        if (wave < 2) {
-            chunk_rows<Mode::Fused, IN, OUT, K, false, 2 * kChunk>(args, ex.half[wave], lane, tok, L, wave, &ex);
+            __syncthreads();  // the first half's key fragments are in LDS
+            u32x4 fr[2][kSteps];
+#pragma unroll
+            for (int bi = 0; bi < 2; ++bi) {
+                const uint32_t voff = (uint32_t)(64 + 32 * w2 + 16 * bi + m) * args.k_row_bytes + q * 16;
+#pragma unroll
+                for (int s = 0; s < kSteps; ++s) fr[bi][s] = __builtin_amdgcn_raw_buffer_load_b128(k_rsrc, voff + s * 64, 0, 0);
+            }
+#pragma unroll
+            for (int s = 0; s < kSteps; ++s) {
+                u32x4 fc[4][1];
+#pragma unroll
+                for (int bj = 0; bj < 4; ++bj) fc[bj][0] = ex.kimg[bj][s][lane];
+                u32x4 fs[2][1] = {{fr[0][s]}, {fr[1][s]}};
+                cross_gram<IN, 1>(fs, fc, acc);
+            }
+            cross_scale(args, ex.cross_gate[w2], lane, w2, cin, acc);
         } else {
-            cross_block_rows<IN, K>(args, ex, ex.cross_gate[wave - 2], lane, tok, L, wave - 2);
+            cross_block_rows<IN, K>(args, ex.cross_gate[w2], lane, tok, L, w2, acc);
         }
+        __syncthreads();  // end of the first phase: the exchange area overlaps its areas
+        cross_store(ex, lane, w2, acc);
     }
     __syncthreads();
 
@@ -1143,21 +1165,11 @@ hipError_t launch_fused(int64_t K, const KernelArgs& a, hipStream_t stream)
     }
 }
 
-// 128-token chunks: grids of at most this many workgroups stage the key tile
-// in LDS (fewer redundant loads; measured 13.6 vs 14.5 us at 512 tiles), larger
-// ones let every wave load its own keys (no barrier before compute; 160 vs
-// 171 us at 8192 tiles).  Staging needs at most 4 k-steps (16-bit K <= 128,
-// fp32 K = 64).
-constexpr int64_t kStageMaxGroups128 = 1024;
-
 template <Elt IN, Elt OUT, int K>
 hipError_t launch_fused128_k(const KernelArgs& a, hipStream_t stream)
 {
     constexpr int kSteps = K / (4 * (16 / EltInfo<IN>::bytes));
-    if constexpr (kSteps <= 4) {
-        if (a.n_groups <= kStageMaxGroups128) return launch(kkt_solve128_kernel<IN, OUT, K, true>, a, stream);
-    }
-    return launch(kkt_solve128_kernel<IN, OUT, K, false>, a, stream);
+    return launch(kkt_solve128_kernel<IN, OUT, K, (kSteps <= 4) ? kKeysShared : kKeysGlobal>, a, stream);
 }
 
 template <Elt IN, Elt OUT>

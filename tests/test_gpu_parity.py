@@ -125,9 +125,10 @@ VARLEN_CASES = {
     "single": [777],
     "all_empty_but_one": [0, 0, 40, 0],
     "many_short": [1, 3] * 70,  # 140 sequences
-    # the chunk search narrows 64-fold per level: one level up to 64
-    # sequences, two up to 4096, three beyond; cases on both sides of each
-    # step, with empty sequences among them
+    # the chunk lookup: one scan up to 64 sequences, beyond that a search
+    # that narrows 64-fold per level (two levels up to 4096 sequences, three
+    # beyond); cases on both sides of each step, with empty sequences among
+    # them
     "one_level_64": _lengths(510, 64, 1, 70),
     "two_levels_65": _lengths(511, 65, 0, 70, empty_every=5),
     "two_levels_3000": _lengths(512, 3000, 0, 40, empty_every=7),
