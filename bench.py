@@ -145,8 +145,36 @@ def cpu_baseline(inp, nbytes: int, budget_s: float, op: str = "fused"):
             break
     what = {"fused": "the fused op", "scaled_dot": "A alone", "solve_tril": "the solve of a given A",
             "chain": "A, then its solve", "gate_cumsum": "gate sum, then the fused op"}[op]
-    return {"value": nbytes * reps / el / 1e9, "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"the whole workload ({what}), {reps} calls in {el:.1f} s (fp64, OpenMP over chunk-head tiles)"}
+    threads = oracle.num_threads()
+    out = {"value": nbytes * reps / el / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+           "sample": f"the whole workload ({what}), {reps} calls in {el:.1f} s (fp64, OpenMP over chunk-head tiles)",
+           "cpu": cpu_model()}
+    if op == "fused":
+        # the same on one thread, over a shorter sample
+        oracle.set_num_threads(1)
+        try:
+            reps1, t1 = 0, time.perf_counter()
+            while True:
+                oracle.kkt_solve_ref(k64, g64, b64, cu)
+                reps1 += 1
+                el1 = time.perf_counter() - t1
+                if el1 >= budget_s / 3:
+                    break
+        finally:
+            oracle.set_num_threads(threads)
+        out["single_thread_value"] = nbytes * reps1 / el1 / 1e9
+        out["single_thread_sample"] = f"{reps1} calls in {el1:.1f} s"
+    return out
+
+
+def cpu_model() -> str:
+    """The host CPU's model name and logical CPU count (Linux)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            names = [l.split(":", 1)[1].strip() for l in f if l.startswith("model name")]
+        return f"{names[0]} ({len(names)} logical CPUs)" if names else "unknown"
+    except OSError:
+        return "unknown"
 
 
 def copy_calibration(nbytes: int, steps: int):
@@ -351,6 +379,10 @@ def summarize_trace(directory: str, op: str, workload: str, run_log: str = None,
         import statistics
         last = durations[-200:]
         lines.append(f"median_ns: {statistics.median(durations):.1f}")
+        q = statistics.quantiles(last, n=10)
+        lines.append(f"timed_graph_replay_p10_ns: {q[0]:.1f}")
+        lines.append(f"timed_graph_replay_median_ns: {statistics.median(last):.1f}")
+        lines.append(f"timed_graph_replay_p90_ns: {q[-1]:.1f}")
         lines.append(f"timed_graph_replay_average_ns: {statistics.mean(last):.1f}  # the last 200 dispatches")
     if ev_prof is not None:
         lines.append(f"bench_event_us_per_step_under_profiler: {ev_prof:.3f}")

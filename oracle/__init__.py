@@ -70,6 +70,8 @@ def _load():
     lib.kkt_oracle_chunk_cumsum.restype = ctypes.c_int
     lib.kkt_oracle_num_threads.argtypes = []
     lib.kkt_oracle_num_threads.restype = ctypes.c_int
+    lib.kkt_oracle_set_num_threads.argtypes = [ctypes.c_int]
+    lib.kkt_oracle_set_num_threads.restype = None
     _lib = lib
     return lib
 
@@ -77,6 +79,11 @@ def _load():
 def num_threads() -> int:
     """Threads the oracle's parallel loop uses (OpenMP default)."""
     return int(_load().kkt_oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads for the oracle's later parallel loops (timing only)."""
+    _load().kkt_oracle_set_num_threads(int(n))
 
 
 def _ptr(a, ctype):

@@ -194,6 +194,16 @@ int kkt_oracle_num_threads(void)
 #endif
 }
 
+/* Sets the number of threads of later parallel loops (no effect without OpenMP). */
+void kkt_oracle_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* The chunks of a call, in order: batch row or sequence, then position. */
 typedef struct {
     int64_t n;
