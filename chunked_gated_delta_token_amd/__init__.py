@@ -10,6 +10,7 @@ forward pass, for AMD Instinct MI355X (gfx950).
 The computation is the HIP library ``libkkt_solve.so`` (C ABI in
 ``include/kkt_solve.h``); this package only marshals arguments.
 """
-from .kkt import (KKTError, chunk_gated_delta_rule_fwd_kkt_solve, chunk_scaled_dot_kkt_fwd,  # noqa: F401
+from .kkt import (KKTError, KKTInvalidArgument, KKTUnsupported,  # noqa: F401
+                  chunk_gated_delta_rule_fwd_kkt_solve, chunk_scaled_dot_kkt_fwd,
                   kkt_scaled_dot, kkt_solve, kkt_solve_gate_cumsum, kkt_solve_tril, last_error, load_library,
                   solve_tril, version)

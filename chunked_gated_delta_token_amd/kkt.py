@@ -50,6 +50,21 @@ class KKTError(RuntimeError):
         self.status = status
 
 
+class KKTInvalidArgument(KKTError, ValueError):
+    """KKT_ERR_INVALID_ARGUMENT: a pointer, size or dtype the call cannot take."""
+
+
+class KKTUnsupported(KKTError, NotImplementedError):
+    """KKT_ERR_UNSUPPORTED: a valid request this build does not serve (chunk
+    size, head dimension, a device other than gfx950)."""
+
+
+def _error(status: int) -> KKTError:
+    """The exception for a non-OK status, with the library's message."""
+    cls = {KKT_ERR_INVALID_ARGUMENT: KKTInvalidArgument, KKT_ERR_UNSUPPORTED: KKTUnsupported}.get(status, KKTError)
+    return cls(status, last_error())
+
+
 def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     """Load ``libkkt_solve.so``; raises if it has not been built."""
     global _lib
@@ -158,7 +173,7 @@ def kkt_solve(k: torch.Tensor, g: Optional[torch.Tensor] = None, beta: Optional[
         st = kkt_solve_raw(_ptr(k), _ptr(g), _ptr(beta), _ptr(cu_seqlens), num_seqs, B, T, H, K, chunk_size,
                            _TORCH_TO_KKT[k.dtype], _TORCH_TO_KKT[odt], _ptr(out), _stream_ptr(stream, k.device))
     if st != KKT_OK:
-        raise KKTError(st, last_error())
+        raise _error(st)
     return out
 
 
@@ -189,7 +204,7 @@ def kkt_solve_gate_cumsum(k: torch.Tensor, g_decay: torch.Tensor, beta: Optional
                                                   B, T, H, K, chunk_size, _TORCH_TO_KKT[k.dtype], _TORCH_TO_KKT[odt],
                                                   _ptr(out), _ptr(g_out), _stream_ptr(stream, k.device))
     if st != KKT_OK:
-        raise KKTError(st, last_error())
+        raise _error(st)
     return (out, g_out) if g_out is not None else out
 
 
@@ -209,7 +224,7 @@ def kkt_scaled_dot(k: torch.Tensor, g: Optional[torch.Tensor] = None, beta: Opti
                                            chunk_size, _TORCH_TO_KKT[k.dtype], _ptr(out),
                                            _stream_ptr(stream, k.device))
     if st != KKT_OK:
-        raise KKTError(st, last_error())
+        raise _error(st)
     return out
 
 
@@ -235,7 +250,7 @@ def kkt_solve_tril(A: torch.Tensor, cu_seqlens: Optional[torch.Tensor] = None, c
         st = load_library().kkt_solve_tril(_ptr(A), _ptr(cu_seqlens), num_seqs, B, T, H, chunk_size,
                                            _TORCH_TO_KKT[odt], _ptr(out), _stream_ptr(stream, A.device))
     if st != KKT_OK:
-        raise KKTError(st, last_error())
+        raise _error(st)
     return out
 
 

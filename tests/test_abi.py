@@ -226,6 +226,20 @@ def test_python_binding_rejects_chunk_size():
         kkt.kkt_solve_tril(torch.zeros(1, 4, 1, 64))
 
 
+def test_python_exceptions_follow_the_status(lib):
+    """The binding raises ValueError for KKT_ERR_INVALID_ARGUMENT and
+    NotImplementedError for KKT_ERR_UNSUPPORTED (both also KKTError, with the
+    status and the library's message)."""
+    from chunked_gated_delta_token_amd import kkt
+    for over, cls, base in ((dict(B=0), kkt.KKTInvalidArgument, ValueError),
+                            (dict(K=100), kkt.KKTUnsupported, NotImplementedError)):
+        st = _call(lib, **over)
+        err = kkt._error(st)
+        assert type(err) is cls and isinstance(err, base) and isinstance(err, kkt.KKTError)
+        assert err.status == st and kkt.last_error() in str(err)
+    assert type(kkt._error(kkt.KKT_ERR_HIP)) is kkt.KKTError
+
+
 def test_header_compiles_as_c_and_links(tmp_path, lib):
     """A plain C program includes the header, links the library and makes a
     host-only call (argument rejection)."""
