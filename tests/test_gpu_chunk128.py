@@ -138,10 +138,27 @@ def test_chunk128_halves_equal_64_token_results(kkt):
         assert np.all(x128[:, t0:t0 + 64, :, 64:].view(np.uint32) == 0)
 
 
-def test_chunk128_repeatable(kkt):
-    inp = W.generate("T8192_H8_bf16_f32")
-    say("[case] chunk128 repeatable: T8192_H8")
-    t = to_device(inp)
-    a = run(kkt, inp, "f32", tensors=t)
-    b = run(kkt, inp, "f32", tensors=t)
-    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+@pytest.mark.parametrize("case", ["B2_T16384_H32 shared keys", "K256 keys from memory", "fp32 K64 packed"])
+def test_chunk128_repeatable(kkt, case):
+    """Repeated launches give the same bits: 20 calls on the large grid (four
+    workgroups per CU, both LDS layouts in use) and on the other key paths,
+    each compared on the device with the first."""
+    if case.startswith("B2"):
+        inp, out_dtype = W.generate("B2_T16384_H32_bf16_bf16"), "bf16"
+    elif case.startswith("K256"):
+        inp, out_dtype = W.generate("T8192_H8_bf16_f32", K=256, seed=3600), "f32"
+    else:
+        inp = W.generate("T256_H8_bf16_f32", lengths=[700, 0, 129, 1] * 30, H=6, K=64, in_dtype="f32", seed=3601)
+        out_dtype = "f32"
+    say(f"[case] chunk128 repeatable: {case}, 20 calls")
+    k, g, b, cu = to_device(inp)
+    B, T, H, _ = k.shape
+    first = torch.empty((B, T, H, CH), dtype=TORCH_DT[out_dtype], device=k.device)
+    out = torch.empty_like(first)
+    kkt.kkt_solve(k, g, b, cu, chunk_size=CH, output_dtype=TORCH_DT[out_dtype], out=first)
+    bits = torch.int32 if out_dtype == "f32" else torch.int16
+    for rep in range(20):
+        out.fill_(float("nan"))
+        kkt.kkt_solve(k, g, b, cu, chunk_size=CH, output_dtype=TORCH_DT[out_dtype], out=out)
+        assert torch.equal(out.view(bits), first.view(bits)), rep
+    torch.cuda.synchronize()
