@@ -21,8 +21,10 @@
 //       MFMA k-step.  S = K K^T uses the same fragments as both operands, so
 //       any fixed assignment of k indices to (lane group, slot) gives S.
 //   a3  g and beta: one row per lane.
-//   a4  Gram on MFMA (bf16/f16: 16x16x32, fp32: 16x16x4), fp32 accumulate,
-//       only the 10 lower 16x16 blocks.
+//   a4  Gram on MFMA, 16x16x32 bf16/f16, fp32 accumulate, only the 10 lower
+//       16x16 blocks.  fp32 keys are split into three bf16 parts (exact to
+//       2^-27) and six part products are summed (split_bf16x3, gram_bf16x3):
+//       fp32-level accuracy at 2.7 times fewer MFMA cycles than fp32 MFMA.
 //   a5  epilogue on the accumulators.  When every gate value of the chunk
 //       is within 25 of g_0, no pair differs by more than 50, the clamp
 //       cannot bind, and exp(g_i - g_j) factors into exp(g_i - g_0)
@@ -61,7 +63,7 @@
 
 #include "kkt_solve.h"
 
-#define KKT_VERSION_NUMBER 502  // 0.5.2
+#define KKT_VERSION_NUMBER 503  // 0.5.3
 
 namespace {
 
@@ -155,7 +157,8 @@ __device__ __forceinline__ f32x4 mm16(f32x4 a, f32x4 b, f32x4 c)
     return c;
 }
 
-// One k-step of the Gram for a 16-byte fragment pair.
+// One k-step of the Gram for a 16-byte fragment pair of 16-bit keys (fp32
+// keys go through split_bf16x3 / gram_bf16x3 below).
 template <Elt E> __device__ __forceinline__ f32x4 gram_step(u32x4 a, u32x4 b, f32x4 c);
 template <> __device__ __forceinline__ f32x4 gram_step<Elt::BF16>(u32x4 a, u32x4 b, f32x4 c)
 {
@@ -167,16 +170,53 @@ template <> __device__ __forceinline__ f32x4 gram_step<Elt::F16>(u32x4 a, u32x4 
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
-template <> __device__ __forceinline__ f32x4 gram_step<Elt::F32>(u32x4 a, u32x4 b, f32x4 c)
+
+
+// fp32 keys on the 16-bit matrix cores.  Eight fp32 values (two fragments)
+// become three bf16 parts, x = hi + mid + lo + e with |e| <= 2^-27 |x|: each
+// part is the round-to-nearest-even bf16 of what the parts before it leave,
+// and each remainder is exact in fp32.  (Eight values per lane make one k-slot
+// set of a 16x16x32 MFMA; the two Gram operands use the same set, so their
+// product sums the same k.)
+struct Bf16x3 {
+    bf16x8 hi, mid, lo;
+};
+
+__device__ __forceinline__ Bf16x3 split_bf16x3(u32x4 a0, u32x4 a1)
 {
-    // reinterpret whole vectors: a bit-cast of a single vector element would
-    // read the vector's first element instead
-    const f32x4 af = __builtin_bit_cast(f32x4, a);
-    const f32x4 bf = __builtin_bit_cast(f32x4, b);
-    c = __builtin_amdgcn_mfma_f32_16x16x4f32(af[0], bf[0], c, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_f32_16x16x4f32(af[1], bf[1], c, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_f32_16x16x4f32(af[2], bf[2], c, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_f32_16x16x4f32(af[3], bf[3], c, 0, 0, 0);
+    const f32x4 x0 = __builtin_bit_cast(f32x4, a0);
+    const f32x4 x1 = __builtin_bit_cast(f32x4, a1);
+    float x[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+    u32x4 part[3];
+#pragma unroll
+    for (int p = 0; p < 3; ++p) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            // one hardware convert packs two values; their fp32 values are
+            // the packed halves moved to the top of a word
+            const uint32_t w = pack2<Elt::BF16>(x[2 * e], x[2 * e + 1]);
+            part[p][e] = w;
+            if (p < 2) {
+                x[2 * e] -= __builtin_bit_cast(float, w << 16);
+                x[2 * e + 1] -= __builtin_bit_cast(float, w & 0xffff0000u);
+            }
+        }
+    }
+    return Bf16x3{__builtin_bit_cast(bf16x8, part[0]), __builtin_bit_cast(bf16x8, part[1]),
+                  __builtin_bit_cast(bf16x8, part[2])};
+}
+
+// c += A B^T over one 32-wide k-slot set of split fp32 rows: the six part
+// products down to order 2^-18 |a||b| (the three left out are below
+// 2^-26 |a||b|), smallest first.
+__device__ __forceinline__ f32x4 gram_bf16x3(const Bf16x3& a, const Bf16x3& b, f32x4 c)
+{
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.lo, b.hi, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.lo, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.mid, b.mid, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.mid, b.hi, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.mid, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.hi, c, 0, 0, 0);
     return c;
 }
 
@@ -485,17 +525,39 @@ __device__ __forceinline__ void chunk_rows(const KernelArgs& args, WaveLds& lds,
         }
 
         // ---- a4: Gram blocks.  Block (i, j): lane (q, n=m) holds rows 16i + 4q + r, column 16j + n.
-        auto gram = [&](int i, int j) -> f32x4 {
-            f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int s = 0; s < kSteps; ++s) acc = gram_step<IN>(frag[i][s], frag[j][s], acc);
-            return acc;
-        };
         f32x4 S[4][4];
+        if constexpr (IN == Elt::F32) {
+            // fp32 keys: k-outer, each pair of fragments split once for all
+            // ten blocks (the split parts of one pair are all that is live)
+            static_assert(kSteps % 2 == 0, "fragment pairs");
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < 4; ++i) {
 #pragma unroll
-            for (int j = 0; j <= i; ++j) S[i][j] = gram(i, j);
+                for (int j = 0; j <= i; ++j) S[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            }
+#pragma unroll
+            for (int s = 0; s < kSteps; s += 2) {
+                Bf16x3 sp[4];
+#pragma unroll
+                for (int bi = 0; bi < 4; ++bi) sp[bi] = split_bf16x3(frag[bi][s], frag[bi][s + 1]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+#pragma unroll
+                    for (int j = 0; j <= i; ++j) S[i][j] = gram_bf16x3(sp[i], sp[j], S[i][j]);
+                }
+            }
+        } else {
+            auto gram = [&](int i, int j) -> f32x4 {
+                f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int s = 0; s < kSteps; ++s) acc = gram_step<IN>(frag[i][s], frag[j][s], acc);
+                return acc;
+            };
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+#pragma unroll
+                for (int j = 0; j <= i; ++j) S[i][j] = gram(i, j);
+            }
         }
         if constexpr (SHARE) {
             if (half == 0) {
@@ -836,12 +898,29 @@ __device__ __forceinline__ void cross_store(Chunk128Lds& ex, int lane, int w2, c
 template <Elt IN, int P>
 __device__ __forceinline__ void cross_gram(const u32x4 (&fr)[2][P], const u32x4 (&fc)[4][P], f32x4 (&acc)[2][4])
 {
+    if constexpr (IN == Elt::F32) {
+        static_assert(P % 2 == 0, "fragment pairs");
 #pragma unroll
-    for (int bi = 0; bi < 2; ++bi) {
+        for (int s = 0; s < P; s += 2) {
+            Bf16x3 r[2], c[4];
 #pragma unroll
-        for (int bj = 0; bj < 4; ++bj) {
+            for (int bi = 0; bi < 2; ++bi) r[bi] = split_bf16x3(fr[bi][s], fr[bi][s + 1]);
 #pragma unroll
-            for (int s = 0; s < P; ++s) acc[bi][bj] = gram_step<IN>(fc[bj][s], fr[bi][s], acc[bi][bj]);
+            for (int bj = 0; bj < 4; ++bj) c[bj] = split_bf16x3(fc[bj][s], fc[bj][s + 1]);
+#pragma unroll
+            for (int bi = 0; bi < 2; ++bi) {
+#pragma unroll
+                for (int bj = 0; bj < 4; ++bj) acc[bi][bj] = gram_bf16x3(c[bj], r[bi], acc[bi][bj]);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int bi = 0; bi < 2; ++bi) {
+#pragma unroll
+            for (int bj = 0; bj < 4; ++bj) {
+#pragma unroll
+                for (int s = 0; s < P; ++s) acc[bi][bj] = gram_step<IN>(fc[bj][s], fr[bi][s], acc[bi][bj]);
+            }
         }
     }
 }
@@ -949,9 +1028,9 @@ enum KeyStage { kKeysGlobal = 0, kKeysShared = 1 };
 
 template <Elt IN, Elt OUT, int K, int STAGE>
 __global__ __launch_bounds__(kWave * kWavesPerGroup)
-// (shared keys: at most 128 VGPRs, so that registers, like the 39 KB of LDS,
-// leave room for four workgroups per CU)
-__attribute__((amdgpu_waves_per_eu(STAGE == kKeysShared ? 4 : 1)))
+// (shared 16-bit keys: at most 128 VGPRs, so that registers, like the 39 KB
+// of LDS, leave room for four workgroups per CU; split fp32 keys need more)
+__attribute__((amdgpu_waves_per_eu(STAGE == kKeysShared && IN != Elt::F32 ? 4 : 1)))
 void kkt_solve128_kernel(const KernelArgs args)
 {
     constexpr int kOutBytes = EltInfo<OUT>::bytes;
@@ -1000,13 +1079,18 @@ void kkt_solve128_kernel(const KernelArgs args)
 #pragma unroll
                 for (int s = 0; s < kSteps; ++s) fr[bi][s] = __builtin_amdgcn_raw_buffer_load_b128(k_rsrc, voff + s * 64, 0, 0);
             }
+            constexpr int kPer = (IN == Elt::F32) ? 2 : 1;  // fragments per Gram step
 #pragma unroll
-            for (int s = 0; s < kSteps; ++s) {
-                u32x4 fc[4][1];
+            for (int s = 0; s < kSteps; s += kPer) {
+                u32x4 fc[4][kPer], fs[2][kPer];
 #pragma unroll
-                for (int bj = 0; bj < 4; ++bj) fc[bj][0] = ex.kimg[bj][s][lane];
-                u32x4 fs[2][1] = {{fr[0][s]}, {fr[1][s]}};
-                cross_gram<IN, 1>(fs, fc, acc);
+                for (int e = 0; e < kPer; ++e) {
+#pragma unroll
+                    for (int bj = 0; bj < 4; ++bj) fc[bj][e] = ex.kimg[bj][s + e][lane];
+                    fs[0][e] = fr[0][s + e];
+                    fs[1][e] = fr[1][s + e];
+                }
+                cross_gram<IN, kPer>(fs, fc, acc);
             }
             cross_scale(args, ex.cross_gate[w2], lane, w2, cin, acc);
         } else {
