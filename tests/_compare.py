@@ -106,8 +106,9 @@ def compare_A(got: np.ndarray, ref: np.ndarray, scale: np.ndarray, K: int, cu_se
     Structure, bit-exact: +0.0 on and above the diagonal and in columns >= L.
     Strictly lower elements: |gpu - ref| <= (K + 128) 2^-24 scale.  K 2^-24
     bounds an fp32 dot product of length K (products of 16-bit inputs are
-    exact in fp32; fp32 inputs add one rounding per product, within the same
-    bound); 128 2^-24 covers the gate: the difference g_i - g_j (or g_i - g_0
+    exact in fp32; fp32 inputs are summed as six products of their three-part
+    bf16 splits, whose split error and left-out terms stay below 2^-25 of
+    each |k_ik k_jk|, within the same bound); 128 2^-24 covers the gate: the difference g_i - g_j (or g_i - g_0
     and g_0 - g_j, |.| <= 25, in the factored form) rounds with an absolute
     error up to 50 2^-24, exp turns that into the same relative error, and the
     exp2 instruction with its scaling by log2(e) adds about as much again, plus

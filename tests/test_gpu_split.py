@@ -130,6 +130,18 @@ def test_scaled_dot_dtypes_and_head_dims(kkt, in_dtype, K):
     check_scaled_dot(kkt, inp, f"{in_dtype} K={K}")
 
 
+def test_scaled_dot_fp32_keys_across_magnitudes(kkt):
+    """Unnormalised fp32 keys scaled per token by 10^u, u uniform in
+    [-15, 15]: the three-part bf16 split of fp32 keys keeps its relative
+    accuracy at every magnitude (A is checked against a bound proportional to
+    the magnitude of its own terms)."""
+    inp = W.generate("T256_H8_bf16_f32", T=256, H=3, K=128, in_dtype="f32", seed=1150)
+    rng = np.random.default_rng(1151)
+    scale = 10.0 ** rng.uniform(-15.0, 15.0, inp.k_store.shape[:-1] + (1,))
+    inp.k_store = (inp.k_store.astype(np.float64) * scale).astype(np.float32)
+    check_scaled_dot(kkt, inp, "fp32 keys over 30 decades")
+
+
 @pytest.mark.parametrize("out_dtype", ["f32", "bf16", "f16"])
 def test_solve_tril_out_dtypes(kkt, out_dtype):
     inp = W.generate("T256_H8_bf16_f32", B=2, T=200, H=3, seed=1200)
