@@ -122,6 +122,12 @@ def test_chunk128_large_grid(kkt, T, H):
     check(kkt, inp, "bf16", f"large grid T={T} H={H}")
 
 
+def test_chunk128_many_heads(kkt):
+    """H = 96: 24 chunks x 96 workgroups, above 1024 workgroups."""
+    inp = W.generate("T256_H8_bf16_f32", T=3000, H=96, seed=3700)
+    check(kkt, inp, "bf16", "many heads H=96")
+
+
 def test_chunk128_halves_equal_64_token_results(kkt):
     """The diagonal 64x64 blocks of each 128-token chunk are bit-identical to
     the 64-token op on each half (the same arithmetic on the same values), and

@@ -111,6 +111,14 @@ def test_large_grid_tile_order(kkt, T, H):
     check(kkt, inp, "bf16", f"large grid T={T} H={H}")
 
 
+def test_many_heads(kkt):
+    """H = 96 (not a power of two): 47 chunks x 24 workgroups per chunk, a grid
+    above 1024 workgroups in the chunk-grouped order, with runs of 16
+    workgroups and a remainder; row stride 24 KB."""
+    inp = W.generate("T256_H8_bf16_f32", T=3000, H=96, seed=470)
+    check(kkt, inp, "bf16", "many heads H=96")
+
+
 # ---------------------------------------------------------------- varlen
 def _lengths(seed, n, lo, hi, empty_every=0):
     rng = np.random.default_rng(seed)
