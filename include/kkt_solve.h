@@ -78,6 +78,11 @@ typedef enum {
  *   in_dtype   element type of k.
  *   out_dtype  element type of out.  bf16 / f16 results are rounded to nearest
  *              even from the fp32 value.
+ * Precision: all arithmetic is fp32.  The dot products k_i . k_j accumulate
+ * in fp32 on the matrix cores; 16-bit keys multiply exactly, fp32 keys are
+ * split into three bf16 parts (exact to 2^-27 relative) whose six leading
+ * part products are summed, so every A entry stays within (K + 128) 2^-24 of
+ * |beta_i| sum_k |k_ik k_jk| exp(clamp(g_i - g_j)) whatever the key dtype.
  *   out        device, [B,T,H,chunk_size] of out_dtype, contiguous; every element is
  *              written (for varlen: every element of the rows covered by the
  *              sequences).  Must not overlap any input.
