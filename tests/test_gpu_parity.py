@@ -297,6 +297,69 @@ def test_repeatable_and_stream(kkt):
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
 
 
+def test_concurrent_host_threads(kkt):
+    """Four host threads, each with its own stream and its own entry point
+    (64- and 128-token chunks, the gate-sum entry and the two-step chain),
+    launch 25 calls each at the same time; every result equals the same
+    call made alone, bit for bit."""
+    import threading
+    inp = W.generate("T256_H8_bf16_f32", B=2, T=1000, H=6, seed=610)
+    say("[case] concurrent host threads: 4 threads x 25 calls")
+    k, g, b, cu = to_device(inp)
+    B, T, H, _ = k.shape
+    dev = k.device
+
+    def jobs():
+        out = {
+            "fused64": torch.empty((B, T, H, 64), dtype=torch.float32, device=dev),
+            "fused128": torch.empty((B, T, H, 128), dtype=torch.bfloat16, device=dev),
+            "gate_cumsum": torch.empty((B, T, H, 64), dtype=torch.float16, device=dev),
+            "chain_A": torch.empty((B, T, H, 64), dtype=torch.float32, device=dev),
+            "chain": torch.empty((B, T, H, 64), dtype=torch.float32, device=dev),
+        }
+        decay = g.clone()
+        calls = {
+            "fused64": lambda s: kkt.kkt_solve(k, g, b, output_dtype=torch.float32, out=out["fused64"], stream=s),
+            "fused128": lambda s: kkt.kkt_solve(k, g, b, chunk_size=128, output_dtype=torch.bfloat16,
+                                                out=out["fused128"], stream=s),
+            "gate_cumsum": lambda s: kkt.kkt_solve_gate_cumsum(k, decay, b, output_dtype=torch.float16,
+                                                               out=out["gate_cumsum"], stream=s),
+            "chain": lambda s: (kkt.kkt_scaled_dot(k, g, b, out=out["chain_A"], stream=s),
+                                kkt.kkt_solve_tril(out["chain_A"], output_dtype=torch.float32, out=out["chain"],
+                                                   stream=s)),
+        }
+        return out, calls
+
+    alone, alone_calls = jobs()
+    s0 = torch.cuda.Stream()
+    for fn in alone_calls.values():
+        fn(s0)
+    torch.cuda.synchronize()
+    together, calls = jobs()
+    errors = []
+
+    def worker(name):
+        try:
+            s = torch.cuda.Stream()
+            for _ in range(25):
+                calls[name](s)
+            s.synchronize()
+        except Exception as e:  # noqa: BLE001  (reported below)
+            errors.append((name, repr(e)))
+
+    threads = [threading.Thread(target=worker, args=(n,)) for n in calls]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for name in ("fused64", "fused128", "gate_cumsum", "chain"):
+        a, b2 = alone[name], together[name]
+        bits = torch.int32 if a.dtype == torch.float32 else torch.int16
+        assert torch.equal(a.view(bits), b2.view(bits)), name
+
+
 def test_graph_capture_replays(kkt):
     """kkt_solve captured in a HIP graph (the library launches one kernel and
     records no memset): every replay, with eager work and synchronisations in
