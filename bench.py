@@ -42,14 +42,16 @@ KERNEL_SRC = os.path.join(ROOT, "chunked_gated_delta_token_amd", "csrc", "kkt_so
 # the kernel each op launches (chain: both of the unfused steps)
 KERNELS = {"fused": "kkt_solve_kernel", "scaled_dot": "kkt_scaled_dot_kernel",
            "solve_tril": "kkt_solve_tril_kernel", "chain": "kkt_scaled_dot_kernel+kkt_solve_tril_kernel",
-           "gate_cumsum": "kkt_solve_gate_cumsum_kernel", "fused128": "kkt_solve128_kernel"}
-# names of the profile files (fused128: kkt_solve with 128-token chunks)
+           "gate_cumsum": "kkt_solve_gate_cumsum_kernel", "fused128": "kkt_solve128_kernel",
+           "gate_cumsum128": "kkt_solve128_kernel"}
+# names of the profile files (fused128 / gate_cumsum128: those ops with 128-token chunks)
 ENTRY = {"fused": "kkt_solve", "scaled_dot": "kkt_scaled_dot", "solve_tril": "kkt_solve_tril",
-         "gate_cumsum": "kkt_solve_gate_cumsum", "fused128": "kkt_solve128"}
+         "gate_cumsum": "kkt_solve_gate_cumsum", "fused128": "kkt_solve128",
+         "gate_cumsum128": "kkt_solve_gate_cumsum128"}
 
 
 def op_key(op: str, chunk: int) -> str:
-    return "fused128" if (op == "fused" and chunk == 128) else op
+    return op + "128" if (op in ("fused", "gate_cumsum") and chunk == 128) else op
 
 
 def traffic_file(op: str, workload: str) -> str:
@@ -116,7 +118,7 @@ def read_traffic(digest: str, path: str):
         return None
 
 
-def cpu_baseline(inp, nbytes: int, budget_s: float, op: str = "fused"):
+def cpu_baseline(inp, nbytes: int, budget_s: float, op: str = "fused", chunk: int = 64):
     """The fp64 oracle (as it is) for the same step on the same workload,
     repeated until about budget_s seconds of CPU work; throughput in the
     metric's unit."""
@@ -130,9 +132,9 @@ def cpu_baseline(inp, nbytes: int, budget_s: float, op: str = "fused"):
     reps, t0 = 0, time.perf_counter()
     while True:
         if op == "fused":
-            oracle.kkt_solve_ref(k64, g64, b64, cu)
+            oracle.kkt_solve_ref(k64, g64, b64, cu, chunk_size=chunk)
         elif op == "gate_cumsum":
-            oracle.kkt_solve_gate_cumsum_ref(k64, inp.g_raw, b64, cu)
+            oracle.kkt_solve_gate_cumsum_ref(k64, inp.g_raw, b64, cu, chunk_size=chunk)
         elif op == "scaled_dot":
             oracle.scaled_dot_ref(k64, g64, b64, cu)
         elif op == "solve_tril":
@@ -155,7 +157,7 @@ def cpu_baseline(inp, nbytes: int, budget_s: float, op: str = "fused"):
         try:
             reps1, t1 = 0, time.perf_counter()
             while True:
-                oracle.kkt_solve_ref(k64, g64, b64, cu)
+                oracle.kkt_solve_ref(k64, g64, b64, cu, chunk_size=chunk)
                 reps1 += 1
                 el1 = time.perf_counter() - t1
                 if el1 >= budget_s / 3:
@@ -482,8 +484,8 @@ def main():
             raise SystemExit(f"--op gate_cumsum needs a workload with a gate ({name} has none)")
         g0 = torch.from_numpy(inp.g_raw).to(dev)  # per-token log-decays, summed by the kernel
     chunk = args.chunk
-    if chunk != 64 and op != "fused":
-        raise SystemExit("--chunk 128 applies to the fused op only")
+    if chunk != 64 and op not in ("fused", "gate_cumsum"):
+        raise SystemExit("--chunk 128 applies to the fused op and its gate-sum form only")
     nbytes = algorithmic_bytes(w, n_tokens, op, inp.cu_seqlens, chunk)
     num_seqs = 0 if inp.cu_seqlens is None else len(inp.cu_seqlens) - 1
     stream = torch.cuda.Stream(dev)
@@ -534,7 +536,8 @@ def main():
             kargs_c = kargs[:9] + (chunk,) + kargs[10:]
             return [(lib.kkt_solve, kargs_c + (kdt[w.out_dtype], ptr(s_["out"]), sp))]
         if op == "gate_cumsum":
-            return [(lib.kkt_solve_gate_cumsum, kargs + (kdt[w.out_dtype], ptr(s_["out"]), ptr(s_["g_out"]), sp))]
+            kargs_c = kargs[:9] + (chunk,) + kargs[10:]
+            return [(lib.kkt_solve_gate_cumsum, kargs_c + (kdt[w.out_dtype], ptr(s_["out"]), ptr(s_["g_out"]), sp))]
         tril = (lib.kkt_solve_tril, (ptr(s_["A"]), ptr(s_["cu"]), num_seqs, w.B, w.T, w.H, 64, kdt[w.out_dtype],
                                      ptr(s_.get("out")), sp))
         dot = (lib.kkt_scaled_dot, kargs + (ptr(s_["A"]), sp))
@@ -612,7 +615,8 @@ def main():
     metric = METRIC if (op == "fused" and chunk == 64 and name == W.BENCH_WORKLOAD) else {
         "fused": f"fused KKT+solve{' with 128-token chunks' if chunk == 128 else ''} ms/iter & achieved HBM "
                  f"GB/s on {name}, 1 GPU",
-        "gate_cumsum": "fused KKT+solve with the chunk-local gate sum in the kernel ms/iter & achieved HBM GB/s, 1 GPU",
+        "gate_cumsum": f"fused KKT+solve{' with 128-token chunks' if chunk == 128 else ''} and the chunk-local gate "
+                       f"sum in the kernel ms/iter & achieved HBM GB/s on {name}, 1 GPU",
         "scaled_dot": "KKT A alone (first step of the unfused chain) ms/iter & achieved HBM GB/s, 1 GPU",
         "solve_tril": "solve of a given A (second step of the unfused chain) ms/iter & achieved HBM GB/s, 1 GPU",
         "chain": "unfused two-step chain (A through HBM) ms/iter & GB/s of the fused op's bytes, 1 GPU"}[op]
@@ -653,7 +657,7 @@ def main():
             "f32_tflops": round(mf["mfma_flop_f32_per_launch"] / (ev_ms * 1e-3) / 1e12, 2),
         }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(inp, nbytes, args.cpu_seconds, op)
+        line["cpu_baseline"] = cpu_baseline(inp, nbytes, args.cpu_seconds, op, chunk)
     print(json.dumps(line), flush=True)
 
 

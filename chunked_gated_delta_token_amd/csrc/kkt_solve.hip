@@ -63,7 +63,7 @@
 
 #include "kkt_solve.h"
 
-#define KKT_VERSION_NUMBER 503  // 0.5.3
+#define KKT_VERSION_NUMBER 600  // 0.6.0
 
 namespace {
 
@@ -408,6 +408,19 @@ static_assert(sizeof(Chunk128Lds) * 4 <= 160 * 1024, "four 128-token workgroups 
 // Index of lower block (i, j), j <= i, of a 4x4 block-triangular matrix.
 __host__ __device__ constexpr int tri(int i, int j) { return i * (i + 1) / 2 + j; }
 
+// Inclusive prefix sum over the 64 lanes of a wave, in fp32 (a 6-level tree).
+// Every wave that needs a chunk's summed gate uses this one function, so the
+// same decays give the same bits wherever they are summed.
+__device__ __forceinline__ float wave_prefix_sum(float v, int lane)
+{
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const float up = __shfl_up(v, d, kWave);
+        if (lane >= d) v += up;
+    }
+    return v;
+}
+
 // ---------------------------------------------------------------- the kernel
 // Steps a2-a8 for 64 rows of one chunk of CH tokens, on one wave.  CH = 64:
 // the whole chunk (half = 0).  CH = 128: rows 64*half .. 64*half+63, the
@@ -432,7 +445,7 @@ __device__ __forceinline__ void chunk_rows(const KernelArgs& args, WaveLds& lds,
     constexpr int kElemsPer16B = 16 / kInBytes;            // 8 (16-bit) or 4 (fp32)
     constexpr int kSteps = K / (4 * kElemsPer16B);          // 16-byte fragments per row per lane
     static_assert(K % (4 * kElemsPer16B) == 0, "K must fill whole fragments");
-    static_assert(CH == 64 || (CH == 128 && MODE == Mode::Fused && !GATE_SUM), "128-token chunks: fused op only");
+    static_assert(CH == 64 || (CH == 128 && MODE == Mode::Fused), "128-token chunks: fused op only");
     static_assert(!SHARE || (CH == 128 && kSteps <= 4), "shared key tile: 128-token kernel, at most 4 k-steps");
     const int q = lane / 16;   // lane group (k-slot group of an MFMA operand)
     const int m = lane % 16;   // row inside a 16-row block (A operand) / column (D layout)
@@ -469,7 +482,7 @@ __device__ __forceinline__ void chunk_rows(const KernelArgs& args, WaveLds& lds,
     } else {
         const bool has_g = args.g != nullptr;
         const bool valid = lane < L - (int)row_base;
-        float gv = 0.0f, bv = 1.0f;
+        float gv = 0.0f, bv = 1.0f, g_first = 0.0f;
         u32x4 frag[4][kSteps];
         const __amdgpu_buffer_rsrc_t k_rsrc = make_rsrc(
             static_cast<const char*>(args.k) + tok * (int64_t)(K * kInBytes),
@@ -484,6 +497,11 @@ __device__ __forceinline__ void chunk_rows(const KernelArgs& args, WaveLds& lds,
             // the loads return raw 32-bit words: reinterpret, do not convert
             if (has_g) {
                 gv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(args.g + tok, span), voff, 0, 0));
+                if (GATE_SUM && CH == 128 && half == 1) {
+                    // the second half's gate starts from the first half's total
+                    g_first = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                        make_rsrc(args.g + tok, span), (uint32_t)lane * (uint32_t)H * 4u, 0, 0));
+                }
             }
             if (args.beta != nullptr) {
                 bv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(args.beta + tok, span), voff, 0, 0));
@@ -512,12 +530,15 @@ __device__ __forceinline__ void chunk_rows(const KernelArgs& args, WaveLds& lds,
         // row).  It needs only g, the first load issued, so it runs while the
         // K tile is still arriving.
         if (GATE_SUM && has_g) {
-#pragma unroll
-            for (int d = 1; d < kWave; d <<= 1) {
-                const float up = __shfl_up(gv, d, kWave);
-                if (lane >= d) gv += up;
-            }
-            if (args.g_out != nullptr) {
+            gv = wave_prefix_sum(gv, lane);
+            if constexpr (CH == 128) {
+                // 128-token chunks: the second half adds the first half's
+                // total; the A21 waves write the summed gate of both halves
+                if (half == 1) {
+                    const float total = __shfl(wave_prefix_sum(g_first, lane), kWave - 1, kWave);
+                    gv = total + gv;
+                }
+            } else if (args.g_out != nullptr) {
                 const uint32_t span = (uint32_t)(L - 1) * (uint32_t)H * 4u + 4u;
                 __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, gv), make_rsrc(args.g_out + tok, span),
                                                       (uint32_t)lane * (uint32_t)H * 4u, 0, 0);
@@ -848,6 +869,17 @@ __device__ __forceinline__ CrossIn cross_gate_beta(const KernelArgs& args, int l
     return c;
 }
 
+// Gate-sum kernel, 128-token chunks: the loaded per-token decays of the two
+// halves become the chunk's summed gate (the second half starts from the
+// first half's total), bit for bit as the halves' own waves form it.
+__device__ __forceinline__ void cross_gate_sum(CrossIn& c, int lane)
+{
+    const float lo = wave_prefix_sum(c.g_lo, lane);
+    const float total = __shfl(lo, kWave - 1, kWave);
+    c.g_lo = lo;
+    c.g_hi = total + wave_prefix_sum(c.g_hi, lane);
+}
+
 // acc[bi][bj]: S21 block (2 w2 + bi, bj) in left-operand layout, i.e. lane
 // (q, m) holds S21[m][4q + r]: second-half row 32 w2 + 16 bi + m, first-half
 // column 16 bj + 4q + r.  Turned into the A21 blocks in place.
@@ -928,9 +960,9 @@ __device__ __forceinline__ void cross_gram(const u32x4 (&fr)[2][P], const u32x4 
 // A21 blocks (the rows of w2; scaled, in registers) with the keys read from
 // global memory in passes of at most 4 fragments per row (head dimensions
 // whose key fragments do not fit the LDS image).
-template <Elt IN, int K>
+template <Elt IN, int K, bool GATE_SUM>
 __device__ __forceinline__ void cross_block_rows(const KernelArgs& args, GateLds& lds, int lane, int64_t tok, int L,
-                                                 int w2, f32x4 (&acc)[2][4])
+                                                 int w2, f32x4 (&acc)[2][4], CrossIn& in)
 {
     constexpr int kInBytes = EltInfo<IN>::bytes;
     constexpr int kElemsPer16B = 16 / kInBytes;
@@ -942,7 +974,8 @@ __device__ __forceinline__ void cross_block_rows(const KernelArgs& args, GateLds
     const __amdgpu_buffer_rsrc_t k_rsrc = make_rsrc(
         static_cast<const char*>(args.k) + tok * (int64_t)(K * kInBytes),
         (uint32_t)(L - 1) * args.k_row_bytes + K * kInBytes);
-    const CrossIn in = cross_gate_beta(args, lane, tok, L);
+    in = cross_gate_beta(args, lane, tok, L);
+    if (GATE_SUM && args.g != nullptr) cross_gate_sum(in, lane);
 #pragma unroll
     for (int bi = 0; bi < 2; ++bi) {
 #pragma unroll
@@ -1026,7 +1059,7 @@ void kkt_solve_tril_kernel(const KernelArgs args)
 //                passes of 4 k-steps.
 enum KeyStage { kKeysGlobal = 0, kKeysShared = 1 };
 
-template <Elt IN, Elt OUT, int K, int STAGE>
+template <Elt IN, Elt OUT, int K, int STAGE, bool GATE_SUM>
 __global__ __launch_bounds__(kWave * kWavesPerGroup)
 // (shared 16-bit keys: at most 128 VGPRs, so that registers, like the 39 KB
 // of LDS, leave room for four workgroups per CU; split fp32 keys need more)
@@ -1052,11 +1085,12 @@ void kkt_solve128_kernel(const KernelArgs args)
     constexpr int kSteps = K / (4 * (16 / kInBytes));
     static_assert(STAGE == kKeysGlobal || kSteps <= 4, "the LDS key image holds at most 4 k-steps");
     if (wave < 2) {
-        chunk_rows<Mode::Fused, IN, OUT, K, false, 2 * kChunk, STAGE == kKeysShared>(args, ex.half[wave], lane, tok, L,
-                                                                                     wave, &ex);
+        chunk_rows<Mode::Fused, IN, OUT, K, GATE_SUM, 2 * kChunk, STAGE == kKeysShared>(args, ex.half[wave], lane, tok,
+                                                                                        L, wave, &ex);
     } else {
         const int w2 = wave - 2;
         f32x4 acc[2][4];
+        CrossIn cin;
         if constexpr (STAGE == kKeysShared) {
             // the first half's fragments from wave 0 via LDS; the own rows
             // (64 + 32 w2 ..) from memory, but only after the barrier: wave 1
@@ -1065,7 +1099,8 @@ void kkt_solve128_kernel(const KernelArgs args)
             const __amdgpu_buffer_rsrc_t k_rsrc = make_rsrc(
                 static_cast<const char*>(args.k) + tok * (int64_t)(K * kInBytes),
                 (uint32_t)(L - 1) * args.k_row_bytes + K * kInBytes);
-            const CrossIn cin = cross_gate_beta(args, lane, tok, L);
+            cin = cross_gate_beta(args, lane, tok, L);
+            if (GATE_SUM && args.g != nullptr) cross_gate_sum(cin, lane);
 #pragma unroll
             for (int bi = 0; bi < 2; ++bi) {
 #pragma unroll
@@ -1094,10 +1129,21 @@ void kkt_solve128_kernel(const KernelArgs args)
             }
             cross_scale(args, ex.cross_gate[w2], lane, w2, cin, acc);
         } else {
-            cross_block_rows<IN, K>(args, ex.cross_gate[w2], lane, tok, L, w2, acc);
+            cross_block_rows<IN, K, GATE_SUM>(args, ex.cross_gate[w2], lane, tok, L, w2, acc, cin);
         }
         __syncthreads();  // end of the first phase: the exchange area overlaps its areas
         cross_store(ex, lane, w2, acc);
+        if constexpr (GATE_SUM) {
+            // every wave has read its decays by now, so g_out may alias them
+            if (w2 == 0 && args.g != nullptr && args.g_out != nullptr) {
+                const uint32_t span = (uint32_t)(L - 1) * (uint32_t)H * 4u + 4u;
+                const __amdgpu_buffer_rsrc_t go = make_rsrc(args.g_out + tok, span);
+                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, cin.g_lo), go,
+                                                      (uint32_t)lane * (uint32_t)H * 4u, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, cin.g_hi), go,
+                                                      (64u + (uint32_t)lane) * (uint32_t)H * 4u, 0, 0);
+            }
+        }
     }
     __syncthreads();
 
@@ -1249,20 +1295,20 @@ hipError_t launch_fused(int64_t K, const KernelArgs& a, hipStream_t stream)
     }
 }
 
-template <Elt IN, Elt OUT, int K>
+template <Elt IN, Elt OUT, int K, bool GATE_SUM>
 hipError_t launch_fused128_k(const KernelArgs& a, hipStream_t stream)
 {
     constexpr int kSteps = K / (4 * (16 / EltInfo<IN>::bytes));
-    return launch(kkt_solve128_kernel<IN, OUT, K, (kSteps <= 4) ? kKeysShared : kKeysGlobal>, a, stream);
+    return launch(kkt_solve128_kernel<IN, OUT, K, (kSteps <= 4) ? kKeysShared : kKeysGlobal, GATE_SUM>, a, stream);
 }
 
-template <Elt IN, Elt OUT>
+template <Elt IN, Elt OUT, bool GATE_SUM>
 hipError_t launch_fused128(int64_t K, const KernelArgs& a, hipStream_t stream)
 {
     switch (K) {
-    case 64: return launch_fused128_k<IN, OUT, 64>(a, stream);
-    case 128: return launch_fused128_k<IN, OUT, 128>(a, stream);
-    default: return launch_fused128_k<IN, OUT, 256>(a, stream);
+    case 64: return launch_fused128_k<IN, OUT, 64, GATE_SUM>(a, stream);
+    case 128: return launch_fused128_k<IN, OUT, 128, GATE_SUM>(a, stream);
+    default: return launch_fused128_k<IN, OUT, 256, GATE_SUM>(a, stream);
     }
 }
 
@@ -1271,9 +1317,9 @@ hipError_t launch_fused_out(kkt_dtype_t od, int64_t K, int64_t chunk, const Kern
 {
     if (chunk == 2 * kChunk) {
         switch (od) {
-        case KKT_DTYPE_F32: return launch_fused128<IN, Elt::F32>(K, a, stream);
-        case KKT_DTYPE_BF16: return launch_fused128<IN, Elt::BF16>(K, a, stream);
-        default: return launch_fused128<IN, Elt::F16>(K, a, stream);
+        case KKT_DTYPE_F32: return launch_fused128<IN, Elt::F32, GATE_SUM>(K, a, stream);
+        case KKT_DTYPE_BF16: return launch_fused128<IN, Elt::BF16, GATE_SUM>(K, a, stream);
+        default: return launch_fused128<IN, Elt::F16, GATE_SUM>(K, a, stream);
         }
     }
     switch (od) {
@@ -1418,7 +1464,7 @@ extern "C" kkt_status_t kkt_solve_gate_cumsum(const void* k, const float* g_deca
                                               void* out, float* g_out, hipStream_t stream)
 {
     g_last_error.clear();
-    if (chunk_size != kChunk) return fail(KKT_ERR_UNSUPPORTED, "chunk_size must be 64");
+    if (chunk_size != kChunk && chunk_size != 2 * kChunk) return fail(KKT_ERR_UNSUPPORTED, "chunk_size must be 64 or 128");
     if (!valid_dtype((int)in_dtype) || !valid_dtype((int)out_dtype)) return fail(KKT_ERR_INVALID_ARGUMENT, "unknown dtype");
     kkt_status_t st = check_k_sizes(B, T, H, K, num_seqs, cu_seqlens);
     if (st != KKT_OK) return st;
@@ -1427,15 +1473,15 @@ extern "C" kkt_status_t kkt_solve_gate_cumsum(const void* k, const float* g_deca
     if ((reinterpret_cast<uintptr_t>(g_out) & 3u) != 0) return fail(KKT_ERR_INVALID_ARGUMENT, "g_out must be 4-byte aligned");
     KernelArgs a;
     st = setup(a, k, g_decay, beta, cu_seqlens, num_seqs, B, T, H, H * K * dtype_bytes(in_dtype),
-               H * kChunk * dtype_bytes(out_dtype), out, stream);
+               H * chunk_size * dtype_bytes(out_dtype), out, stream, chunk_size);
     if (st != KKT_OK) return st;
     a.g_out = g_out;
 
     hipError_t e;
     switch (in_dtype) {
-    case KKT_DTYPE_F32: e = launch_fused_out<Elt::F32, true>(out_dtype, K, kChunk, a, stream); break;
-    case KKT_DTYPE_BF16: e = launch_fused_out<Elt::BF16, true>(out_dtype, K, kChunk, a, stream); break;
-    default: e = launch_fused_out<Elt::F16, true>(out_dtype, K, kChunk, a, stream); break;
+    case KKT_DTYPE_F32: e = launch_fused_out<Elt::F32, true>(out_dtype, K, chunk_size, a, stream); break;
+    case KKT_DTYPE_BF16: e = launch_fused_out<Elt::BF16, true>(out_dtype, K, chunk_size, a, stream); break;
+    default: e = launch_fused_out<Elt::F16, true>(out_dtype, K, chunk_size, a, stream); break;
     }
     if (e != hipSuccess) return fail(KKT_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(e));
     return KKT_OK;

@@ -186,15 +186,16 @@ def kkt_solve_gate_cumsum(k: torch.Tensor, g_decay: torch.Tensor, beta: Optional
     fp32: the kernel sums it within every chunk (the gate ``kkt_solve``
     takes) before using it.  With ``return_gate`` (or a given ``g_out``) the
     summed gate is written too and ``(out, g)`` is returned; ``g_out`` may be
-    ``g_decay`` itself (in-place sum)."""
+    ``g_decay`` itself (in-place sum).  ``chunk_size`` 64 or 128, as for
+    ``kkt_solve``."""
     if g_decay is None:
         raise ValueError("g_decay is required (use kkt_solve without a gate)")
-    k, g_decay, beta, cu_seqlens, num_seqs = _k_inputs(k, g_decay, beta, cu_seqlens, chunk_size)
+    k, g_decay, beta, cu_seqlens, num_seqs = _k_inputs(k, g_decay, beta, cu_seqlens, chunk_size, (64, 128))
     B, T, H, K = k.shape
     odt = k.dtype if output_dtype is None else output_dtype
     if odt not in _TORCH_TO_KKT:
         raise TypeError(f"unsupported output dtype {odt}")
-    out = _out_tensor(out, (B, T, H, 64), odt, k.device)
+    out = _out_tensor(out, (B, T, H, chunk_size), odt, k.device)
     if g_out is None and return_gate:
         g_out = torch.empty((B, T, H), dtype=torch.float32, device=k.device)
     elif g_out is not None:

@@ -122,11 +122,13 @@ kkt_status_t kkt_solve(const void* k, const float* g, const float* beta,
  *              every covered row (the later steps of the forward pass use
  *              it).  It may be the same pointer as g_decay (the sum is then
  *              done in place); it must not overlap any other argument.
- *   The sum is a 6-level tree (a parallel inclusive scan over the 64 rows) in
- *   fp32; its result differs from a left-to-right sum by rounding only.
- *   kkt_solve(k, g_out, ...) on the g_out this call wrote gives bit-identical
- *   output.  Everything else (arguments, alignment, errors) as for kkt_solve,
- *   except that chunk_size must be 64; g_out must be 4-byte aligned.
+ *   The sum is a 6-level tree (a parallel inclusive scan over 64 rows) in
+ *   fp32; with chunk_size 128 the second half's scan is added to the first
+ *   half's total (7 levels).  Its result differs from a left-to-right sum by
+ *   rounding only.  kkt_solve(k, g_out, ...) with the same chunk_size on the
+ *   g_out this call wrote gives bit-identical output.  Everything else
+ *   (arguments, chunk_size 64 or 128, alignment, errors) as for kkt_solve;
+ *   g_out must be 4-byte aligned.
  */
 kkt_status_t kkt_solve_gate_cumsum(const void* k, const float* g_decay, const float* beta,
                                    const int32_t* cu_seqlens, int64_t num_seqs,

@@ -48,7 +48,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version(lib):
-    assert lib.kkt_version() == 503
+    assert lib.kkt_version() == 600
 
 
 def _call(lib, **over):
@@ -112,12 +112,13 @@ def test_scaled_dot_invalid_arguments(lib, over, status, msg):
     assert msg in kkt.last_error()
 
 
-def test_chunk128_is_served_by_kkt_solve_only(lib):
-    """chunk_size 128 passes kkt_solve's argument checks (NULL pointers are
-    then the first error) and is rejected by the other entry points."""
+def test_chunk128_is_served_by_the_fused_entry_points_only(lib):
+    """chunk_size 128 passes the argument checks of kkt_solve and
+    kkt_solve_gate_cumsum (NULL pointers are then the first error) and is
+    rejected by the two split steps."""
     from chunked_gated_delta_token_amd import kkt
     assert _call(lib, chunk_size=128, k=None) == 1 and "NULL" in kkt.last_error()
-    assert _call_gate_cumsum(lib, chunk_size=128) == 2 and "chunk_size" in kkt.last_error()
+    assert _call_gate_cumsum(lib, chunk_size=128, k=None) == 1 and "NULL" in kkt.last_error()
     assert _call_scaled_dot(lib, chunk_size=128) == 2 and "chunk_size" in kkt.last_error()
     assert _call_solve_tril(lib, chunk_size=128) == 2 and "chunk_size" in kkt.last_error()
 
@@ -133,6 +134,7 @@ def _call_gate_cumsum(lib, **over):
 
 @pytest.mark.parametrize("over,status,msg", [
     (dict(chunk_size=32), 2, "chunk_size"),
+    (dict(chunk_size=256), 2, "chunk_size"),
     (dict(out_dtype=9), 1, "dtype"),
     (dict(K=48), 2, "K must be"),
     (dict(T=-1), 1, ">= 1"),

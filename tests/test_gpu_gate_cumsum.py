@@ -1,5 +1,7 @@
 """GPU parity of ``kkt_solve_gate_cumsum``: the fused op fed with per-token
-log-decays, the chunk-local sum formed in the kernel.
+log-decays, the chunk-local sum formed in the kernel (64- and 128-token
+chunks; with 128, the second half's 6-level scan is added to the first
+half's total, 7 levels, still within the bound below).
 
 Against the oracle: the summed gate within 8 2^-24 of the running sum of
 |decay| (a 6-level fp32 tree sum has first-order error at most 6 2^-24 times
@@ -30,28 +32,28 @@ def kkt():
     return load_kkt()
 
 
-def run(kkt, inp: W.Inputs, out_dtype: str, with_gate_out=True, in_place=False):
+def run(kkt, inp: W.Inputs, out_dtype: str, with_gate_out=True, in_place=False, chunk=64):
     k, _g, b, cu = to_device(inp)
     a = torch.from_numpy(inp.g_raw).to(k.device)
     B, T, H, _ = k.shape
-    out = torch.full((B, T, H, 64), float("nan"), dtype=TORCH_DT[out_dtype], device=k.device)
+    out = torch.full((B, T, H, chunk), float("nan"), dtype=TORCH_DT[out_dtype], device=k.device)
     g_out = None
     if in_place:
         g_out = a
     elif with_gate_out:
         g_out = torch.full((B, T, H), float("nan"), dtype=torch.float32, device=k.device)
-    kkt.kkt_solve_gate_cumsum(k, a, b, cu, output_dtype=TORCH_DT[out_dtype], out=out, g_out=g_out)
+    kkt.kkt_solve_gate_cumsum(k, a, b, cu, chunk_size=chunk, output_dtype=TORCH_DT[out_dtype], out=out, g_out=g_out)
     torch.cuda.synchronize()
     return from_device(out, out_dtype), (None if g_out is None else g_out.cpu().numpy())
 
 
-def check(kkt, inp: W.Inputs, out_dtype: str, label: str):
+def check(kkt, inp: W.Inputs, out_dtype: str, label: str, chunk: int = 64):
     w = inp.workload
-    say(f"[case] gate_cumsum {label}: B={w.B} T={w.T} H={w.H} K={w.K} in={w.in_dtype} out={out_dtype} "
+    say(f"[case] gate_cumsum {label}: chunk={chunk} B={w.B} T={w.T} H={w.H} K={w.K} in={w.in_dtype} out={out_dtype} "
         f"beta={inp.beta is not None} seqs={0 if inp.cu_seqlens is None else len(inp.cu_seqlens) - 1}")
-    got, g = run(kkt, inp, out_dtype)
-    X_ref, g_ref = oracle.kkt_solve_gate_cumsum_ref(inp.k64(), inp.g_raw, inp.beta, inp.cu_seqlens)
-    prefix_abs = oracle.chunk_cumsum_ref(np.abs(inp.g_raw.astype(np.float64)), inp.cu_seqlens)
+    got, g = run(kkt, inp, out_dtype, chunk=chunk)
+    X_ref, g_ref = oracle.kkt_solve_gate_cumsum_ref(inp.k64(), inp.g_raw, inp.beta, inp.cu_seqlens, chunk_size=chunk)
+    prefix_abs = oracle.chunk_cumsum_ref(np.abs(inp.g_raw.astype(np.float64)), inp.cu_seqlens, chunk_size=chunk)
     err = np.abs(g.astype(np.float64) - g_ref)
     bound = GATE_BOUND_ULPS * 2.0 ** -24 * prefix_abs
     assert not np.any(np.isnan(g)), f"{label}: unwritten gate rows"
@@ -62,8 +64,9 @@ def check(kkt, inp: W.Inputs, out_dtype: str, label: str):
     # the same gate through kkt_solve gives the same rows, bit for bit
     k, _g, b, cu = to_device(inp)
     B, T, H, _ = k.shape
-    out2 = torch.full((B, T, H, 64), float("nan"), dtype=TORCH_DT[out_dtype], device=k.device)
-    kkt.kkt_solve(k, torch.from_numpy(g).to(k.device), b, cu, output_dtype=TORCH_DT[out_dtype], out=out2)
+    out2 = torch.full((B, T, H, chunk), float("nan"), dtype=TORCH_DT[out_dtype], device=k.device)
+    kkt.kkt_solve(k, torch.from_numpy(g).to(k.device), b, cu, chunk_size=chunk, output_dtype=TORCH_DT[out_dtype],
+                  out=out2)
     torch.cuda.synchronize()
     view = np.uint32 if out_dtype == "f32" else np.uint16
     assert np.array_equal(from_device(out2, out_dtype).view(view), got.view(view)), f"{label}: kkt_solve differs"
@@ -117,6 +120,52 @@ def test_gate_cumsum_in_place_and_without_gate_output(kkt):
     ref_X, ref_g = run(kkt, inp, "f32")
     X_in, g_in = run(kkt, inp, "f32", in_place=True)
     X_none, _ = run(kkt, inp, "f32", with_gate_out=False)
+    assert np.array_equal(g_in.view(np.uint32), ref_g.view(np.uint32))
+    assert np.array_equal(X_in.view(np.uint32), ref_X.view(np.uint32))
+    assert np.array_equal(X_none.view(np.uint32), ref_X.view(np.uint32))
+
+
+# ---------------------------------------------------------------- 128-token chunks
+@pytest.mark.parametrize("name", GATED)
+def test_gate_cumsum128_full_parity(kkt, name):
+    inp = W.generate(name)
+    check(kkt, inp, inp.workload.out_dtype, name, chunk=128)
+
+
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 127, 128, 129, 300])
+def test_gate_cumsum128_lengths(kkt, T):
+    inp = W.generate("T256_H8_bf16_f32", B=2, T=T, H=3, seed=2500 + T, beta=bool(T % 2))
+    check(kkt, inp, "f32", f"T={T}", chunk=128)
+
+
+def test_gate_cumsum128_varlen_short(kkt):
+    inp = W.generate("T256_H8_bf16_f32", lengths=[1, 2, 3, 0, 64, 65, 0, 130, 5, 128, 129, 300] + [1, 3] * 40,
+                     H=3, seed=2600)
+    check(kkt, inp, "bf16", "varlen short", chunk=128)
+
+
+def test_gate_cumsum128_strong_decay_takes_the_clamp(kkt):
+    inp = W.generate("T256_H8_bf16_f32", T=300, H=2, seed=2700)
+    rng = np.random.default_rng(2701)
+    inp.g_raw = (-rng.uniform(0.0, 3.0, inp.g_raw.shape)).astype(np.float32)
+    check(kkt, inp, "f32", "strong decay", chunk=128)
+
+
+@pytest.mark.parametrize("in_dtype,out_dtype,K", [("f16", "f16", 128), ("f32", "bf16", 128), ("bf16", "f32", 256),
+                                                  ("f32", "f32", 64)])
+def test_gate_cumsum128_dtypes_and_key_paths(kkt, in_dtype, out_dtype, K):
+    """Keys shared through LDS (16-bit K <= 128, fp32 K = 64) and read by
+    every wave (fp32 K = 128, 16-bit K = 256)."""
+    inp = W.generate("T256_H8_bf16_f32", B=2, T=300, H=3, K=K, in_dtype=in_dtype, seed=2800 + K)
+    check(kkt, inp, out_dtype, f"{in_dtype}->{out_dtype} K={K}", chunk=128)
+
+
+def test_gate_cumsum128_in_place_and_without_gate_output(kkt):
+    inp = W.generate("T256_H8_bf16_f32", B=2, T=300, H=5, seed=2900)
+    say("[case] gate_cumsum chunk=128 in place / no gate output: B=2 T=300 H=5")
+    ref_X, ref_g = run(kkt, inp, "f32", chunk=128)
+    X_in, g_in = run(kkt, inp, "f32", in_place=True, chunk=128)
+    X_none, _ = run(kkt, inp, "f32", with_gate_out=False, chunk=128)
     assert np.array_equal(g_in.view(np.uint32), ref_g.view(np.uint32))
     assert np.array_equal(X_in.view(np.uint32), ref_X.view(np.uint32))
     assert np.array_equal(X_none.view(np.uint32), ref_X.view(np.uint32))

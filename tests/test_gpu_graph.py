@@ -30,13 +30,15 @@ def _calls(kkt, name, k, g, b, cu):
 
         def launch(o, s):
             kkt.kkt_solve(k, g, b, cu, chunk_size=C, output_dtype=torch.bfloat16, out=o[0], stream=s)
-    elif name == "gate_cumsum":
+    elif name in ("gate_cumsum", "gate_cumsum128"):
+        C = 64 if name == "gate_cumsum" else 128
         decay = g.clone()
-        outs = [torch.empty((B, T, H, 64), dtype=torch.float32, device=dev),
+        outs = [torch.empty((B, T, H, C), dtype=torch.float32, device=dev),
                 torch.empty((B, T, H), dtype=torch.float32, device=dev)]
 
         def launch(o, s):
-            kkt.kkt_solve_gate_cumsum(k, decay, b, cu, output_dtype=torch.float32, out=o[0], g_out=o[1], stream=s)
+            kkt.kkt_solve_gate_cumsum(k, decay, b, cu, chunk_size=C, output_dtype=torch.float32, out=o[0],
+                                      g_out=o[1], stream=s)
     else:  # the two-step chain
         outs = [torch.empty((B, T, H, 64), dtype=torch.float32, device=dev),
                 torch.empty((B, T, H, 64), dtype=torch.float16, device=dev)]
@@ -48,7 +50,7 @@ def _calls(kkt, name, k, g, b, cu):
 
 
 @pytest.mark.parametrize("packed", [False, True])
-@pytest.mark.parametrize("name", ["fused64", "fused128", "gate_cumsum", "chain"])
+@pytest.mark.parametrize("name", ["fused64", "fused128", "gate_cumsum", "gate_cumsum128", "chain"])
 def test_graph_replays_equal_eager(kkt, name, packed):
     if packed:
         inp = W.generate("T256_H8_bf16_f32", lengths=[300, 1, 0, 129, 64, 77] + [5, 40] * 40, H=5, seed=7100)
