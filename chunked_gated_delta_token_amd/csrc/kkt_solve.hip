@@ -545,6 +545,30 @@ __device__ __forceinline__ void chunk_rows(const KernelArgs& args, WaveLds& lds,
             }
         }
 
+        // ---- a5, first part: the row and column scales of the epilogue.
+        // They need only g and beta, the first loads issued, so they are
+        // formed and put in LDS while the K tile is still arriving.
+        bool factored = true;
+        if (has_g) {
+            // reference: row 0's gate (always a valid row), so the factors of
+            // rows < L do not depend on L.  If every valid row is within 25 of
+            // it, every pair differs by at most 50 (the clamp cannot bind) and
+            // every factor lies in [e^-25, e^25].
+            const float gref = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, gv)));
+            factored = __all(!valid || fabsf(gv - gref) <= 0.5f * kGateClamp);
+            if (factored) {
+                const float d = gv - gref;
+                lds.row_scale[lane] = valid ? bv * __expf(d) : 0.0f;
+                lds.col_scale[lane] = valid ? __expf(-d) : 0.0f;
+            } else {
+                lds.row_scale[lane] = valid ? bv : 0.0f;
+                lds.gate[lane] = valid ? gv : 0.0f;
+            }
+        } else {
+            lds.row_scale[lane] = valid ? bv : 0.0f;
+        }
+        wave_lds_sync();
+
         // ---- a4: Gram blocks.  Block (i, j): lane (q, n=m) holds rows 16i + 4q + r, column 16j + n.
         f32x4 S[4][4];
         if constexpr (IN == Elt::F32) {
@@ -592,27 +616,7 @@ __device__ __forceinline__ void chunk_rows(const KernelArgs& args, WaveLds& lds,
             __syncthreads();  // the first half's key fragments are in LDS
         }
 
-        // ---- a5: epilogue
-        bool factored = true;
-        if (has_g) {
-            // reference: row 0's gate (always a valid row), so the factors of
-            // rows < L do not depend on L.  If every valid row is within 25 of
-            // it, every pair differs by at most 50 (the clamp cannot bind) and
-            // every factor lies in [e^-25, e^25].
-            const float gref = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, gv)));
-            factored = __all(!valid || fabsf(gv - gref) <= 0.5f * kGateClamp);
-            if (factored) {
-                const float d = gv - gref;
-                lds.row_scale[lane] = valid ? bv * __expf(d) : 0.0f;
-                lds.col_scale[lane] = valid ? __expf(-d) : 0.0f;
-            } else {
-                lds.row_scale[lane] = valid ? bv : 0.0f;
-                lds.gate[lane] = valid ? gv : 0.0f;
-            }
-        } else {
-            lds.row_scale[lane] = valid ? bv : 0.0f;
-        }
-        wave_lds_sync();
+        // ---- a5: epilogue (the scales are in LDS already)
         if (!has_g) {
             // A = beta_i S (rows >= L have beta 0 and zero keys)
 #pragma unroll
@@ -715,14 +719,15 @@ __device__ __forceinline__ void chunk_rows(const KernelArgs& args, WaveLds& lds,
         return;
     }
 
-    // strict lower triangle inside the diagonal blocks, stored transposed
-    // (blk[d][col][row]): lane (q, n) holds rows 4q..4q+3 of column n, one
-    // 16-byte write, and the solve below reads columns as contiguous rows
+    // strict lower triangle inside the diagonal blocks, negated and stored
+    // transposed (blk[d][col][row]): lane (q, n) holds rows 4q..4q+3 of
+    // column n, one 16-byte write, and each lane of the solve below reads its
+    // column as one contiguous row
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         f32x4 v;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = (4 * q + r > m) ? A[i][i][r] : 0.0f;
+        for (int r = 0; r < 4; ++r) v[r] = (4 * q + r > m) ? -A[i][i][r] : 0.0f;
         *reinterpret_cast<f32x4*>(&lds.blk[i][m][4 * q]) = v;
     }
     wave_lds_sync();
@@ -730,29 +735,86 @@ __device__ __forceinline__ void chunk_rows(const KernelArgs& args, WaveLds& lds,
     // ---- a6: X_dd = (I + A_dd)^{-1}; lane (d = lane / 16, c = lane % 16)
     // computes column c of X_dd by right-looking forward substitution: once
     // x[p] is final, every later row takes its term, acc[r] -= A[r][p] x[p].
-    // Each step's updates are independent of each other, so the dependent
-    // chain is one FMA per row; column p of A_dd is row p of the transposed
-    // block.  acc[r] starts at [r == c]; rows above c stay exactly 0.
+    // acc[r] starts at [r == c]; rows above c stay exactly 0.  Each lane
+    // reads its own column of -A_dd once; the element A[r][p] that step p
+    // needs is row r of lane p's column, which a DPP row broadcast
+    // (row_newbcast:p, lane p of each 16-lane row to the whole row: the 16
+    // lanes of one block) feeds straight into the FMA.  A step's updates are
+    // independent, so the dependent chain is one FMA per row, and no step
+    // waits on LDS.
     {
         const int d = lane / 16;
         const int c = lane % 16;
+        float col[16];  // -A_dd[r][c]; zero for r <= c
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const f32x4 v = *reinterpret_cast<const f32x4*>(&lds.blk[d][c][4 * u]);
+            col[4 * u + 0] = v[0];
+            col[4 * u + 1] = v[1];
+            col[4 * u + 2] = v[2];
+            col[4 * u + 3] = v[3];
+        }
         float acc[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[r] = (r == c) ? 1.0f : 0.0f;
-#pragma unroll
-        for (int p = 0; p < 15; ++p) {
-            float col[16];
-#pragma unroll
-            for (int u = (p + 1) / 4; u < 4; ++u) {
-                const f32x4 v = *reinterpret_cast<const f32x4*>(&lds.blk[d][p][4 * u]);
-                col[4 * u + 0] = v[0];
-                col[4 * u + 1] = v[1];
-                col[4 * u + 2] = v[2];
-                col[4 * u + 3] = v[3];
-            }
-#pragma unroll
-            for (int r = p + 1; r < 16; ++r) acc[r] = __builtin_fmaf(-col[r], acc[p], acc[r]);
-        }
+        // Step p: acc[r] = fma(-A[r][p], acc[p], acc[r]) for r = p+1 .. 15,
+        // one v_fmac_f32 with the broadcast on its first operand per row.
+        // One statement per step; its leading s_nop covers the two wait
+        // states a DPP instruction needs after a VALU write of a VGPR it
+        // reads (the previous step's results, or any copy the compiler
+        // makes of an input), and inside a step no instruction reads what
+        // another one writes.
+#define KKT_BCAST_FMAC(r, p) "v_fmac_f32_dpp %[a" #r "], %[c" #r "], %[x] row_newbcast:" #p " row_mask:0xf bank_mask:0xf\n"
+#define KKT_ACC(r) [a##r] "+v"(acc[r])
+#define KKT_COL(r) [c##r] "v"(col[r])
+        asm("s_nop 1\n" KKT_BCAST_FMAC(1, 0) KKT_BCAST_FMAC(2, 0) KKT_BCAST_FMAC(3, 0) KKT_BCAST_FMAC(4, 0) KKT_BCAST_FMAC(5, 0) KKT_BCAST_FMAC(6, 0) KKT_BCAST_FMAC(7, 0) KKT_BCAST_FMAC(8, 0) KKT_BCAST_FMAC(9, 0) KKT_BCAST_FMAC(10, 0) KKT_BCAST_FMAC(11, 0) KKT_BCAST_FMAC(12, 0) KKT_BCAST_FMAC(13, 0) KKT_BCAST_FMAC(14, 0) KKT_BCAST_FMAC(15, 0)
+            : KKT_ACC(1), KKT_ACC(2), KKT_ACC(3), KKT_ACC(4), KKT_ACC(5), KKT_ACC(6), KKT_ACC(7), KKT_ACC(8), KKT_ACC(9), KKT_ACC(10), KKT_ACC(11), KKT_ACC(12), KKT_ACC(13), KKT_ACC(14), KKT_ACC(15)
+            : KKT_COL(1), KKT_COL(2), KKT_COL(3), KKT_COL(4), KKT_COL(5), KKT_COL(6), KKT_COL(7), KKT_COL(8), KKT_COL(9), KKT_COL(10), KKT_COL(11), KKT_COL(12), KKT_COL(13), KKT_COL(14), KKT_COL(15), [x] "v"(acc[0]));
+        asm("s_nop 1\n" KKT_BCAST_FMAC(2, 1) KKT_BCAST_FMAC(3, 1) KKT_BCAST_FMAC(4, 1) KKT_BCAST_FMAC(5, 1) KKT_BCAST_FMAC(6, 1) KKT_BCAST_FMAC(7, 1) KKT_BCAST_FMAC(8, 1) KKT_BCAST_FMAC(9, 1) KKT_BCAST_FMAC(10, 1) KKT_BCAST_FMAC(11, 1) KKT_BCAST_FMAC(12, 1) KKT_BCAST_FMAC(13, 1) KKT_BCAST_FMAC(14, 1) KKT_BCAST_FMAC(15, 1)
+            : KKT_ACC(2), KKT_ACC(3), KKT_ACC(4), KKT_ACC(5), KKT_ACC(6), KKT_ACC(7), KKT_ACC(8), KKT_ACC(9), KKT_ACC(10), KKT_ACC(11), KKT_ACC(12), KKT_ACC(13), KKT_ACC(14), KKT_ACC(15)
+            : KKT_COL(2), KKT_COL(3), KKT_COL(4), KKT_COL(5), KKT_COL(6), KKT_COL(7), KKT_COL(8), KKT_COL(9), KKT_COL(10), KKT_COL(11), KKT_COL(12), KKT_COL(13), KKT_COL(14), KKT_COL(15), [x] "v"(acc[1]));
+        asm("s_nop 1\n" KKT_BCAST_FMAC(3, 2) KKT_BCAST_FMAC(4, 2) KKT_BCAST_FMAC(5, 2) KKT_BCAST_FMAC(6, 2) KKT_BCAST_FMAC(7, 2) KKT_BCAST_FMAC(8, 2) KKT_BCAST_FMAC(9, 2) KKT_BCAST_FMAC(10, 2) KKT_BCAST_FMAC(11, 2) KKT_BCAST_FMAC(12, 2) KKT_BCAST_FMAC(13, 2) KKT_BCAST_FMAC(14, 2) KKT_BCAST_FMAC(15, 2)
+            : KKT_ACC(3), KKT_ACC(4), KKT_ACC(5), KKT_ACC(6), KKT_ACC(7), KKT_ACC(8), KKT_ACC(9), KKT_ACC(10), KKT_ACC(11), KKT_ACC(12), KKT_ACC(13), KKT_ACC(14), KKT_ACC(15)
+            : KKT_COL(3), KKT_COL(4), KKT_COL(5), KKT_COL(6), KKT_COL(7), KKT_COL(8), KKT_COL(9), KKT_COL(10), KKT_COL(11), KKT_COL(12), KKT_COL(13), KKT_COL(14), KKT_COL(15), [x] "v"(acc[2]));
+        asm("s_nop 1\n" KKT_BCAST_FMAC(4, 3) KKT_BCAST_FMAC(5, 3) KKT_BCAST_FMAC(6, 3) KKT_BCAST_FMAC(7, 3) KKT_BCAST_FMAC(8, 3) KKT_BCAST_FMAC(9, 3) KKT_BCAST_FMAC(10, 3) KKT_BCAST_FMAC(11, 3) KKT_BCAST_FMAC(12, 3) KKT_BCAST_FMAC(13, 3) KKT_BCAST_FMAC(14, 3) KKT_BCAST_FMAC(15, 3)
+            : KKT_ACC(4), KKT_ACC(5), KKT_ACC(6), KKT_ACC(7), KKT_ACC(8), KKT_ACC(9), KKT_ACC(10), KKT_ACC(11), KKT_ACC(12), KKT_ACC(13), KKT_ACC(14), KKT_ACC(15)
+            : KKT_COL(4), KKT_COL(5), KKT_COL(6), KKT_COL(7), KKT_COL(8), KKT_COL(9), KKT_COL(10), KKT_COL(11), KKT_COL(12), KKT_COL(13), KKT_COL(14), KKT_COL(15), [x] "v"(acc[3]));
+        asm("s_nop 1\n" KKT_BCAST_FMAC(5, 4) KKT_BCAST_FMAC(6, 4) KKT_BCAST_FMAC(7, 4) KKT_BCAST_FMAC(8, 4) KKT_BCAST_FMAC(9, 4) KKT_BCAST_FMAC(10, 4) KKT_BCAST_FMAC(11, 4) KKT_BCAST_FMAC(12, 4) KKT_BCAST_FMAC(13, 4) KKT_BCAST_FMAC(14, 4) KKT_BCAST_FMAC(15, 4)
+            : KKT_ACC(5), KKT_ACC(6), KKT_ACC(7), KKT_ACC(8), KKT_ACC(9), KKT_ACC(10), KKT_ACC(11), KKT_ACC(12), KKT_ACC(13), KKT_ACC(14), KKT_ACC(15)
+            : KKT_COL(5), KKT_COL(6), KKT_COL(7), KKT_COL(8), KKT_COL(9), KKT_COL(10), KKT_COL(11), KKT_COL(12), KKT_COL(13), KKT_COL(14), KKT_COL(15), [x] "v"(acc[4]));
+        asm("s_nop 1\n" KKT_BCAST_FMAC(6, 5) KKT_BCAST_FMAC(7, 5) KKT_BCAST_FMAC(8, 5) KKT_BCAST_FMAC(9, 5) KKT_BCAST_FMAC(10, 5) KKT_BCAST_FMAC(11, 5) KKT_BCAST_FMAC(12, 5) KKT_BCAST_FMAC(13, 5) KKT_BCAST_FMAC(14, 5) KKT_BCAST_FMAC(15, 5)
+            : KKT_ACC(6), KKT_ACC(7), KKT_ACC(8), KKT_ACC(9), KKT_ACC(10), KKT_ACC(11), KKT_ACC(12), KKT_ACC(13), KKT_ACC(14), KKT_ACC(15)
+            : KKT_COL(6), KKT_COL(7), KKT_COL(8), KKT_COL(9), KKT_COL(10), KKT_COL(11), KKT_COL(12), KKT_COL(13), KKT_COL(14), KKT_COL(15), [x] "v"(acc[5]));
+        asm("s_nop 1\n" KKT_BCAST_FMAC(7, 6) KKT_BCAST_FMAC(8, 6) KKT_BCAST_FMAC(9, 6) KKT_BCAST_FMAC(10, 6) KKT_BCAST_FMAC(11, 6) KKT_BCAST_FMAC(12, 6) KKT_BCAST_FMAC(13, 6) KKT_BCAST_FMAC(14, 6) KKT_BCAST_FMAC(15, 6)
+            : KKT_ACC(7), KKT_ACC(8), KKT_ACC(9), KKT_ACC(10), KKT_ACC(11), KKT_ACC(12), KKT_ACC(13), KKT_ACC(14), KKT_ACC(15)
+            : KKT_COL(7), KKT_COL(8), KKT_COL(9), KKT_COL(10), KKT_COL(11), KKT_COL(12), KKT_COL(13), KKT_COL(14), KKT_COL(15), [x] "v"(acc[6]));
+        asm("s_nop 1\n" KKT_BCAST_FMAC(8, 7) KKT_BCAST_FMAC(9, 7) KKT_BCAST_FMAC(10, 7) KKT_BCAST_FMAC(11, 7) KKT_BCAST_FMAC(12, 7) KKT_BCAST_FMAC(13, 7) KKT_BCAST_FMAC(14, 7) KKT_BCAST_FMAC(15, 7)
+            : KKT_ACC(8), KKT_ACC(9), KKT_ACC(10), KKT_ACC(11), KKT_ACC(12), KKT_ACC(13), KKT_ACC(14), KKT_ACC(15)
+            : KKT_COL(8), KKT_COL(9), KKT_COL(10), KKT_COL(11), KKT_COL(12), KKT_COL(13), KKT_COL(14), KKT_COL(15), [x] "v"(acc[7]));
+        asm("s_nop 1\n" KKT_BCAST_FMAC(9, 8) KKT_BCAST_FMAC(10, 8) KKT_BCAST_FMAC(11, 8) KKT_BCAST_FMAC(12, 8) KKT_BCAST_FMAC(13, 8) KKT_BCAST_FMAC(14, 8) KKT_BCAST_FMAC(15, 8)
+            : KKT_ACC(9), KKT_ACC(10), KKT_ACC(11), KKT_ACC(12), KKT_ACC(13), KKT_ACC(14), KKT_ACC(15)
+            : KKT_COL(9), KKT_COL(10), KKT_COL(11), KKT_COL(12), KKT_COL(13), KKT_COL(14), KKT_COL(15), [x] "v"(acc[8]));
+        asm("s_nop 1\n" KKT_BCAST_FMAC(10, 9) KKT_BCAST_FMAC(11, 9) KKT_BCAST_FMAC(12, 9) KKT_BCAST_FMAC(13, 9) KKT_BCAST_FMAC(14, 9) KKT_BCAST_FMAC(15, 9)
+            : KKT_ACC(10), KKT_ACC(11), KKT_ACC(12), KKT_ACC(13), KKT_ACC(14), KKT_ACC(15)
+            : KKT_COL(10), KKT_COL(11), KKT_COL(12), KKT_COL(13), KKT_COL(14), KKT_COL(15), [x] "v"(acc[9]));
+        asm("s_nop 1\n" KKT_BCAST_FMAC(11, 10) KKT_BCAST_FMAC(12, 10) KKT_BCAST_FMAC(13, 10) KKT_BCAST_FMAC(14, 10) KKT_BCAST_FMAC(15, 10)
+            : KKT_ACC(11), KKT_ACC(12), KKT_ACC(13), KKT_ACC(14), KKT_ACC(15)
+            : KKT_COL(11), KKT_COL(12), KKT_COL(13), KKT_COL(14), KKT_COL(15), [x] "v"(acc[10]));
+        asm("s_nop 1\n" KKT_BCAST_FMAC(12, 11) KKT_BCAST_FMAC(13, 11) KKT_BCAST_FMAC(14, 11) KKT_BCAST_FMAC(15, 11)
+            : KKT_ACC(12), KKT_ACC(13), KKT_ACC(14), KKT_ACC(15)
+            : KKT_COL(12), KKT_COL(13), KKT_COL(14), KKT_COL(15), [x] "v"(acc[11]));
+        asm("s_nop 1\n" KKT_BCAST_FMAC(13, 12) KKT_BCAST_FMAC(14, 12) KKT_BCAST_FMAC(15, 12)
+            : KKT_ACC(13), KKT_ACC(14), KKT_ACC(15)
+            : KKT_COL(13), KKT_COL(14), KKT_COL(15), [x] "v"(acc[12]));
+        asm("s_nop 1\n" KKT_BCAST_FMAC(14, 13) KKT_BCAST_FMAC(15, 13)
+            : KKT_ACC(14), KKT_ACC(15)
+            : KKT_COL(14), KKT_COL(15), [x] "v"(acc[13]));
+        asm("s_nop 1\n" KKT_BCAST_FMAC(15, 14)
+            : KKT_ACC(15)
+            : KKT_COL(15), [x] "v"(acc[14]));
+#undef KKT_BCAST_FMAC
+#undef KKT_ACC
+#undef KKT_COL
         wave_lds_sync();  // every read of A_dd precedes the overwrite with X_dd
         // X_dd stored transposed as well: column c is contiguous
 #pragma unroll
