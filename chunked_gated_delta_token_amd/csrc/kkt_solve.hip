@@ -252,6 +252,7 @@ struct KernelArgs {
     int32_t log2_group_run;     // kChunkRoundRobin: log2 of the workgroups kept together on one XCD
     uint32_t remap_groups;      // kChunkRoundRobin: workgroups in whole rounds (the rest keep their order)
     float* g_out;               // gate-sum kernel: where the summed gate goes, or nullptr
+    int32_t split_tiles;        // host only: launch the fused op's two-wave-per-tile kernel
 };
 
 // ---------------------------------------------------------------- tile map (a1)
@@ -436,8 +437,18 @@ __device__ __forceinline__ float wave_prefix_sum(float v, int lane)
 // first-phase areas).  SHARE: after its Gram, wave 0 also writes its key
 // fragments to ex->kimg for the A21 waves, and both waves take part in the
 // barrier that makes them visible.
-template <Mode MODE, Elt IN, Elt OUT, int K, bool GATE_SUM, int CH, bool SHARE = false>
-__device__ __forceinline__ void chunk_rows(const KernelArgs& args, WaveLds& lds, int lane, int64_t tok, int L,
+// SPLIT: 0, the wave does the whole 64-token tile; 1 or 2, the first or
+// second wave of a tile split over two waves (kkt_solve_split_kernel): wave 1
+// takes block rows 0..2, wave 2 block row 3 (Gram, epilogue and diagonal
+// inverse of its own blocks, then the merge products of its rows), and they
+// exchange the diagonal inverses and X10, X21, X20 through LDS at three
+// workgroup barriers.  Every block is formed by the same operations in the
+// same order as in the one-wave tile, so the results are bit-identical.
+// blk: the diagonal-block area (lds.blk for one wave; shared by the two waves
+// of a split tile); xchg: the split tile's exchange area (else unused).
+template <Mode MODE, Elt IN, Elt OUT, int K, bool GATE_SUM, int CH, bool SHARE = false, int SPLIT = 0>
+__device__ __forceinline__ void chunk_rows(const KernelArgs& args, WaveLds& lds, float (&blk)[4][16][kBlockLd],
+                                           f32x4 (*xchg)[kWave], int lane, int64_t tok, int L,
                                            int half, Chunk128Lds* ex)
 {
     constexpr int kInBytes = EltInfo<IN>::bytes;
@@ -447,6 +458,9 @@ __device__ __forceinline__ void chunk_rows(const KernelArgs& args, WaveLds& lds,
     static_assert(K % (4 * kElemsPer16B) == 0, "K must fill whole fragments");
     static_assert(CH == 64 || (CH == 128 && MODE == Mode::Fused), "128-token chunks: fused op only");
     static_assert(!SHARE || (CH == 128 && kSteps <= 4), "shared key tile: 128-token kernel, at most 4 k-steps");
+    static_assert(SPLIT == 0 || (CH == 64 && MODE == Mode::Fused && !GATE_SUM), "split tiles: the 64-token fused op");
+    // block rows (and diagonal blocks) this wave finishes
+    auto owns = [](int i) { return SPLIT == 0 || (SPLIT == 1 ? i < 3 : i == 3); };
     const int q = lane / 16;   // lane group (k-slot group of an MFMA operand)
     const int m = lane % 16;   // row inside a 16-row block (A operand) / column (D layout)
     const int H = args.H;
@@ -725,10 +739,11 @@ __device__ __forceinline__ void chunk_rows(const KernelArgs& args, WaveLds& lds,
     // column as one contiguous row
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+        if (!owns(i)) continue;
         f32x4 v;
 #pragma unroll
         for (int r = 0; r < 4; ++r) v[r] = (4 * q + r > m) ? -A[i][i][r] : 0.0f;
-        *reinterpret_cast<f32x4*>(&lds.blk[i][m][4 * q]) = v;
+        *reinterpret_cast<f32x4*>(&blk[i][m][4 * q]) = v;
     }
     wave_lds_sync();
 
@@ -743,12 +758,15 @@ __device__ __forceinline__ void chunk_rows(const KernelArgs& args, WaveLds& lds,
     // independent, so the dependent chain is one FMA per row, and no step
     // waits on LDS.
     {
-        const int d = lane / 16;
+        // (a lane group whose block the other wave of a split tile owns
+        // repeats one of this wave's blocks and keeps its result)
+        const int d = (SPLIT == 0) ? lane / 16 : (SPLIT == 1) ? (lane / 16 < 3 ? lane / 16 : 2) : 3;
+        const bool keep = (SPLIT == 0) || (lane / 16 == d);
         const int c = lane % 16;
         float col[16];  // -A_dd[r][c]; zero for r <= c
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const f32x4 v = *reinterpret_cast<const f32x4*>(&lds.blk[d][c][4 * u]);
+            const f32x4 v = *reinterpret_cast<const f32x4*>(&blk[d][c][4 * u]);
             col[4 * u + 0] = v[0];
             col[4 * u + 1] = v[1];
             col[4 * u + 2] = v[2];
@@ -817,13 +835,16 @@ __device__ __forceinline__ void chunk_rows(const KernelArgs& args, WaveLds& lds,
 #undef KKT_COL
         wave_lds_sync();  // every read of A_dd precedes the overwrite with X_dd
         // X_dd stored transposed as well: column c is contiguous
+        if (keep) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const f32x4 v = {acc[4 * u], acc[4 * u + 1], acc[4 * u + 2], acc[4 * u + 3]};
-            *reinterpret_cast<f32x4*>(&lds.blk[d][c][4 * u]) = v;
+            for (int u = 0; u < 4; ++u) {
+                const f32x4 v = {acc[4 * u], acc[4 * u + 1], acc[4 * u + 2], acc[4 * u + 3]};
+                *reinterpret_cast<f32x4*>(&blk[d][c][4 * u]) = v;
+            }
         }
     }
     wave_lds_sync();
+    if constexpr (SPLIT != 0) __syncthreads();  // split tile: all four diagonal inverses are in blk
 
     // X_dd in both operand layouts (blk[d][col][row] = X_dd[row][col]):
     //   xa[d]: lane (q, m) holds X_dd[m][4q .. 4q+3]   (left operand)
@@ -831,9 +852,48 @@ __device__ __forceinline__ void chunk_rows(const KernelArgs& args, WaveLds& lds,
     f32x4 xa[4], xd[4];
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-        xd[d] = *reinterpret_cast<const f32x4*>(&lds.blk[d][m][4 * q]);
+        xd[d] = *reinterpret_cast<const f32x4*>(&blk[d][m][4 * q]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) xa[d][r] = lds.blk[d][4 * q + r][m];
+        for (int r = 0; r < 4; ++r) xa[d][r] = blk[d][4 * q + r][m];
+    }
+
+    if constexpr (SPLIT == 1) {
+        // block rows 0..2; X10 and X21 go to the other wave before the
+        // second barrier, X20 before the third
+        store_block_row(0, xd[0], zero4, zero4, zero4);
+        const f32x4 wt10 = mm16(A[1][0], xa[1], zero4);
+        const f32x4 wt20 = mm16(A[2][0], xa[2], zero4);
+        const f32x4 wt21 = mm16(A[2][1], xa[2], zero4);
+        const f32x4 x10 = zero4 - mm16(wt10, xd[0], zero4);
+        const f32x4 x21 = zero4 - mm16(wt21, xd[1], zero4);
+        const f32x4 p20 = mm16(wt20, xd[0], zero4);
+        xchg[0][lane] = x10;
+        xchg[1][lane] = x21;
+        __syncthreads();
+        store_block_row(1, x10, xd[1], zero4, zero4);
+        const f32x4 x20 = zero4 - mm16(wt21, x10, p20);
+        xchg[2][lane] = x20;
+        __syncthreads();
+        store_block_row(2, x20, x21, xd[2], zero4);
+        return;
+    } else if constexpr (SPLIT == 2) {
+        // block row 3
+        const f32x4 wt30 = mm16(A[3][0], xa[3], zero4);
+        const f32x4 wt31 = mm16(A[3][1], xa[3], zero4);
+        const f32x4 wt32 = mm16(A[3][2], xa[3], zero4);
+        const f32x4 x32 = zero4 - mm16(wt32, xd[2], zero4);
+        const f32x4 p31 = mm16(wt31, xd[1], zero4);
+        f32x4 p30 = mm16(wt30, xd[0], zero4);
+        __syncthreads();
+        const f32x4 x10 = xchg[0][lane];
+        const f32x4 x21 = xchg[1][lane];
+        p30 = mm16(wt31, x10, p30);
+        const f32x4 x31 = zero4 - mm16(wt32, x21, p31);
+        __syncthreads();
+        const f32x4 x20 = xchg[2][lane];
+        const f32x4 x30 = zero4 - mm16(wt32, x20, p30);
+        store_block_row(3, x30, x31, x32, xd[3]);
+        return;
     }
 
     // block row 0 is final already
@@ -900,7 +960,39 @@ __device__ __forceinline__ void run_tile(const KernelArgs& args, WaveLds* lds_al
     const int h = (int)(tile_id % (uint32_t)H);
     const Tile tile = chunk_tile<kChunk>(args, tile_id / (uint32_t)H, lane);
     if (tile.len <= 0) return;  // wave-uniform
-    chunk_rows<MODE, IN, OUT, K, GATE_SUM, kChunk>(args, lds_all[wave], lane, tile.row0 * H + h, tile.len, 0, nullptr);
+    chunk_rows<MODE, IN, OUT, K, GATE_SUM, kChunk>(args, lds_all[wave], lds_all[wave].blk, nullptr, lane,
+                                                   tile.row0 * H + h, tile.len, 0, nullptr);
+}
+
+// LDS of a 64-token tile split over two waves: their own gate arrays and
+// store stages, the shared diagonal blocks and the exchanged X10, X21, X20.
+struct SplitLds {
+    WaveLds wave[2];
+    float blk[4][16][kBlockLd];
+    f32x4 xchg[3][kWave];
+};
+
+// One 64-token chunk per two-wave workgroup (the fused op on small grids,
+// where a tile's latency, not the chip's throughput, sets the time).
+template <Elt IN, Elt OUT, int K>
+__device__ __forceinline__ void run_split_tile(const KernelArgs& args, SplitLds& lds)
+{
+    const int lane = threadIdx.x % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const uint32_t tile_id = workgroup_order(args);
+    if (tile_id >= (uint32_t)args.n_tiles) return;  // workgroup-uniform
+    const int H = args.H;
+    const int h = (int)(tile_id % (uint32_t)H);
+    const Tile tile = chunk_tile<kChunk>(args, tile_id / (uint32_t)H, lane);
+    if (tile.len <= 0) return;  // workgroup-uniform
+    const int64_t tok = tile.row0 * H + h;
+    if (wave == 0) {
+        chunk_rows<Mode::Fused, IN, OUT, K, false, kChunk, false, 1>(args, lds.wave[0], lds.blk, lds.xchg, lane, tok,
+                                                                     tile.len, 0, nullptr);
+    } else {
+        chunk_rows<Mode::Fused, IN, OUT, K, false, kChunk, false, 2>(args, lds.wave[1], lds.blk, lds.xchg, lane, tok,
+                                                                     tile.len, 0, nullptr);
+    }
 }
 
 // 128-token chunks: the 64x64 block A21 of A (rows 64..127, columns 0..63)
@@ -1074,6 +1166,15 @@ void kkt_solve_kernel(const KernelArgs args)
     run_tile<Mode::Fused, IN, OUT, K>(args, lds_all);
 }
 
+// The fused op with each 64-token tile split over a two-wave workgroup.
+template <Elt IN, Elt OUT, int K>
+__global__ __launch_bounds__(kWave * 2)
+void kkt_solve_split_kernel(const KernelArgs args)
+{
+    __shared__ SplitLds lds;
+    run_split_tile<IN, OUT, K>(args, lds);
+}
+
 template <Elt IN, Elt OUT, int K>
 __global__ __launch_bounds__(kWave * kWavesPerGroup)
 void kkt_solve_gate_cumsum_kernel(const KernelArgs args)
@@ -1147,8 +1248,8 @@ void kkt_solve128_kernel(const KernelArgs args)
     constexpr int kSteps = K / (4 * (16 / kInBytes));
     static_assert(STAGE == kKeysGlobal || kSteps <= 4, "the LDS key image holds at most 4 k-steps");
     if (wave < 2) {
-        chunk_rows<Mode::Fused, IN, OUT, K, GATE_SUM, 2 * kChunk, STAGE == kKeysShared>(args, ex.half[wave], lane, tok,
-                                                                                        L, wave, &ex);
+        chunk_rows<Mode::Fused, IN, OUT, K, GATE_SUM, 2 * kChunk, STAGE == kKeysShared>(
+            args, ex.half[wave], ex.half[wave].blk, nullptr, lane, tok, L, wave, &ex);
     } else {
         const int w2 = wave - 2;
         f32x4 acc[2][4];
@@ -1333,9 +1434,9 @@ kkt_status_t validate_cu_seqlens(const int32_t* cu, int64_t num_seqs, int64_t T,
     return KKT_OK;
 }
 
-hipError_t launch(void (*kernel)(KernelArgs), const KernelArgs& a, hipStream_t stream)
+hipError_t launch(void (*kernel)(KernelArgs), const KernelArgs& a, hipStream_t stream, int waves = kWavesPerGroup)
 {
-    hipLaunchKernelGGL(kernel, dim3(a.n_groups), dim3(kWave * kWavesPerGroup), 0, stream, a);
+    hipLaunchKernelGGL(kernel, dim3(a.n_groups), dim3(kWave * waves), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -1347,6 +1448,12 @@ hipError_t launch_fused(int64_t K, const KernelArgs& a, hipStream_t stream)
         case 64: return launch(kkt_solve_gate_cumsum_kernel<IN, OUT, 64>, a, stream);
         case 128: return launch(kkt_solve_gate_cumsum_kernel<IN, OUT, 128>, a, stream);
         default: return launch(kkt_solve_gate_cumsum_kernel<IN, OUT, 256>, a, stream);
+        }
+    } else if (a.split_tiles) {
+        switch (K) {
+        case 64: return launch(kkt_solve_split_kernel<IN, OUT, 64>, a, stream, 2);
+        case 128: return launch(kkt_solve_split_kernel<IN, OUT, 128>, a, stream, 2);
+        default: return launch(kkt_solve_split_kernel<IN, OUT, 256>, a, stream, 2);
         }
     } else {
         switch (K) {
@@ -1412,6 +1519,20 @@ constexpr int64_t kRemapMaxGroups = 1024;
 #define KKT_LARGE_GRID_ORDER kChunkRoundRobin
 #endif
 
+// Grids of up to this many 64-token tiles of the fused op (1.5 per CU of
+// the chip) run one tile per two-wave workgroup: there the time is a tile's
+// latency after its keys arrive, which the split shortens (128 to 256 tiles:
+// 22-30% less time), rather than the chip's throughput.  From about 512
+// tiles up the split's extra key reads, barriers and second wave per SIMD
+// cost more than the shorter tail saves (1024 tiles: 11-16% more time).
+// KKT_SPLIT_TILES overrides the bound (0: never split).
+constexpr int64_t kSplitMaxTiles = 384;
+int64_t split_max_tiles()
+{
+    const char* v = getenv("KKT_SPLIT_TILES");
+    return (v != nullptr && v[0] != '\0') ? strtoll(v, nullptr, 10) : kSplitMaxTiles;
+}
+
 // Checks shared by every entry point and the launch geometry.  in_row_bytes
 // and out_row_bytes are the strides between consecutive tokens of one head;
 // chunk is 64 (one tile per wave) or 128 (one tile per workgroup).
@@ -1419,7 +1540,7 @@ constexpr int64_t kRemapMaxGroups = 1024;
 kkt_status_t setup(KernelArgs& a, const void* in, const float* g, const float* beta,
                    const int32_t* cu_seqlens, int64_t num_seqs, int64_t B, int64_t T, int64_t H,
                    int64_t in_row_bytes, int64_t out_row_bytes, void* out, hipStream_t stream,
-                   int64_t chunk = kChunk)
+                   int64_t chunk = kChunk, bool allow_split = false)
 {
     if (in == nullptr || out == nullptr) return fail(KKT_ERR_INVALID_ARGUMENT, "input and output must not be NULL");
     // the kernel moves the row tensors in 16-byte vectors, g / beta / cu_seqlens in 4-byte words
@@ -1438,7 +1559,8 @@ kkt_status_t setup(KernelArgs& a, const void* in, const float* g, const float* b
     // Packed sequences: at most floor(T/chunk) + num_seqs chunks; surplus tiles exit.
     const int64_t n_chunks = (cu_seqlens == nullptr) ? B * chunks_per_row : T / chunk + num_seqs;
     const int64_t n_tiles = n_chunks * H;
-    const int64_t tiles_per_group = (chunk == kChunk) ? kWavesPerGroup : 1;
+    const bool split = allow_split && chunk == kChunk && n_tiles <= split_max_tiles();
+    const int64_t tiles_per_group = (chunk == kChunk && !split) ? kWavesPerGroup : 1;
     if (n_tiles >= (1LL << 31) - kWavesPerGroup || num_seqs >= (1LL << 31) - 1) {
         return fail(KKT_ERR_UNSUPPORTED, "problem too large for one launch");
     }
@@ -1475,6 +1597,7 @@ kkt_status_t setup(KernelArgs& a, const void* in, const float* g, const float* b
     a.log2_group_run = lg;
     a.remap_groups = (uint32_t)((groups >> (lg + 3)) << (lg + 3));
     a.g_out = nullptr;
+    a.split_tiles = split ? 1 : 0;
     return KKT_OK;
 }
 
@@ -1506,7 +1629,7 @@ extern "C" kkt_status_t kkt_solve(const void* k, const float* g, const float* be
     if (T == 0) return KKT_OK;
     KernelArgs a;
     st = setup(a, k, g, beta, cu_seqlens, num_seqs, B, T, H, H * K * dtype_bytes(in_dtype),
-               H * chunk_size * dtype_bytes(out_dtype), out, stream, chunk_size);
+               H * chunk_size * dtype_bytes(out_dtype), out, stream, chunk_size, true);
     if (st != KKT_OK) return st;
 
     hipError_t e;

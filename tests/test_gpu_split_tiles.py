@@ -1,0 +1,112 @@
+"""GPU: the fused op's two launch forms give the same bits.
+
+Small grids run each 64-token tile on a two-wave workgroup (the first wave
+finishes block rows 0..2, the second block row 3, exchanging the diagonal
+inverses and X10, X21, X20 through LDS); large grids run one tile per wave.
+Both form every block by the same operations in the same order, so their
+outputs must be bit-identical.  KKT_SPLIT_TILES (read by the library on every
+call) forces one form or the other on the same inputs; each case is also
+checked against the fp64 oracle.
+"""
+from __future__ import annotations
+
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from chunked_gated_delta_token_amd import workloads as W
+from tests._compare import compare
+from tests._gpu_util import TORCH_DT, from_device, load_kkt, say, to_device
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def kkt():
+    return load_kkt()
+
+
+def run_form(kkt, t, out_dtype: str, split: bool) -> np.ndarray:
+    k, g, b, cu = t
+    B, T, H, _ = k.shape
+    old = os.environ.get("KKT_SPLIT_TILES")
+    os.environ["KKT_SPLIT_TILES"] = "1000000000" if split else "0"
+    try:
+        out = torch.full((B, T, H, 64), float("nan"), dtype=TORCH_DT[out_dtype], device=k.device)
+        kkt.kkt_solve(k, g, b, cu, output_dtype=TORCH_DT[out_dtype], out=out)
+        torch.cuda.synchronize()
+    finally:
+        if old is None:
+            del os.environ["KKT_SPLIT_TILES"]
+        else:
+            os.environ["KKT_SPLIT_TILES"] = old
+    return from_device(out, out_dtype)
+
+
+def both_forms(kkt, inp: W.Inputs, out_dtype: str, label: str):
+    w = inp.workload
+    say(f"[case] split vs one-wave tiles, {label}: B={w.B} T={w.T} H={w.H} K={w.K} in={w.in_dtype} "
+        f"out={out_dtype} g={inp.g is not None} beta={inp.beta is not None} "
+        f"seqs={0 if inp.cu_seqlens is None else len(inp.cu_seqlens) - 1}")
+    t = to_device(inp)
+    one = run_form(kkt, t, out_dtype, split=False)
+    two = run_form(kkt, t, out_dtype, split=True)
+    view = np.uint32 if out_dtype == "f32" else np.uint16
+    assert np.array_equal(one.view(view), two.view(view)), label
+    ref = oracle.kkt_solve_ref(inp.k64(), inp.g, inp.beta, inp.cu_seqlens)
+    stats = compare(two, ref, out_dtype, inp.cu_seqlens, label)
+    say("[ok] " + json.dumps(stats))
+
+
+@pytest.mark.parametrize("name", list(W.WORKLOADS))
+def test_split_tiles_workloads(kkt, name):
+    """Every workload at full size (the large one included, forced split)."""
+    inp = W.generate(name)
+    both_forms(kkt, inp, inp.workload.out_dtype, name)
+
+
+@pytest.mark.parametrize("in_dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("K", [64, 256])
+def test_split_tiles_dtypes_and_K(kkt, in_dtype, out_dtype, K):
+    inp = W.generate("T256_H8_bf16_f32", B=2, T=333, H=3, K=K, in_dtype=in_dtype, seed=4100 + K)
+    both_forms(kkt, inp, out_dtype, f"{in_dtype}->{out_dtype} K={K}")
+
+
+@pytest.mark.parametrize("gate,beta", [(False, False), (True, False), (False, True)])
+def test_split_tiles_without_gate_or_beta(kkt, gate, beta):
+    inp = W.generate("T256_H8_bf16_f32", B=1, T=1000, H=5, seed=4200, gate=gate, beta=beta)
+    both_forms(kkt, inp, "f32", f"gate={gate} beta={beta}")
+
+
+@pytest.mark.parametrize("T", [1, 2, 17, 48, 63, 64, 65, 130])
+def test_split_tiles_short_chunks(kkt, T):
+    """Partial chunks: one or both waves' rows past the chunk's end."""
+    inp = W.generate("T256_H8_bf16_f32", B=3, T=T, H=2, seed=4300 + T)
+    both_forms(kkt, inp, "f32", f"T={T}")
+
+
+def test_split_tiles_gate_beyond_clamp(kkt):
+    """Within-chunk gate differences beyond +-50: the clamped per-element
+    epilogue instead of the factored one."""
+    inp = W.generate("T256_H8_bf16_f32", T=256, H=4, seed=4400)
+    rng = np.random.default_rng(4401)
+    inc = -rng.uniform(0.0, 3.0, inp.g.shape)
+    g = np.empty_like(inc)
+    for t0 in range(0, 256, 64):
+        g[:, t0:t0 + 64] = np.cumsum(inc[:, t0:t0 + 64], axis=1)
+    inp.g = g.astype(np.float32)
+    both_forms(kkt, inp, "f32", "gate spread ~ -96")
+
+
+def test_split_tiles_packed_short_sequences(kkt):
+    """Packed sequences with empty and one-token members."""
+    lens = np.random.default_rng(4500).integers(0, 150, 40)
+    lens[[3, 17]] = 0
+    lens[[5, 30]] = 1
+    inp = W.generate("T256_H8_bf16_f32", lengths=lens.tolist(), H=3, seed=4501)
+    both_forms(kkt, inp, "f32", "packed 40 short sequences")
