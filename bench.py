@@ -50,6 +50,24 @@ ENTRY = {"fused": "kkt_solve", "scaled_dot": "kkt_scaled_dot", "solve_tril": "kk
          "gate_cumsum128": "kkt_solve_gate_cumsum128"}
 
 
+SPLIT_MAX_TILES = 256          # the library's bound for two-wave tiles of the fused op (KKT_SPLIT_TILES overrides it)
+
+
+def kernel_name(key: str, workload: str) -> str:
+    """The kernel an op key launches on a workload: the fused op at 64-token
+    chunks takes its two-wave-per-tile form on grids of up to SPLIT_MAX_TILES
+    chunk-head tiles (the library's grid counts T/64 + num_seqs chunks for
+    packed sequences)."""
+    from chunked_gated_delta_token_amd import workloads as W
+    if key == "fused":
+        w = W.WORKLOADS[workload]
+        grid = w.H * ((w.T // 64 + w.n_seqs) if w.n_seqs else w.B * (-(-w.T // 64)))
+        env = os.environ.get("KKT_SPLIT_TILES", "")
+        if grid <= (int(env) if env else SPLIT_MAX_TILES):
+            return "kkt_solve_split_kernel"
+    return KERNELS[key]
+
+
 def op_key(op: str, chunk: int) -> str:
     return op + "128" if (op in ("fused", "gate_cumsum") and chunk == 128) else op
 
@@ -219,7 +237,7 @@ def summarize_traffic(dirs, copy_bytes: int, op: str, workload: str, chunk: int 
     if op == "chain":
         raise SystemExit("traffic is summarized per kernel: use --op fused, gate_cumsum, scaled_dot or solve_tril")
     key = op_key(op, chunk)
-    kname = KERNELS[key]
+    kname = kernel_name(key, workload)
     op_fetch = statistics.median(_counter_values(dirs[0], "FETCH_SIZE", kname))
     op_write = statistics.median(_counter_values(dirs[1], "WRITE_SIZE", kname))
     cp_fetch = statistics.median(_counter_values(dirs[2], "FETCH_SIZE", "copy"))
@@ -271,7 +289,7 @@ def summarize_mfma(directory: str, op: str, workload: str, chunk: int = 64):
     flop) per launch, medians over the launches."""
     import statistics
     key = op_key(op, chunk)
-    kname = KERNELS[key]
+    kname = kernel_name(key, workload)
     med = {c: statistics.median(_counter_values(directory, c, kname)) for c in MFMA_COUNTERS}
     sel = f"--op {op} --workload {workload}" + (f" --chunk {chunk}" if chunk != 64 else "")
     lines = [
@@ -325,7 +343,7 @@ def summarize_trace(directory: str, op: str, workload: str, run_log: str = None,
     if op == "chain":
         raise SystemExit("kernel traces are summarized per kernel: use --op fused, gate_cumsum, scaled_dot or solve_tril")
     key = op_key(op, chunk)
-    kname = KERNELS[key]
+    kname = kernel_name(key, workload)
     stats = [r for path in glob.glob(os.path.join(directory, "**", "*kernel_stats.csv"), recursive=True)
              for r in csv.DictReader(open(path, newline="")) if f"::{kname}<" in r["Name"]]
     if len(stats) != 1:
@@ -639,7 +657,8 @@ def main():
                    "algorithmic_bytes": nbytes, "buffer_sets": R, "timing": args.timing,
                    "chunks_per_s": round(n_tiles / (ms_per_step * 1e-3), 1)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": KERNELS[key],
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": KERNELS[key] if op == "chain" else kernel_name(key, name),
                      "event_ms_per_step": round(ev_ms, 6), "launches_per_step": len(calls[0]),
                      "kernel_source_sha256_16": digest},
     }

@@ -438,12 +438,13 @@ __device__ __forceinline__ float wave_prefix_sum(float v, int lane)
 // fragments to ex->kimg for the A21 waves, and both waves take part in the
 // barrier that makes them visible.
 // SPLIT: 0, the wave does the whole 64-token tile; 1 or 2, the first or
-// second wave of a tile split over two waves (kkt_solve_split_kernel): wave 1
-// takes block rows 0..2, wave 2 block row 3 (Gram, epilogue and diagonal
-// inverse of its own blocks, then the merge products of its rows), and they
-// exchange the diagonal inverses and X10, X21, X20 through LDS at three
-// workgroup barriers.  Every block is formed by the same operations in the
-// same order as in the one-wave tile, so the results are bit-identical.
+// second wave of a tile split over two waves (kkt_solve_split_kernel).  The
+// first wave forms the diagonal blocks and block rows 1 and 2 of A, inverts
+// all four diagonal blocks and finishes block rows 0..2; the second forms
+// A30, A31, A32 meanwhile and finishes block row 3.  They exchange the
+// diagonal inverses and X10, X21, X20 through LDS at three workgroup
+// barriers.  Every block is formed by the same operations in the same order
+// as in the one-wave tile, so the results are bit-identical.
 // blk: the diagonal-block area (lds.blk for one wave; shared by the two waves
 // of a split tile); xchg: the split tile's exchange area (else unused).
 template <Mode MODE, Elt IN, Elt OUT, int K, bool GATE_SUM, int CH, bool SHARE = false, int SPLIT = 0>
@@ -459,8 +460,9 @@ __device__ __forceinline__ void chunk_rows(const KernelArgs& args, WaveLds& lds,
     static_assert(CH == 64 || (CH == 128 && MODE == Mode::Fused), "128-token chunks: fused op only");
     static_assert(!SHARE || (CH == 128 && kSteps <= 4), "shared key tile: 128-token kernel, at most 4 k-steps");
     static_assert(SPLIT == 0 || (CH == 64 && MODE == Mode::Fused && !GATE_SUM), "split tiles: the 64-token fused op");
-    // block rows (and diagonal blocks) this wave finishes
-    auto owns = [](int i) { return SPLIT == 0 || (SPLIT == 1 ? i < 3 : i == 3); };
+    // diagonal blocks this wave inverts (the first wave of a split tile
+    // inverts all four, while the second forms its row's other blocks)
+    auto owns = [](int) { return SPLIT != 2; };
     const int q = lane / 16;   // lane group (k-slot group of an MFMA operand)
     const int m = lane % 16;   // row inside a 16-row block (A operand) / column (D layout)
     const int H = args.H;
@@ -757,11 +759,8 @@ __device__ __forceinline__ void chunk_rows(const KernelArgs& args, WaveLds& lds,
     // lanes of one block) feeds straight into the FMA.  A step's updates are
     // independent, so the dependent chain is one FMA per row, and no step
     // waits on LDS.
-    {
-        // (a lane group whose block the other wave of a split tile owns
-        // repeats one of this wave's blocks and keeps its result)
-        const int d = (SPLIT == 0) ? lane / 16 : (SPLIT == 1) ? (lane / 16 < 3 ? lane / 16 : 2) : 3;
-        const bool keep = (SPLIT == 0) || (lane / 16 == d);
+    if constexpr (SPLIT != 2) {
+        const int d = lane / 16;
         const int c = lane % 16;
         float col[16];  // -A_dd[r][c]; zero for r <= c
 #pragma unroll
@@ -835,12 +834,10 @@ __device__ __forceinline__ void chunk_rows(const KernelArgs& args, WaveLds& lds,
 #undef KKT_COL
         wave_lds_sync();  // every read of A_dd precedes the overwrite with X_dd
         // X_dd stored transposed as well: column c is contiguous
-        if (keep) {
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const f32x4 v = {acc[4 * u], acc[4 * u + 1], acc[4 * u + 2], acc[4 * u + 3]};
-                *reinterpret_cast<f32x4*>(&blk[d][c][4 * u]) = v;
-            }
+        for (int u = 0; u < 4; ++u) {
+            const f32x4 v = {acc[4 * u], acc[4 * u + 1], acc[4 * u + 2], acc[4 * u + 3]};
+            *reinterpret_cast<f32x4*>(&blk[d][c][4 * u]) = v;
         }
     }
     wave_lds_sync();
@@ -1519,14 +1516,14 @@ constexpr int64_t kRemapMaxGroups = 1024;
 #define KKT_LARGE_GRID_ORDER kChunkRoundRobin
 #endif
 
-// Grids of up to this many 64-token tiles of the fused op (1.5 per CU of
+// Grids of up to this many 64-token tiles of the fused op (one per CU of
 // the chip) run one tile per two-wave workgroup: there the time is a tile's
 // latency after its keys arrive, which the split shortens (128 to 256 tiles:
-// 22-30% less time), rather than the chip's throughput.  From about 512
+// 21-33% less time), rather than the chip's throughput.  From about 384
 // tiles up the split's extra key reads, barriers and second wave per SIMD
-// cost more than the shorter tail saves (1024 tiles: 11-16% more time).
-// KKT_SPLIT_TILES overrides the bound (0: never split).
-constexpr int64_t kSplitMaxTiles = 384;
+// cost as much as the shorter tail saves or more (1024 tiles: 13-25% more
+// time).  KKT_SPLIT_TILES overrides the bound (0: never split).
+constexpr int64_t kSplitMaxTiles = 256;
 int64_t split_max_tiles()
 {
     const char* v = getenv("KKT_SPLIT_TILES");

@@ -93,10 +93,10 @@ typedef enum {
  * Alignment: k and out 16-byte aligned; g, beta and cu_seqlens 4-byte aligned
  * (KKT_ERR_INVALID_ARGUMENT otherwise).
  *
- * Launch form (chunk_size 64): grids of up to 384 chunk-head tiles run each
+ * Launch form (chunk_size 64): grids of up to 256 chunk-head tiles run each
  * tile on two waves, larger grids one tile per wave; both give bit-identical
  * results.  The environment variable KKT_SPLIT_TILES, read on every call,
- * replaces the 384 (0: always one wave per tile).
+ * replaces the 256 (0: always one wave per tile).
  *
  * All pointers are owned by the caller; the library allocates nothing and
  * keeps no pointer after the call returns.  The call is asynchronous: it

@@ -88,3 +88,19 @@ def test_gpus_above_one_exit_with_a_message(monkeypatch, capsys):
         bench.main()
     assert e.value.code == 2
     assert "one GPU" in capsys.readouterr().err
+
+
+def test_kernel_name_follows_the_launch_form(monkeypatch):
+    """Small fused grids name the two-wave kernel, the rest one wave per tile;
+    KKT_SPLIT_TILES moves the bound as it does in the library."""
+    monkeypatch.delenv("KKT_SPLIT_TILES", raising=False)
+    assert bench.kernel_name("fused", "T256_H8_bf16_f32") == "kkt_solve_split_kernel"      # 32 tiles
+    assert bench.kernel_name("fused", "T2000_H8_bf16_bf16") == "kkt_solve_split_kernel"    # 256 tiles
+    assert bench.kernel_name("fused", "T8192_H8_bf16_f32") == "kkt_solve_kernel"           # 1024 tiles
+    assert bench.kernel_name("fused", "varlen12_T16384_H7_f32_f32") == "kkt_solve_kernel"  # 7 * (256 + 12)
+    assert bench.kernel_name("fused128", "T256_H8_bf16_f32") == "kkt_solve128_kernel"
+    assert bench.kernel_name("gate_cumsum", "T256_H8_bf16_f32") == "kkt_solve_gate_cumsum_kernel"
+    monkeypatch.setenv("KKT_SPLIT_TILES", "0")
+    assert bench.kernel_name("fused", "T256_H8_bf16_f32") == "kkt_solve_kernel"
+    monkeypatch.setenv("KKT_SPLIT_TILES", "1024")
+    assert bench.kernel_name("fused", "T8192_H8_bf16_f32") == "kkt_solve_split_kernel"
