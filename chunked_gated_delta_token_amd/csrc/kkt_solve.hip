@@ -252,7 +252,7 @@ struct KernelArgs {
     int32_t log2_group_run;     // kChunkRoundRobin: log2 of the workgroups kept together on one XCD
     uint32_t remap_groups;      // kChunkRoundRobin: workgroups in whole rounds (the rest keep their order)
     float* g_out;               // gate-sum kernel: where the summed gate goes, or nullptr
-    int32_t split_tiles;        // host only: launch the fused op's two-wave-per-tile kernel
+    int32_t split_tiles;        // host only: launch the fused op's two-wave-per-tile form
 };
 
 // ---------------------------------------------------------------- tile map (a1)
@@ -459,7 +459,7 @@ __device__ __forceinline__ void chunk_rows(const KernelArgs& args, WaveLds& lds,
     static_assert(K % (4 * kElemsPer16B) == 0, "K must fill whole fragments");
     static_assert(CH == 64 || (CH == 128 && MODE == Mode::Fused), "128-token chunks: fused op only");
     static_assert(!SHARE || (CH == 128 && kSteps <= 4), "shared key tile: 128-token kernel, at most 4 k-steps");
-    static_assert(SPLIT == 0 || (CH == 64 && MODE == Mode::Fused && !GATE_SUM), "split tiles: the 64-token fused op");
+    static_assert(SPLIT == 0 || (CH == 64 && MODE == Mode::Fused), "split tiles: the 64-token fused op");
     // diagonal blocks this wave inverts (the first wave of a split tile
     // inverts all four, while the second forms its row's other blocks)
     auto owns = [](int) { return SPLIT != 2; };
@@ -474,6 +474,11 @@ __device__ __forceinline__ void chunk_rows(const KernelArgs& args, WaveLds& lds,
     const __amdgpu_buffer_rsrc_t o_rsrc = make_rsrc(
         static_cast<char*>(args.out) + tok * (int64_t)(CH * kOutBytes),
         (uint32_t)(L - 1) * args.o_row_bytes + CH * kOutBytes);
+
+    // split tile, GATE_SUM: the summed gate of row `lane`, written to g_out by
+    // the first wave once the second has read the decays (g_out may be g)
+    float g_sum = 0.0f;
+    (void)g_sum;
 
     // The 10 lower 16x16 blocks of A, result layout: A[i][j] lane (q, n)
     // holds A_ij[4q .. 4q+3][n] (rows 16i + 4q + r, column 16j + n).  The
@@ -554,11 +559,12 @@ __device__ __forceinline__ void chunk_rows(const KernelArgs& args, WaveLds& lds,
                     const float total = __shfl(wave_prefix_sum(g_first, lane), kWave - 1, kWave);
                     gv = total + gv;
                 }
-            } else if (args.g_out != nullptr) {
+            } else if (args.g_out != nullptr && SPLIT == 0) {
                 const uint32_t span = (uint32_t)(L - 1) * (uint32_t)H * 4u + 4u;
                 __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, gv), make_rsrc(args.g_out + tok, span),
                                                       (uint32_t)lane * (uint32_t)H * 4u, 0, 0);
             }
+            g_sum = gv;
         }
 
         // ---- a5, first part: the row and column scales of the epilogue.
@@ -842,6 +848,14 @@ __device__ __forceinline__ void chunk_rows(const KernelArgs& args, WaveLds& lds,
     }
     wave_lds_sync();
     if constexpr (SPLIT != 0) __syncthreads();  // split tile: all four diagonal inverses are in blk
+    if constexpr (GATE_SUM && SPLIT == 1) {
+        // both waves loaded the decays before this barrier
+        if (args.g != nullptr && args.g_out != nullptr) {
+            const uint32_t span = (uint32_t)(L - 1) * (uint32_t)H * 4u + 4u;
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, g_sum), make_rsrc(args.g_out + tok, span),
+                                                  (uint32_t)lane * (uint32_t)H * 4u, 0, 0);
+        }
+    }
 
     // X_dd in both operand layouts (blk[d][col][row] = X_dd[row][col]):
     //   xa[d]: lane (q, m) holds X_dd[m][4q .. 4q+3]   (left operand)
@@ -970,8 +984,9 @@ struct SplitLds {
 };
 
 // One 64-token chunk per two-wave workgroup (the fused op on small grids,
-// where a tile's latency, not the chip's throughput, sets the time).
-template <Elt IN, Elt OUT, int K>
+// where a tile's latency, not the chip's throughput, sets the time).  Both
+// waves sum the gate of a GATE_SUM tile, with the same scan.
+template <Elt IN, Elt OUT, int K, bool GATE_SUM = false>
 __device__ __forceinline__ void run_split_tile(const KernelArgs& args, SplitLds& lds)
 {
     const int lane = threadIdx.x % kWave;
@@ -984,11 +999,11 @@ __device__ __forceinline__ void run_split_tile(const KernelArgs& args, SplitLds&
     if (tile.len <= 0) return;  // workgroup-uniform
     const int64_t tok = tile.row0 * H + h;
     if (wave == 0) {
-        chunk_rows<Mode::Fused, IN, OUT, K, false, kChunk, false, 1>(args, lds.wave[0], lds.blk, lds.xchg, lane, tok,
-                                                                     tile.len, 0, nullptr);
+        chunk_rows<Mode::Fused, IN, OUT, K, GATE_SUM, kChunk, false, 1>(args, lds.wave[0], lds.blk, lds.xchg, lane,
+                                                                        tok, tile.len, 0, nullptr);
     } else {
-        chunk_rows<Mode::Fused, IN, OUT, K, false, kChunk, false, 2>(args, lds.wave[1], lds.blk, lds.xchg, lane, tok,
-                                                                     tile.len, 0, nullptr);
+        chunk_rows<Mode::Fused, IN, OUT, K, GATE_SUM, kChunk, false, 2>(args, lds.wave[1], lds.blk, lds.xchg, lane,
+                                                                        tok, tile.len, 0, nullptr);
     }
 }
 
@@ -1178,6 +1193,14 @@ void kkt_solve_gate_cumsum_kernel(const KernelArgs args)
 {
     __shared__ WaveLds lds_all[kWavesPerGroup];
     run_tile<Mode::Fused, IN, OUT, K, true>(args, lds_all);
+}
+
+template <Elt IN, Elt OUT, int K>
+__global__ __launch_bounds__(kWave * 2)
+void kkt_solve_gate_cumsum_split_kernel(const KernelArgs args)
+{
+    __shared__ SplitLds lds;
+    run_split_tile<IN, OUT, K, true>(args, lds);
 }
 
 template <Elt IN, int K>
@@ -1441,6 +1464,13 @@ template <Elt IN, Elt OUT, bool GATE_SUM>
 hipError_t launch_fused(int64_t K, const KernelArgs& a, hipStream_t stream)
 {
     if constexpr (GATE_SUM) {
+        if (a.split_tiles) {
+            switch (K) {
+            case 64: return launch(kkt_solve_gate_cumsum_split_kernel<IN, OUT, 64>, a, stream, 2);
+            case 128: return launch(kkt_solve_gate_cumsum_split_kernel<IN, OUT, 128>, a, stream, 2);
+            default: return launch(kkt_solve_gate_cumsum_split_kernel<IN, OUT, 256>, a, stream, 2);
+            }
+        }
         switch (K) {
         case 64: return launch(kkt_solve_gate_cumsum_kernel<IN, OUT, 64>, a, stream);
         case 128: return launch(kkt_solve_gate_cumsum_kernel<IN, OUT, 128>, a, stream);
@@ -1655,7 +1685,7 @@ extern "C" kkt_status_t kkt_solve_gate_cumsum(const void* k, const float* g_deca
     if ((reinterpret_cast<uintptr_t>(g_out) & 3u) != 0) return fail(KKT_ERR_INVALID_ARGUMENT, "g_out must be 4-byte aligned");
     KernelArgs a;
     st = setup(a, k, g_decay, beta, cu_seqlens, num_seqs, B, T, H, H * K * dtype_bytes(in_dtype),
-               H * chunk_size * dtype_bytes(out_dtype), out, stream, chunk_size);
+               H * chunk_size * dtype_bytes(out_dtype), out, stream, chunk_size, true);
     if (st != KKT_OK) return st;
     a.g_out = g_out;
 

@@ -132,8 +132,8 @@ kkt_status_t kkt_solve(const void* k, const float* g, const float* beta,
  *   half's total (7 levels).  Its result differs from a left-to-right sum by
  *   rounding only.  kkt_solve(k, g_out, ...) with the same chunk_size on the
  *   g_out this call wrote gives bit-identical output.  Everything else
- *   (arguments, chunk_size 64 or 128, alignment, errors) as for kkt_solve;
- *   g_out must be 4-byte aligned.
+ *   (arguments, chunk_size 64 or 128, alignment, errors, launch form) as for
+ *   kkt_solve; g_out must be 4-byte aligned.
  */
 kkt_status_t kkt_solve_gate_cumsum(const void* k, const float* g_decay, const float* beta,
                                    const int32_t* cu_seqlens, int64_t num_seqs,

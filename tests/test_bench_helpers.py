@@ -99,7 +99,9 @@ def test_kernel_name_follows_the_launch_form(monkeypatch):
     assert bench.kernel_name("fused", "T8192_H8_bf16_f32") == "kkt_solve_kernel"           # 1024 tiles
     assert bench.kernel_name("fused", "varlen12_T16384_H7_f32_f32") == "kkt_solve_kernel"  # 7 * (256 + 12)
     assert bench.kernel_name("fused128", "T256_H8_bf16_f32") == "kkt_solve128_kernel"
-    assert bench.kernel_name("gate_cumsum", "T256_H8_bf16_f32") == "kkt_solve_gate_cumsum_kernel"
+    assert bench.kernel_name("gate_cumsum", "T256_H8_bf16_f32") == "kkt_solve_gate_cumsum_split_kernel"
+    assert bench.kernel_name("gate_cumsum", "T8192_H8_bf16_f32") == "kkt_solve_gate_cumsum_kernel"
+    assert bench.kernel_name("gate_cumsum128", "T256_H8_bf16_f32") == "kkt_solve128_kernel"
     monkeypatch.setenv("KKT_SPLIT_TILES", "0")
     assert bench.kernel_name("fused", "T256_H8_bf16_f32") == "kkt_solve_kernel"
     monkeypatch.setenv("KKT_SPLIT_TILES", "1024")

@@ -110,3 +110,52 @@ def test_split_tiles_packed_short_sequences(kkt):
     lens[[5, 30]] = 1
     inp = W.generate("T256_H8_bf16_f32", lengths=lens.tolist(), H=3, seed=4501)
     both_forms(kkt, inp, "f32", "packed 40 short sequences")
+
+
+def run_gate_sum_form(kkt, inp: W.Inputs, split: bool, in_place: bool):
+    k, _, b, cu = to_device(inp)
+    g_raw = torch.from_numpy(inp.g_raw).to(k.device)
+    old = os.environ.get("KKT_SPLIT_TILES")
+    os.environ["KKT_SPLIT_TILES"] = "1000000000" if split else "0"
+    try:
+        B, T, H, _ = k.shape
+        out = torch.full((B, T, H, 64), float("nan"), dtype=torch.float32, device=k.device)
+        g_out = g_raw if in_place else torch.full((B, T, H), float("nan"), dtype=torch.float32, device=k.device)
+        kkt.kkt_solve_gate_cumsum(k, g_raw, b, cu, output_dtype=torch.float32, out=out, g_out=g_out)
+        torch.cuda.synchronize()
+    finally:
+        if old is None:
+            del os.environ["KKT_SPLIT_TILES"]
+        else:
+            os.environ["KKT_SPLIT_TILES"] = old
+    return out.cpu().numpy(), g_out.cpu().numpy()
+
+
+@pytest.mark.parametrize("shape", ["T256", "T2000", "packed"])
+def test_split_tiles_gate_sum(kkt, shape):
+    """kkt_solve_gate_cumsum: the two forms give the same bits for the output
+    and the summed gate, also summing in place (g_out = g_decay, which the
+    second wave of a split tile reads while the first one writes the sums)."""
+    if shape == "packed":
+        lens = np.random.default_rng(4600).integers(0, 300, 30)
+        lens[[2, 9]] = 0
+        inp = W.generate("T256_H8_bf16_f32", lengths=lens.tolist(), H=3, seed=4601)
+    else:
+        inp = W.generate("T2000_H8_bf16_bf16" if shape == "T2000" else "T256_H8_bf16_f32")
+    say(f"[case] gate-sum split vs one-wave tiles, {shape}: B={inp.workload.B} T={inp.workload.T} H={inp.workload.H}")
+    X1, g1 = run_gate_sum_form(kkt, inp, split=False, in_place=False)
+    X2, g2 = run_gate_sum_form(kkt, inp, split=True, in_place=False)
+    X3, g3 = run_gate_sum_form(kkt, inp, split=True, in_place=True)
+    for X in (X2, X3):
+        assert np.array_equal(X1.view(np.uint32), X.view(np.uint32))
+    if inp.cu_seqlens is None:
+        for g in (g2, g3):
+            assert np.array_equal(g1.view(np.uint32), g.view(np.uint32))
+    else:
+        covered = np.zeros(inp.workload.T, dtype=bool)
+        covered[int(inp.cu_seqlens[0]):int(inp.cu_seqlens[-1])] = True
+        for g in (g2, g3):
+            assert np.array_equal(g1[:, covered].view(np.uint32), g[:, covered].view(np.uint32))
+    ref = oracle.kkt_solve_ref(inp.k64(), inp.g, inp.beta, inp.cu_seqlens)
+    compare(X3, ref, "f32", inp.cu_seqlens, f"gate-sum split {shape}")
+    say("[ok]")
