@@ -159,3 +159,13 @@ def test_split_tiles_gate_sum(kkt, shape):
     ref = oracle.kkt_solve_ref(inp.k64(), inp.g, inp.beta, inp.cu_seqlens)
     compare(X3, ref, "f32", inp.cu_seqlens, f"gate-sum split {shape}")
     say("[ok]")
+
+
+def test_split_tiles_many_packed_sequences(kkt):
+    """More than 64 packed sequences (the 64-ary chunk search instead of the
+    scan) on a grid small enough for two-wave tiles."""
+    lens = np.random.default_rng(4700).integers(0, 12, 110)
+    lens[[0, 50, 109]] = 0
+    inp = W.generate("T256_H8_bf16_f32", lengths=lens.tolist(), H=2, seed=4701)
+    assert 2 * (inp.workload.T // 64 + 110) <= 256
+    both_forms(kkt, inp, "f32", "packed 110 short sequences")
