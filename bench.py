@@ -55,12 +55,13 @@ SPLIT_MAX_TILES = 256          # the library's bound for two-wave tiles of the f
 
 def kernel_name(key: str, workload: str) -> str:
     """The kernel an op key launches on a workload: the fused op at 64-token
-    chunks (with or without the gate sum) takes its two-wave-per-tile form on
-    grids of up to SPLIT_MAX_TILES
+    chunks (with or without the gate sum) and the solve of a given A take
+    their two-wave-per-tile form on grids of up to SPLIT_MAX_TILES
     chunk-head tiles (the library's grid counts T/64 + num_seqs chunks for
     packed sequences)."""
     from chunked_gated_delta_token_amd import workloads as W
-    split_names = {"fused": "kkt_solve_split_kernel", "gate_cumsum": "kkt_solve_gate_cumsum_split_kernel"}
+    split_names = {"fused": "kkt_solve_split_kernel", "gate_cumsum": "kkt_solve_gate_cumsum_split_kernel",
+                   "solve_tril": "kkt_solve_tril_split_kernel"}
     if key in split_names:
         w = W.WORKLOADS[workload]
         grid = w.H * ((w.T // 64 + w.n_seqs) if w.n_seqs else w.B * (-(-w.T // 64)))

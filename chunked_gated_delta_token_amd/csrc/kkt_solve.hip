@@ -459,7 +459,7 @@ __device__ __forceinline__ void chunk_rows(const KernelArgs& args, WaveLds& lds,
     static_assert(K % (4 * kElemsPer16B) == 0, "K must fill whole fragments");
     static_assert(CH == 64 || (CH == 128 && MODE == Mode::Fused), "128-token chunks: fused op only");
     static_assert(!SHARE || (CH == 128 && kSteps <= 4), "shared key tile: 128-token kernel, at most 4 k-steps");
-    static_assert(SPLIT == 0 || (CH == 64 && MODE == Mode::Fused), "split tiles: the 64-token fused op");
+    static_assert(SPLIT == 0 || (CH == 64 && MODE != Mode::ScaledDot), "split tiles: the 64-token solve");
     // diagonal blocks this wave inverts (the first wave of a split tile
     // inverts all four, while the second forms its row's other blocks)
     auto owns = [](int) { return SPLIT != 2; };
@@ -983,10 +983,11 @@ struct SplitLds {
     f32x4 xchg[3][kWave];
 };
 
-// One 64-token chunk per two-wave workgroup (the fused op on small grids,
-// where a tile's latency, not the chip's throughput, sets the time).  Both
-// waves sum the gate of a GATE_SUM tile, with the same scan.
-template <Elt IN, Elt OUT, int K, bool GATE_SUM = false>
+// One 64-token chunk per two-wave workgroup (the fused op, or the solve of
+// a given A, on small grids, where a tile's latency, not the chip's
+// throughput, sets the time).  Both waves sum the gate of a GATE_SUM tile,
+// with the same scan.
+template <Mode MODE, Elt IN, Elt OUT, int K, bool GATE_SUM = false>
 __device__ __forceinline__ void run_split_tile(const KernelArgs& args, SplitLds& lds)
 {
     const int lane = threadIdx.x % kWave;
@@ -999,11 +1000,11 @@ __device__ __forceinline__ void run_split_tile(const KernelArgs& args, SplitLds&
     if (tile.len <= 0) return;  // workgroup-uniform
     const int64_t tok = tile.row0 * H + h;
     if (wave == 0) {
-        chunk_rows<Mode::Fused, IN, OUT, K, GATE_SUM, kChunk, false, 1>(args, lds.wave[0], lds.blk, lds.xchg, lane,
-                                                                        tok, tile.len, 0, nullptr);
+        chunk_rows<MODE, IN, OUT, K, GATE_SUM, kChunk, false, 1>(args, lds.wave[0], lds.blk, lds.xchg, lane, tok,
+                                                                 tile.len, 0, nullptr);
     } else {
-        chunk_rows<Mode::Fused, IN, OUT, K, GATE_SUM, kChunk, false, 2>(args, lds.wave[1], lds.blk, lds.xchg, lane,
-                                                                        tok, tile.len, 0, nullptr);
+        chunk_rows<MODE, IN, OUT, K, GATE_SUM, kChunk, false, 2>(args, lds.wave[1], lds.blk, lds.xchg, lane, tok,
+                                                                 tile.len, 0, nullptr);
     }
 }
 
@@ -1184,7 +1185,7 @@ __global__ __launch_bounds__(kWave * 2)
 void kkt_solve_split_kernel(const KernelArgs args)
 {
     __shared__ SplitLds lds;
-    run_split_tile<IN, OUT, K>(args, lds);
+    run_split_tile<Mode::Fused, IN, OUT, K>(args, lds);
 }
 
 template <Elt IN, Elt OUT, int K>
@@ -1200,7 +1201,7 @@ __global__ __launch_bounds__(kWave * 2)
 void kkt_solve_gate_cumsum_split_kernel(const KernelArgs args)
 {
     __shared__ SplitLds lds;
-    run_split_tile<IN, OUT, K, true>(args, lds);
+    run_split_tile<Mode::Fused, IN, OUT, K, true>(args, lds);
 }
 
 template <Elt IN, int K>
@@ -1218,6 +1219,14 @@ void kkt_solve_tril_kernel(const KernelArgs args)
 {
     __shared__ WaveLds lds_all[kWavesPerGroup];
     run_tile<Mode::SolveTril, Elt::F32, OUT, 64>(args, lds_all);
+}
+
+template <Elt OUT>
+__global__ __launch_bounds__(kWave * 2)
+void kkt_solve_tril_split_kernel(const KernelArgs args)
+{
+    __shared__ SplitLds lds;
+    run_split_tile<Mode::SolveTril, Elt::F32, OUT, 64>(args, lds);
 }
 
 // 128-token chunks (the GDR case page's chunk size), one workgroup per
@@ -1738,14 +1747,23 @@ extern "C" kkt_status_t kkt_solve_tril(const float* A, const int32_t* cu_seqlens
     if (T == 0) return KKT_OK;
     KernelArgs a;
     kkt_status_t st = setup(a, A, nullptr, nullptr, cu_seqlens, num_seqs, B, T, H, H * kChunk * 4,
-                            H * kChunk * dtype_bytes(out_dtype), out, stream);
+                            H * kChunk * dtype_bytes(out_dtype), out, stream, kChunk, true);
     if (st != KKT_OK) return st;
 
     hipError_t e;
     switch (out_dtype) {
-    case KKT_DTYPE_F32: e = launch(kkt_solve_tril_kernel<Elt::F32>, a, stream); break;
-    case KKT_DTYPE_BF16: e = launch(kkt_solve_tril_kernel<Elt::BF16>, a, stream); break;
-    default: e = launch(kkt_solve_tril_kernel<Elt::F16>, a, stream); break;
+    case KKT_DTYPE_F32:
+        e = a.split_tiles ? launch(kkt_solve_tril_split_kernel<Elt::F32>, a, stream, 2)
+                          : launch(kkt_solve_tril_kernel<Elt::F32>, a, stream);
+        break;
+    case KKT_DTYPE_BF16:
+        e = a.split_tiles ? launch(kkt_solve_tril_split_kernel<Elt::BF16>, a, stream, 2)
+                          : launch(kkt_solve_tril_kernel<Elt::BF16>, a, stream);
+        break;
+    default:
+        e = a.split_tiles ? launch(kkt_solve_tril_split_kernel<Elt::F16>, a, stream, 2)
+                          : launch(kkt_solve_tril_kernel<Elt::F16>, a, stream);
+        break;
     }
     if (e != hipSuccess) return fail(KKT_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(e));
     return KKT_OK;

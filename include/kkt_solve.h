@@ -178,7 +178,8 @@ kkt_status_t kkt_scaled_dot(const void* k, const float* g, const float* beta,
  *
  *   kkt_solve_tril(kkt_scaled_dot(k, ...)) with fp32 A in between gives
  *   bit-identical results to kkt_solve(k, ...): both run the same solve on the
- *   same fp32 values.  Errors: as for kkt_solve (no K, no in_dtype here).
+ *   same fp32 values.  Errors and launch form: as for kkt_solve (no K, no
+ *   in_dtype here).
  */
 kkt_status_t kkt_solve_tril(const float* A, const int32_t* cu_seqlens, int64_t num_seqs,
                             int64_t B, int64_t T, int64_t H, int64_t chunk_size,

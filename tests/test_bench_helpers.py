@@ -102,6 +102,9 @@ def test_kernel_name_follows_the_launch_form(monkeypatch):
     assert bench.kernel_name("gate_cumsum", "T256_H8_bf16_f32") == "kkt_solve_gate_cumsum_split_kernel"
     assert bench.kernel_name("gate_cumsum", "T8192_H8_bf16_f32") == "kkt_solve_gate_cumsum_kernel"
     assert bench.kernel_name("gate_cumsum128", "T256_H8_bf16_f32") == "kkt_solve128_kernel"
+    assert bench.kernel_name("solve_tril", "T2000_H8_bf16_bf16") == "kkt_solve_tril_split_kernel"
+    assert bench.kernel_name("solve_tril", "T8192_H8_bf16_f32") == "kkt_solve_tril_kernel"
+    assert bench.kernel_name("scaled_dot", "T256_H8_bf16_f32") == "kkt_scaled_dot_kernel"
     monkeypatch.setenv("KKT_SPLIT_TILES", "0")
     assert bench.kernel_name("fused", "T256_H8_bf16_f32") == "kkt_solve_kernel"
     monkeypatch.setenv("KKT_SPLIT_TILES", "1024")

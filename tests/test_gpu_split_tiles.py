@@ -169,3 +169,40 @@ def test_split_tiles_many_packed_sequences(kkt):
     inp = W.generate("T256_H8_bf16_f32", lengths=lens.tolist(), H=2, seed=4701)
     assert 2 * (inp.workload.T // 64 + 110) <= 256
     both_forms(kkt, inp, "f32", "packed 110 short sequences")
+
+
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", ["T2000", "packed"])
+def test_split_tiles_solve_tril(kkt, shape, out_dtype):
+    """kkt_solve_tril of the same A in both forms: the same bits, and the
+    chain kkt_solve_tril(kkt_scaled_dot(...)) bit-equal to the fused op."""
+    if shape == "packed":
+        lens = np.random.default_rng(4800).integers(0, 200, 25)
+        lens[[1, 7]] = 0
+        inp = W.generate("T256_H8_bf16_f32", lengths=lens.tolist(), H=3, seed=4801)
+    else:
+        inp = W.generate("T2000_H8_bf16_bf16")
+    say(f"[case] solve_tril split vs one-wave tiles, {shape} -> {out_dtype}")
+    k, g, b, cu = to_device(inp)
+    A = kkt.kkt_scaled_dot(k, g, b, cu)
+    torch.cuda.synchronize()
+    old = os.environ.get("KKT_SPLIT_TILES")
+    try:
+        res = []
+        for split in (False, True):
+            os.environ["KKT_SPLIT_TILES"] = "1000000000" if split else "0"
+            X = kkt.kkt_solve_tril(A, cu, output_dtype=TORCH_DT[out_dtype])
+            torch.cuda.synchronize()
+            res.append(from_device(X, out_dtype))
+    finally:
+        if old is None:
+            del os.environ["KKT_SPLIT_TILES"]
+        else:
+            os.environ["KKT_SPLIT_TILES"] = old
+    view = np.uint32 if out_dtype == "f32" else np.uint16
+    assert np.array_equal(res[0].view(view), res[1].view(view))
+    fused = run_form(kkt, (k, g, b, cu), out_dtype, split=True)
+    assert np.array_equal(res[1].view(view), fused.view(view))
+    ref = oracle.kkt_solve_ref(inp.k64(), inp.g, inp.beta, inp.cu_seqlens)
+    compare(res[1], ref, out_dtype, inp.cu_seqlens, f"solve_tril split {shape}")
+    say("[ok]")
