@@ -7,7 +7,8 @@
 //   A[i][j] = beta_i (k_i . k_j) exp(clamp(g_i - g_j, -50, 50)) for i > j, 0 otherwise
 //   out rows = rows of (I + A)^{-1}, 64 wide, written once in full.
 //
-// One wave64 owns one (chunk, head) tile from load to store; nothing goes
+// One wave64 owns one (chunk, head) tile from load to store (on grids of at
+// most 256 tiles two waves share it, kkt_solve_split_kernel); nothing goes
 // back to HBM between the steps.
 //   a1  tile -> (b, t0, L, h); for packed sequences a scan of (or, beyond
 //       64 sequences, a 64-ary search over) cu_seqlens (no host sync, no
@@ -38,7 +39,8 @@
 //       side-by-side 16x16 blocks, PyPTO GatedDeltaRule case, sections 3.3.1,
 //       3.3.2 and 3.4).  The updates are right-looking (column p of A applied
 //       to every later row as soon as x[p] is final), so the dependent chain is
-//       one FMA per row.
+//       one FMA per row; A[r][p] reaches the lanes of a block by a DPP row
+//       broadcast inside the FMA.
 //   a7  the six off-diagonal 16x16 blocks, fp32 MFMA:
 //         W_ik = X_ii A_ik                      (all six independent)
 //         X_ij = -sum_{k=j}^{i-1} W_ik X_kj     (three dependency levels)
@@ -51,7 +53,10 @@
 // steps (ScaledDot: a1-a5 and A written in fp32; SolveTril: A read back, then
 // a6-a8), the gate formed from per-token log-decays (a wave scan before a4),
 // and 128-token chunks (kkt_solve128_kernel: the two 64-row halves plus the
-// block below the diagonal, one workgroup per chunk).
+// block below the diagonal, one workgroup per chunk), and, split between two
+// waves of a workgroup, the small grids of the fused op, its gate-sum form and
+// the solve of a given A (the same operations in the same order, so the same
+// bits).
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
