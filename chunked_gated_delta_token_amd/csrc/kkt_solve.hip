@@ -258,6 +258,7 @@ struct KernelArgs {
     uint32_t remap_groups;      // kChunkRoundRobin: workgroups in whole rounds (the rest keep their order)
     float* g_out;               // gate-sum kernel: where the summed gate goes, or nullptr
     int32_t split_tiles;        // host only: launch the fused op's two-wave-per-tile form
+    int32_t tile_waves;         // one-wave-per-tile kernels: waves (tiles) per workgroup, 1 or 4
 };
 
 // ---------------------------------------------------------------- tile map (a1)
@@ -968,7 +969,7 @@ __device__ __forceinline__ void run_tile(const KernelArgs& args, WaveLds* lds_al
     // wave-uniform values are pinned to scalar registers so that the buffer
     // resources built from them are scalar too
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const uint32_t tile_id = workgroup_order(args) * kWavesPerGroup + wave;
+    const uint32_t tile_id = workgroup_order(args) * (uint32_t)args.tile_waves + wave;
     if (tile_id >= (uint32_t)args.n_tiles) return;  // wave-uniform
 
     // ---- a1: tile map
@@ -1468,9 +1469,11 @@ kkt_status_t validate_cu_seqlens(const int32_t* cu, int64_t num_seqs, int64_t T,
     return KKT_OK;
 }
 
-hipError_t launch(void (*kernel)(KernelArgs), const KernelArgs& a, hipStream_t stream, int waves = kWavesPerGroup)
+// waves: the workgroup size in waves; the one-wave-per-tile kernels take
+// a.tile_waves (their default), the others name theirs
+hipError_t launch(void (*kernel)(KernelArgs), const KernelArgs& a, hipStream_t stream, int waves = 0)
 {
-    hipLaunchKernelGGL(kernel, dim3(a.n_groups), dim3(kWave * waves), 0, stream, a);
+    hipLaunchKernelGGL(kernel, dim3(a.n_groups), dim3(kWave * (waves > 0 ? waves : a.tile_waves)), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -1509,7 +1512,8 @@ template <Elt IN, Elt OUT, int K, bool GATE_SUM>
 hipError_t launch_fused128_k(const KernelArgs& a, hipStream_t stream)
 {
     constexpr int kSteps = K / (4 * (16 / EltInfo<IN>::bytes));
-    return launch(kkt_solve128_kernel<IN, OUT, K, (kSteps <= 4) ? kKeysShared : kKeysGlobal, GATE_SUM>, a, stream);
+    return launch(kkt_solve128_kernel<IN, OUT, K, (kSteps <= 4) ? kKeysShared : kKeysGlobal, GATE_SUM>, a, stream,
+                  kWavesPerGroup);
 }
 
 template <Elt IN, Elt OUT, bool GATE_SUM>
@@ -1568,6 +1572,17 @@ constexpr int64_t kRemapMaxGroups = 1024;
 // cost as much as the shorter tail saves or more (1024 tiles: 13-25% more
 // time).  KKT_SPLIT_TILES overrides the bound (0: never split).
 constexpr int64_t kSplitMaxTiles = 256;
+
+// Grids of up to this many tiles (two per CU) that run one tile per wave
+// (the fused op, its gate-sum form and the solve of a given A, when not
+// split) do so in workgroups of one wave, which the hardware spreads over
+// every CU; four-wave workgroups put such a grid on a quarter or half of the
+// CUs.  Measured one-wave against four-wave workgroups (µs, bf16 keys, K =
+// 128): 512 tiles 6.11-6.14 vs 6.74, 448 tiles with fp32 keys 9.17-9.19 vs
+// 10.34-10.36; at 768 tiles no difference, and at 1024 tiles and beyond
+// four-wave workgroups are as fast or faster (16384 tiles: 75.0 vs 80.2;
+// the first step of the chain at 1024 tiles: 6.82-6.87 vs 7.33-7.36).
+constexpr int64_t kSmallGridTiles = 512;
 int64_t split_max_tiles()
 {
     const char* v = getenv("KKT_SPLIT_TILES");
@@ -1601,7 +1616,11 @@ kkt_status_t setup(KernelArgs& a, const void* in, const float* g, const float* b
     const int64_t n_chunks = (cu_seqlens == nullptr) ? B * chunks_per_row : T / chunk + num_seqs;
     const int64_t n_tiles = n_chunks * H;
     const bool split = allow_split && chunk == kChunk && n_tiles <= split_max_tiles();
-    const int64_t tiles_per_group = (chunk == kChunk && !split) ? kWavesPerGroup : 1;
+    // one wave per tile: a workgroup of one wave on grids of up to
+    // kSmallGridTiles tiles of the solving entry points (spread over every
+    // CU), else of four
+    const int64_t tiles_per_group =
+        (chunk == kChunk && !split) ? ((allow_split && n_tiles <= kSmallGridTiles) ? 1 : kWavesPerGroup) : 1;
     if (n_tiles >= (1LL << 31) - kWavesPerGroup || num_seqs >= (1LL << 31) - 1) {
         return fail(KKT_ERR_UNSUPPORTED, "problem too large for one launch");
     }
@@ -1639,6 +1658,7 @@ kkt_status_t setup(KernelArgs& a, const void* in, const float* g, const float* b
     a.remap_groups = (uint32_t)((groups >> (lg + 3)) << (lg + 3));
     a.g_out = nullptr;
     a.split_tiles = split ? 1 : 0;
+    a.tile_waves = (int32_t)tiles_per_group;
     return KKT_OK;
 }
 
