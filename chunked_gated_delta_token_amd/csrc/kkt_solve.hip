@@ -1176,12 +1176,20 @@ __device__ __forceinline__ void cross_block_rows(const KernelArgs& args, GateLds
     cross_scale(args, lds, lane, w2, in, acc);
 }
 
+// The one-wave-per-tile kernels size their LDS at launch: one WaveLds per
+// wave of the workgroup (1 or 4), so that one-wave workgroups take 5.9 KB.
+__device__ __forceinline__ WaveLds* tile_lds()
+{
+    extern __shared__ __align__(16) char lds_raw[];
+    return reinterpret_cast<WaveLds*>(lds_raw);
+}
+
 // One kernel per entry point, so that profiles name the operation.
 template <Elt IN, Elt OUT, int K>
 __global__ __launch_bounds__(kWave * kWavesPerGroup)
 void kkt_solve_kernel(const KernelArgs args)
 {
-    __shared__ WaveLds lds_all[kWavesPerGroup];
+    WaveLds* lds_all = tile_lds();
     run_tile<Mode::Fused, IN, OUT, K>(args, lds_all);
 }
 
@@ -1198,7 +1206,7 @@ template <Elt IN, Elt OUT, int K>
 __global__ __launch_bounds__(kWave * kWavesPerGroup)
 void kkt_solve_gate_cumsum_kernel(const KernelArgs args)
 {
-    __shared__ WaveLds lds_all[kWavesPerGroup];
+    WaveLds* lds_all = tile_lds();
     run_tile<Mode::Fused, IN, OUT, K, true>(args, lds_all);
 }
 
@@ -1214,7 +1222,7 @@ template <Elt IN, int K>
 __global__ __launch_bounds__(kWave * kWavesPerGroup)
 void kkt_scaled_dot_kernel(const KernelArgs args)
 {
-    __shared__ WaveLds lds_all[kWavesPerGroup];
+    WaveLds* lds_all = tile_lds();
     run_tile<Mode::ScaledDot, IN, Elt::F32, K>(args, lds_all);
 }
 
@@ -1223,7 +1231,7 @@ template <Elt OUT>
 __global__ __launch_bounds__(kWave * kWavesPerGroup)
 void kkt_solve_tril_kernel(const KernelArgs args)
 {
-    __shared__ WaveLds lds_all[kWavesPerGroup];
+    WaveLds* lds_all = tile_lds();
     run_tile<Mode::SolveTril, Elt::F32, OUT, 64>(args, lds_all);
 }
 
@@ -1473,7 +1481,9 @@ kkt_status_t validate_cu_seqlens(const int32_t* cu, int64_t num_seqs, int64_t T,
 // a.tile_waves (their default), the others name theirs
 hipError_t launch(void (*kernel)(KernelArgs), const KernelArgs& a, hipStream_t stream, int waves = 0)
 {
-    hipLaunchKernelGGL(kernel, dim3(a.n_groups), dim3(kWave * (waves > 0 ? waves : a.tile_waves)), 0, stream, a);
+    // (the one-wave-per-tile kernels take one WaveLds per wave as dynamic LDS)
+    const size_t lds_bytes = (waves > 0) ? 0 : (size_t)a.tile_waves * sizeof(WaveLds);
+    hipLaunchKernelGGL(kernel, dim3(a.n_groups), dim3(kWave * (waves > 0 ? waves : a.tile_waves)), lds_bytes, stream, a);
     return hipGetLastError();
 }
 
@@ -1573,16 +1583,17 @@ constexpr int64_t kRemapMaxGroups = 1024;
 // time).  KKT_SPLIT_TILES overrides the bound (0: never split).
 constexpr int64_t kSplitMaxTiles = 256;
 
-// Grids of up to this many tiles (two per CU) that run one tile per wave
-// (the fused op, its gate-sum form and the solve of a given A, when not
-// split) do so in workgroups of one wave, which the hardware spreads over
-// every CU; four-wave workgroups put such a grid on a quarter or half of the
-// CUs.  Measured one-wave against four-wave workgroups (µs, bf16 keys, K =
-// 128): 512 tiles 6.11-6.14 vs 6.74, 448 tiles with fp32 keys 9.17-9.19 vs
-// 10.34-10.36; at 768 tiles no difference, and at 1024 tiles and beyond
-// four-wave workgroups are as fast or faster (16384 tiles: 75.0 vs 80.2;
-// the first step of the chain at 1024 tiles: 6.82-6.87 vs 7.33-7.36).
-constexpr int64_t kSmallGridTiles = 512;
+// Grids that run one tile per wave use workgroups of one wave up to a bound
+// (the hardware spreads them over every CU; four-wave workgroups put a small
+// grid on a quarter or half of the CUs), of four waves beyond it.  Measured
+// one-wave against four-wave workgroups (µs, bf16 keys, K = 128): 512 tiles
+// 6.11-6.14 vs 6.74, 448 tiles with fp32 keys 9.17-9.19 vs 10.34-10.36; at
+// 1024 tiles the fused op 8.22-8.24 vs 8.34-8.37, its gate-sum form 8.70-8.74
+// vs 8.70-8.71, the solve of a given A 6.49-6.51 vs 6.44-6.46, the first
+// step of the chain 7.33-7.36 vs 6.82-6.87; beyond, four-wave workgroups are
+// faster (16384 tiles: 75.0 vs 80.2; 1876: 20.0 vs 21.0-21.4).
+constexpr int64_t kWave1GroupTilesFused = 1024;  // kkt_solve
+constexpr int64_t kWave1GroupTiles = 512;        // kkt_solve_gate_cumsum, kkt_solve_tril
 int64_t split_max_tiles()
 {
     const char* v = getenv("KKT_SPLIT_TILES");
@@ -1596,7 +1607,7 @@ int64_t split_max_tiles()
 kkt_status_t setup(KernelArgs& a, const void* in, const float* g, const float* beta,
                    const int32_t* cu_seqlens, int64_t num_seqs, int64_t B, int64_t T, int64_t H,
                    int64_t in_row_bytes, int64_t out_row_bytes, void* out, hipStream_t stream,
-                   int64_t chunk = kChunk, bool allow_split = false)
+                   int64_t chunk = kChunk, bool allow_split = false, int64_t wave1_group_tiles = 0)
 {
     if (in == nullptr || out == nullptr) return fail(KKT_ERR_INVALID_ARGUMENT, "input and output must not be NULL");
     // the kernel moves the row tensors in 16-byte vectors, g / beta / cu_seqlens in 4-byte words
@@ -1617,10 +1628,9 @@ kkt_status_t setup(KernelArgs& a, const void* in, const float* g, const float* b
     const int64_t n_tiles = n_chunks * H;
     const bool split = allow_split && chunk == kChunk && n_tiles <= split_max_tiles();
     // one wave per tile: a workgroup of one wave on grids of up to
-    // kSmallGridTiles tiles of the solving entry points (spread over every
-    // CU), else of four
+    // wave1_group_tiles tiles (spread over every CU), else of four
     const int64_t tiles_per_group =
-        (chunk == kChunk && !split) ? ((allow_split && n_tiles <= kSmallGridTiles) ? 1 : kWavesPerGroup) : 1;
+        (chunk == kChunk && !split) ? ((n_tiles <= wave1_group_tiles) ? 1 : kWavesPerGroup) : 1;
     if (n_tiles >= (1LL << 31) - kWavesPerGroup || num_seqs >= (1LL << 31) - 1) {
         return fail(KKT_ERR_UNSUPPORTED, "problem too large for one launch");
     }
@@ -1690,7 +1700,7 @@ extern "C" kkt_status_t kkt_solve(const void* k, const float* g, const float* be
     if (T == 0) return KKT_OK;
     KernelArgs a;
     st = setup(a, k, g, beta, cu_seqlens, num_seqs, B, T, H, H * K * dtype_bytes(in_dtype),
-               H * chunk_size * dtype_bytes(out_dtype), out, stream, chunk_size, true);
+               H * chunk_size * dtype_bytes(out_dtype), out, stream, chunk_size, true, kWave1GroupTilesFused);
     if (st != KKT_OK) return st;
 
     hipError_t e;
@@ -1719,7 +1729,7 @@ extern "C" kkt_status_t kkt_solve_gate_cumsum(const void* k, const float* g_deca
     if ((reinterpret_cast<uintptr_t>(g_out) & 3u) != 0) return fail(KKT_ERR_INVALID_ARGUMENT, "g_out must be 4-byte aligned");
     KernelArgs a;
     st = setup(a, k, g_decay, beta, cu_seqlens, num_seqs, B, T, H, H * K * dtype_bytes(in_dtype),
-               H * chunk_size * dtype_bytes(out_dtype), out, stream, chunk_size, true);
+               H * chunk_size * dtype_bytes(out_dtype), out, stream, chunk_size, true, kWave1GroupTiles);
     if (st != KKT_OK) return st;
     a.g_out = g_out;
 
@@ -1772,7 +1782,7 @@ extern "C" kkt_status_t kkt_solve_tril(const float* A, const int32_t* cu_seqlens
     if (T == 0) return KKT_OK;
     KernelArgs a;
     kkt_status_t st = setup(a, A, nullptr, nullptr, cu_seqlens, num_seqs, B, T, H, H * kChunk * 4,
-                            H * kChunk * dtype_bytes(out_dtype), out, stream, kChunk, true);
+                            H * kChunk * dtype_bytes(out_dtype), out, stream, kChunk, true, kWave1GroupTiles);
     if (st != KKT_OK) return st;
 
     hipError_t e;
