@@ -394,7 +394,7 @@ def summarize_trace(directory: str, op: str, workload: str, run_log: str = None,
     ]
     if disp is not None:
         lines += [f"grid_x: {disp['Grid_Size_X']}", f"workgroup_x: {disp['Workgroup_Size_X']}",
-                  f"lds_bytes_per_workgroup: {disp['LDS_Block_Size']}", f"scratch_bytes: {disp['Scratch_Size']}",
+                  f"lds_bytes_per_workgroup: {disp['LDS_Block_Size']}  # static; one-wave-per-tile kernels add 5888 per wave at launch", f"scratch_bytes: {disp['Scratch_Size']}",
                   f"vgpr_count: {disp['VGPR_Count']}", f"sgpr_count: {disp['SGPR_Count']}"]
     lines.append(f"algorithmic_GBs_at_average: {nbytes / avg:.1f}")
     lines.append("# durations are device-side (dispatch start to end), eager warmup launches included")
