@@ -1586,14 +1586,16 @@ constexpr int64_t kSplitMaxTiles = 256;
 // Grids that run one tile per wave use workgroups of one wave up to a bound
 // (the hardware spreads them over every CU; four-wave workgroups put a small
 // grid on a quarter or half of the CUs), of four waves beyond it.  Measured
-// one-wave against four-wave workgroups (µs, bf16 keys, K = 128): 512 tiles
-// 6.11-6.14 vs 6.74, 448 tiles with fp32 keys 9.17-9.19 vs 10.34-10.36; at
-// 1024 tiles the fused op 8.22-8.24 vs 8.34-8.37, its gate-sum form 8.70-8.74
-// vs 8.70-8.71, the solve of a given A 6.49-6.51 vs 6.44-6.46, the first
-// step of the chain 7.33-7.36 vs 6.82-6.87; beyond, four-wave workgroups are
-// faster (16384 tiles: 75.0 vs 80.2; 1876: 20.0 vs 21.0-21.4).
+// one-wave against four-wave workgroups (µs, bf16 keys, K = 128): the fused
+// op on 512 tiles 6.11-6.14 vs 6.74, on 448 tiles with fp32 keys 9.17-9.19 vs
+// 10.34-10.36; the first step of the chain on 256 and 32 tiles 4.15-4.16 vs
+// 5.46-5.48 and 3.47-3.48 vs 4.93; at 1024 tiles the fused op 8.22-8.24 vs
+// 8.34-8.37, its gate-sum form 8.70-8.74 vs 8.70-8.71, the solve of a given A
+// 6.49-6.51 vs 6.44-6.46, the first step of the chain 7.33-7.36 vs
+// 6.82-6.87; beyond, four-wave workgroups are faster (16384 tiles: 75.0 vs
+// 80.2; 1876: 20.0 vs 21.0-21.4).
 constexpr int64_t kWave1GroupTilesFused = 1024;  // kkt_solve
-constexpr int64_t kWave1GroupTiles = 512;        // kkt_solve_gate_cumsum, kkt_solve_tril
+constexpr int64_t kWave1GroupTiles = 512;        // the other entry points
 int64_t split_max_tiles()
 {
     const char* v = getenv("KKT_SPLIT_TILES");
@@ -1755,7 +1757,8 @@ extern "C" kkt_status_t kkt_scaled_dot(const void* k, const float* g, const floa
     if (st != KKT_OK) return st;
     if (T == 0) return KKT_OK;
     KernelArgs a;
-    st = setup(a, k, g, beta, cu_seqlens, num_seqs, B, T, H, H * K * dtype_bytes(in_dtype), H * kChunk * 4, A, stream);
+    st = setup(a, k, g, beta, cu_seqlens, num_seqs, B, T, H, H * K * dtype_bytes(in_dtype), H * kChunk * 4, A, stream,
+               kChunk, false, kWave1GroupTiles);
     if (st != KKT_OK) return st;
 
     hipError_t e;
