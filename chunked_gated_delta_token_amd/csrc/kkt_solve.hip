@@ -68,7 +68,7 @@
 
 #include "kkt_solve.h"
 
-#define KKT_VERSION_NUMBER 600  // 0.6.0
+#define KKT_VERSION_NUMBER 700  // 0.7.0
 
 namespace {
 
