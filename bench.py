@@ -18,6 +18,11 @@ HBM).
 Timed region: K steps captured in one HIP graph (launch overhead of the
 Python/ctypes call path is not the op's), bracketed by a device
 synchronisation and HIP events on the launch stream.  Prints one JSON line.
+
+The default run (the fused op on the bench workload) also times the second
+shape of the PR #135 table that the target names, (2,16384,32,128) bf16 keys
+and bf16 output, the same way in the same process, and reports it under
+"second_target" (the headline fields stay those of (1,8192,8,128)).
 """
 from __future__ import annotations
 
@@ -37,6 +42,7 @@ METRIC = "fused KKT+solve ms/iter & achieved HBM GB/s at (1,8192,8,128) bf16, 1 
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E peak
 PAGES_FUSED_MS = 0.3593         # Ascend 910B fused op at (1,8192,8,128), PR #135 perf table (context only)
 PAGES_TWO_OP_MS = 0.4318        # Ascend 910B two-op chain at (1,8192,8,128), same table (context only)
+PAGES_FUSED_MS_SECOND = 4.9368  # Ascend 910B fused op at (2,16384,32,128), same table (context only)
 MALL_BYTES = 256 << 20
 KERNEL_SRC = os.path.join(ROOT, "chunked_gated_delta_token_amd", "csrc", "kkt_solve.hip")
 # the kernel each op launches (chain: both of the unfused steps)
@@ -422,67 +428,17 @@ def summarize_trace(directory: str, op: str, workload: str, run_log: str = None,
     print("\n".join(lines))
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=400)
-    ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", default=None)
-    ap.add_argument("--op", choices=["fused", "gate_cumsum", "scaled_dot", "solve_tril", "chain"], default="fused",
-                    help="what one step runs (default: the fused op)")
-    ap.add_argument("--chunk", type=int, choices=[64, 128], default=64,
-                    help="chunk size of the fused op (128: the 128-token variant)")
-    ap.add_argument("--timing", choices=["graph", "eager"], default="graph")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--detail", action="store_true", help="also print per-launch event timings to stderr")
-    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
-                    help="instead of the op, run --steps plain device copies of BYTES bytes (the reference "
-                         "kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")
-    ap.add_argument("--summarize-traffic", nargs=4, metavar=("OP_FETCH", "OP_WRITE", "COPY_FETCH", "COPY_WRITE"),
-                    help="write the HBM-traffic summary from four rocprofv3 --pmc output directories")
-    ap.add_argument("--copy-bytes", type=int, default=0, help="size used by the copy-calibration runs")
-    ap.add_argument("--summarize-trace", metavar="DIR",
-                    help="write the kernel-trace summary of --op from a rocprofv3 --kernel-trace --stats directory")
-    ap.add_argument("--summarize-mfma", metavar="DIR",
-                    help="write the MFMA-counter summary of --op from a rocprofv3 --pmc directory")
-    ap.add_argument("--run-log", help="bench.py output of the profiled run (with --summarize-trace)")
-    ap.add_argument("--plain-log", help="bench.py output of an unprofiled run (with --summarize-trace)")
-    args = ap.parse_args()
-
-    if args.summarize_mfma:
-        from chunked_gated_delta_token_amd import workloads as W
-        summarize_mfma(args.summarize_mfma, args.op, args.workload or W.BENCH_WORKLOAD, args.chunk)
-        return
-
-    if args.summarize_trace:
-        from chunked_gated_delta_token_amd import workloads as W
-        summarize_trace(args.summarize_trace, args.op, args.workload or W.BENCH_WORKLOAD, args.run_log,
-                        args.plain_log, args.chunk)
-        return
-
-    if args.summarize_traffic:
-        from chunked_gated_delta_token_amd import workloads as W
-        summarize_traffic(args.summarize_traffic, args.copy_bytes, args.op, args.workload or W.BENCH_WORKLOAD,
-                          args.chunk)
-        return
-
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the fused KKT + solve has no cross-GPU step, and this "
-              "build runs on a single MI355X (run with --gpus 1).", file=sys.stderr)
-        sys.exit(2)
-
+def measure(name: str, op: str, chunk: int, steps: int, warmup: int, timing: str = "graph", detail: bool = False):
+    """Time `steps` steps of one op on one workload: inputs resident in HBM,
+    R buffer sets rotated so that every step reads HBM, the steps captured in
+    one HIP graph (timing "graph") and replayed once between two device
+    synchronisations, HIP events recorded on the launch stream around the
+    replay.  Returns the measured values and what they were measured on."""
     import numpy as np
     import torch
-
-    if args.copy_calibration:
-        copy_calibration(args.copy_calibration, args.steps)
-        return
-
     from chunked_gated_delta_token_amd import kkt
     from chunked_gated_delta_token_amd import workloads as W
 
-    name = args.workload or W.BENCH_WORKLOAD
     inp = W.generate(name)
     w = inp.workload
     dev = torch.device("cuda:0")
@@ -499,12 +455,10 @@ def main():
     b0 = None if inp.beta is None else torch.from_numpy(inp.beta).to(dev)
     cu0 = None if inp.cu_seqlens is None else torch.from_numpy(inp.cu_seqlens).to(dev)
     n_tokens = w.B * w.T
-    op = args.op
     if op == "gate_cumsum":
         if inp.g_raw is None:
             raise SystemExit(f"--op gate_cumsum needs a workload with a gate ({name} has none)")
         g0 = torch.from_numpy(inp.g_raw).to(dev)  # per-token log-decays, summed by the kernel
-    chunk = args.chunk
     if chunk != 64 and op not in ("fused", "gate_cumsum"):
         raise SystemExit("--chunk 128 applies to the fused op and its gate-sum form only")
     nbytes = algorithmic_bytes(w, n_tokens, op, inp.cu_seqlens, chunk)
@@ -580,14 +534,14 @@ def main():
     assert torch.isfinite(o).all().item(), "non-finite output"
     del o
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         launch(i)
     torch.cuda.synchronize()
 
-    K = args.steps
+    K = steps
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     graph = None
-    if args.timing == "graph":
+    if timing == "graph":
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph, stream=stream, capture_error_mode="thread_local"):
             for i in range(K):
@@ -611,8 +565,7 @@ def main():
     ev_ms = ev0.elapsed_time(ev1) / K
     ms_per_step = wall * 1e3 / K
 
-    detail = {}
-    if args.detail:
+    if detail:
         # per-launch event pairs (eager), for comparison with the profiler
         starts = [torch.cuda.Event(enable_timing=True) for _ in range(64)]
         ends = [torch.cuda.Event(enable_timing=True) for _ in range(64)]
@@ -622,16 +575,97 @@ def main():
             ends[i].record(stream)
         torch.cuda.synchronize()
         per = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
-        detail = {"per_launch_event_ms_median": per[len(per) // 2], "per_launch_event_ms_min": per[0],
-                  "graph_event_ms": ev_ms, "wall_ms": ms_per_step}
-        print(json.dumps(detail), file=sys.stderr, flush=True)
+        print(json.dumps({"workload": name, "per_launch_event_ms_median": per[len(per) // 2],
+                          "per_launch_event_ms_min": per[0], "graph_event_ms": ev_ms, "wall_ms": ms_per_step}),
+              file=sys.stderr, flush=True)
+    del graph, sets, calls
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
 
-    achieved = nbytes / (ev_ms * 1e-3) / 1e9
-    digest = source_digest()
-    key = op_key(op, chunk)
-    traffic = None if op == "chain" else read_traffic(digest, traffic_file(key, name))
     n_tiles = w.H * (sum(-(-(int(inp.cu_seqlens[s + 1]) - int(inp.cu_seqlens[s])) // chunk)
                          for s in range(num_seqs)) if num_seqs else w.B * (-(-w.T // chunk)))
+    key = op_key(op, chunk)
+    return {"inp": inp, "w": w, "nbytes": nbytes, "R": R, "ms_per_step": ms_per_step, "ev_ms": ev_ms,
+            "n_tiles": n_tiles, "key": key,
+            "kernel": KERNELS[key] if op == "chain" else kernel_name(key, name)}
+
+
+# The second shape the target is quoted on (PR #135 performance table, row
+# (2,16384,32,128)): timed beside the headline in the default run.
+SECOND_TARGET = "B2_T16384_H32_bf16_bf16"
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--op", choices=["fused", "gate_cumsum", "scaled_dot", "solve_tril", "chain"], default="fused",
+                    help="what one step runs (default: the fused op)")
+    ap.add_argument("--chunk", type=int, choices=[64, 128], default=64,
+                    help="chunk size of the fused op (128: the 128-token variant)")
+    ap.add_argument("--timing", choices=["graph", "eager"], default="graph")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-second-target", action="store_true",
+                    help="time only the headline workload (by default the fused op's run also times "
+                         "(2,16384,32,128) and reports it under second_target)")
+    ap.add_argument("--detail", action="store_true", help="also print per-launch event timings to stderr")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="instead of the op, run --steps plain device copies of BYTES bytes (the reference "
+                         "kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--summarize-traffic", nargs=4, metavar=("OP_FETCH", "OP_WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="write the HBM-traffic summary from four rocprofv3 --pmc output directories")
+    ap.add_argument("--copy-bytes", type=int, default=0, help="size used by the copy-calibration runs")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="write the kernel-trace summary of --op from a rocprofv3 --kernel-trace --stats directory")
+    ap.add_argument("--summarize-mfma", metavar="DIR",
+                    help="write the MFMA-counter summary of --op from a rocprofv3 --pmc directory")
+    ap.add_argument("--run-log", help="bench.py output of the profiled run (with --summarize-trace)")
+    ap.add_argument("--plain-log", help="bench.py output of an unprofiled run (with --summarize-trace)")
+    args = ap.parse_args()
+
+    if args.summarize_mfma:
+        from chunked_gated_delta_token_amd import workloads as W
+        summarize_mfma(args.summarize_mfma, args.op, args.workload or W.BENCH_WORKLOAD, args.chunk)
+        return
+
+    if args.summarize_trace:
+        from chunked_gated_delta_token_amd import workloads as W
+        summarize_trace(args.summarize_trace, args.op, args.workload or W.BENCH_WORKLOAD, args.run_log,
+                        args.plain_log, args.chunk)
+        return
+
+    if args.summarize_traffic:
+        from chunked_gated_delta_token_amd import workloads as W
+        summarize_traffic(args.summarize_traffic, args.copy_bytes, args.op, args.workload or W.BENCH_WORKLOAD,
+                          args.chunk)
+        return
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the fused KKT + solve has no cross-GPU step, and this "
+              "build runs on a single MI355X (run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, args.steps)
+        return
+
+    from chunked_gated_delta_token_amd import workloads as W
+
+    name = args.workload or W.BENCH_WORKLOAD
+    op, chunk = args.op, args.chunk
+    m = measure(name, op, chunk, args.steps, args.warmup, args.timing, args.detail)
+    inp, w, nbytes, R = m["inp"], m["w"], m["nbytes"], m["R"]
+    ms_per_step, ev_ms, n_tiles, key = m["ms_per_step"], m["ev_ms"], m["n_tiles"], m["key"]
+    K = args.steps
+    achieved = nbytes / (ev_ms * 1e-3) / 1e9
+    digest = source_digest()
+    traffic = None if op == "chain" else read_traffic(digest, traffic_file(key, name))
     value = nbytes / (ms_per_step * 1e-3) / 1e9
     metric = METRIC if (op == "fused" and chunk == 64 and name == W.BENCH_WORKLOAD) else {
         "fused": f"fused KKT+solve{' with 128-token chunks' if chunk == 128 else ''} ms/iter & achieved HBM "
@@ -661,10 +695,24 @@ def main():
                    "chunks_per_s": round(n_tiles / (ms_per_step * 1e-3), 1)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": KERNELS[key] if op == "chain" else kernel_name(key, name),
-                     "event_ms_per_step": round(ev_ms, 6), "launches_per_step": len(calls[0]),
+                     "kernel": m["kernel"],
+                     "event_ms_per_step": round(ev_ms, 6), "launches_per_step": 2 if op == "chain" else 1,
                      "kernel_source_sha256_16": digest},
     }
+    if op == "fused" and chunk == 64 and name == W.BENCH_WORKLOAD and not args.no_second_target:
+        # the second shape of the target, timed the same way in the same run
+        m2 = measure(SECOND_TARGET, "fused", 64, args.steps, min(args.warmup, 20), args.timing, args.detail)
+        w2 = m2["w"]
+        ach2 = m2["nbytes"] / (m2["ev_ms"] * 1e-3) / 1e9
+        line["second_target"] = {
+            "workload": SECOND_TARGET, "B": w2.B, "T": w2.T, "H": w2.H, "K": w2.K, "in_dtype": w2.in_dtype,
+            "out_dtype": w2.out_dtype, "tiles": m2["n_tiles"], "algorithmic_bytes": m2["nbytes"],
+            "buffer_sets": m2["R"], "steps": args.steps, "ms_per_step": round(m2["ms_per_step"], 6),
+            "value": round(m2["nbytes"] / (m2["ms_per_step"] * 1e-3) / 1e9, 2), "unit": "GB/s",
+            "event_ms_per_step": round(m2["ev_ms"], 6), "achieved": round(ach2, 2),
+            "frac": round(ach2 / HBM_PEAK_GBS, 4), "kernel": m2["kernel"],
+            "traffic": read_traffic(digest, traffic_file("fused", SECOND_TARGET)),
+            "vs_baseline": round(PAGES_FUSED_MS_SECOND / m2["ms_per_step"], 3)}
     mf = None if op == "chain" else read_mfma(digest, mfma_file(key, name))
     if mf is not None:
         # matrix-core use of the step, from the committed counter summary and

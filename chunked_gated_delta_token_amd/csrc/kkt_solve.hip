@@ -63,12 +63,12 @@
 #include <stdlib.h>
 #include <string.h>
 
-#include <mutex>
+#include <atomic>
 #include <string>
 
 #include "kkt_solve.h"
 
-#define KKT_VERSION_NUMBER 700  // 0.7.0
+#define KKT_VERSION_NUMBER 800  // 0.8.0
 
 namespace {
 
@@ -115,6 +115,21 @@ __device__ __forceinline__ void wave_lds_sync()
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes)
 {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRawBufferFlags);
+}
+
+// The resource for k-step s (64 bytes of a key row) of a tile whose kernel
+// is built for K_T: the tile's own for s < k_steps, one of zero length beyond
+// (every load through it returns 0).  A kernel built for K_T serves every K
+// that is a multiple of 32 in (K_T / 2, K_T] (K_T = 64: also K = 32), so the
+// steps of K_T / 2 + 32 elements are always present and need no select; the
+// others take a scalar select (k_steps is wave-uniform).
+template <int K_T, int ELT_BYTES>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t k_step_rsrc(__amdgpu_buffer_rsrc_t r, int s, int k_steps)
+{
+    constexpr int kMinK = (K_T == 64) ? 32 : K_T / 2 + 32;
+    constexpr int kAlways = kMinK * ELT_BYTES / 64;
+    if (s < kAlways) return r;
+    return (s < k_steps) ? r : __builtin_amdgcn_make_buffer_rsrc(nullptr, 0, 0, kRawBufferFlags);
 }
 
 // ---------------------------------------------------------------- element types
@@ -259,6 +274,9 @@ struct KernelArgs {
     float* g_out;               // gate-sum kernel: where the summed gate goes, or nullptr
     int32_t split_tiles;        // host only: launch the fused op's two-wave-per-tile form
     int32_t tile_waves;         // one-wave-per-tile kernels: waves (tiles) per workgroup, 1 or 4
+    int32_t k_steps;            // 64-byte k-steps of one key row (K * element size / 64); the
+                                // kernel's template K may be larger: its further steps read as 0
+    uint32_t k_head_bytes;      // bytes of one key row of one head (K * element size)
 };
 
 // ---------------------------------------------------------------- tile map (a1)
@@ -512,8 +530,8 @@ __device__ __forceinline__ void chunk_rows(const KernelArgs& args, WaveLds& lds,
         float gv = 0.0f, bv = 1.0f, g_first = 0.0f;
         u32x4 frag[4][kSteps];
         const __amdgpu_buffer_rsrc_t k_rsrc = make_rsrc(
-            static_cast<const char*>(args.k) + tok * (int64_t)(K * kInBytes),
-            (uint32_t)(L - 1) * args.k_row_bytes + K * kInBytes);
+            static_cast<const char*>(args.k) + tok * (int64_t)args.k_head_bytes,
+            (uint32_t)(L - 1) * args.k_row_bytes + args.k_head_bytes);
 
         // ---- a3: g and beta, one row per lane (rows >= L read as 0).  Issued
         // before the K tile: loads complete in order, so waiting for these two
@@ -541,12 +559,15 @@ __device__ __forceinline__ void chunk_rows(const KernelArgs& args, WaveLds& lds,
         // marked streaming (the lines must survive in L2 until then).  The
         // scheduling barrier keeps every load ahead of the first MFMA, so the
         // whole tile is in flight at once.
+        // (k-steps at or beyond args.k_steps, when K is below the template's
+        // K, are read through a zero-length resource: they return zeros,
+        // which add exact zeros to the Gram)
 #pragma unroll
         for (int bi = 0; bi < 4; ++bi) {
             const uint32_t voff = (row_base + (uint32_t)(16 * bi + m)) * args.k_row_bytes + q * 16;
 #pragma unroll
             for (int s = 0; s < kSteps; ++s) {
-                frag[bi][s] = __builtin_amdgcn_raw_buffer_load_b128(k_rsrc, voff + s * 64, 0, 0);
+                frag[bi][s] = __builtin_amdgcn_raw_buffer_load_b128(k_step_rsrc<K, kInBytes>(k_rsrc, s, args.k_steps), voff + s * 64, 0, 0);
             }
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -1145,8 +1166,8 @@ __device__ __forceinline__ void cross_block_rows(const KernelArgs& args, GateLds
     const int q = lane / 16;
     const int m = lane % 16;
     const __amdgpu_buffer_rsrc_t k_rsrc = make_rsrc(
-        static_cast<const char*>(args.k) + tok * (int64_t)(K * kInBytes),
-        (uint32_t)(L - 1) * args.k_row_bytes + K * kInBytes);
+        static_cast<const char*>(args.k) + tok * (int64_t)args.k_head_bytes,
+        (uint32_t)(L - 1) * args.k_row_bytes + args.k_head_bytes);
     in = cross_gate_beta(args, lane, tok, L);
     if (GATE_SUM && args.g != nullptr) cross_gate_sum(in, lane);
 #pragma unroll
@@ -1161,13 +1182,19 @@ __device__ __forceinline__ void cross_block_rows(const KernelArgs& args, GateLds
         for (int bi = 0; bi < 2; ++bi) {
             const uint32_t voff = (uint32_t)(64 + 32 * w2 + 16 * bi + m) * args.k_row_bytes + q * 16;
 #pragma unroll
-            for (int s = 0; s < kPass; ++s) fr[bi][s] = __builtin_amdgcn_raw_buffer_load_b128(k_rsrc, voff + (p0 + s) * 64, 0, 0);
+            for (int s = 0; s < kPass; ++s) {
+                fr[bi][s] = __builtin_amdgcn_raw_buffer_load_b128(k_step_rsrc<K, kInBytes>(k_rsrc, p0 + s, args.k_steps),
+                                                                  voff + (p0 + s) * 64, 0, 0);
+            }
         }
 #pragma unroll
         for (int bj = 0; bj < 4; ++bj) {
             const uint32_t voff = (uint32_t)(16 * bj + m) * args.k_row_bytes + q * 16;
 #pragma unroll
-            for (int s = 0; s < kPass; ++s) fc[bj][s] = __builtin_amdgcn_raw_buffer_load_b128(k_rsrc, voff + (p0 + s) * 64, 0, 0);
+            for (int s = 0; s < kPass; ++s) {
+                fc[bj][s] = __builtin_amdgcn_raw_buffer_load_b128(k_step_rsrc<K, kInBytes>(k_rsrc, p0 + s, args.k_steps),
+                                                                  voff + (p0 + s) * 64, 0, 0);
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
         cross_gram<IN, kPass>(fr, fc, acc);
@@ -1303,8 +1330,8 @@ void kkt_solve128_kernel(const KernelArgs args)
             // has fetched them by then (L2 hits), and issued at the start
             // they would queue in front of the loads of waves 0 and 1
             const __amdgpu_buffer_rsrc_t k_rsrc = make_rsrc(
-                static_cast<const char*>(args.k) + tok * (int64_t)(K * kInBytes),
-                (uint32_t)(L - 1) * args.k_row_bytes + K * kInBytes);
+                static_cast<const char*>(args.k) + tok * (int64_t)args.k_head_bytes,
+                (uint32_t)(L - 1) * args.k_row_bytes + args.k_head_bytes);
             cin = cross_gate_beta(args, lane, tok, L);
             if (GATE_SUM && args.g != nullptr) cross_gate_sum(cin, lane);
 #pragma unroll
@@ -1318,7 +1345,10 @@ void kkt_solve128_kernel(const KernelArgs args)
             for (int bi = 0; bi < 2; ++bi) {
                 const uint32_t voff = (uint32_t)(64 + 32 * w2 + 16 * bi + m) * args.k_row_bytes + q * 16;
 #pragma unroll
-                for (int s = 0; s < kSteps; ++s) fr[bi][s] = __builtin_amdgcn_raw_buffer_load_b128(k_rsrc, voff + s * 64, 0, 0);
+                for (int s = 0; s < kSteps; ++s) {
+                    fr[bi][s] = __builtin_amdgcn_raw_buffer_load_b128(k_step_rsrc<K, kInBytes>(k_rsrc, s, args.k_steps),
+                                                                      voff + s * 64, 0, 0);
+                }
             }
             constexpr int kPer = (IN == Elt::F32) ? 2 : 1;  // fragments per Gram step
 #pragma unroll
@@ -1440,10 +1470,11 @@ kkt_status_t fail(kkt_status_t st, const std::string& msg)
     return st;
 }
 
-// Per-device "is gfx950" cache: 0 unknown, 1 yes, 2 no.
+// Per-device "is gfx950" cache: 0 unknown, 1 yes, 2 no.  Lock-free: two
+// threads that find it unknown both query the device and store the same
+// value.
 constexpr int kMaxDevices = 64;
-int g_arch_ok[kMaxDevices];
-std::mutex g_arch_mutex;
+std::atomic<int> g_arch_ok[kMaxDevices];
 
 kkt_status_t check_device()
 {
@@ -1451,14 +1482,15 @@ kkt_status_t check_device()
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return fail(KKT_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
     if (dev < 0 || dev >= kMaxDevices) return fail(KKT_ERR_UNSUPPORTED, "device index out of range");
-    std::lock_guard<std::mutex> lock(g_arch_mutex);
-    if (g_arch_ok[dev] == 0) {
+    int ok = g_arch_ok[dev].load(std::memory_order_relaxed);
+    if (ok == 0) {
         hipDeviceProp_t prop;
         e = hipGetDeviceProperties(&prop, dev);
         if (e != hipSuccess) return fail(KKT_ERR_HIP, std::string("hipGetDeviceProperties: ") + hipGetErrorString(e));
-        g_arch_ok[dev] = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+        ok = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+        g_arch_ok[dev].store(ok, std::memory_order_relaxed);
     }
-    if (g_arch_ok[dev] != 1) return fail(KKT_ERR_UNSUPPORTED, "device is not gfx950 (MI355X); this library is built for gfx950 only");
+    if (ok != 1) return fail(KKT_ERR_UNSUPPORTED, "device is not gfx950 (MI355X); this library is built for gfx950 only");
     return KKT_OK;
 }
 
@@ -1477,6 +1509,10 @@ kkt_status_t validate_cu_seqlens(const int32_t* cu, int64_t num_seqs, int64_t T,
     return KKT_OK;
 }
 
+// The kernels are built for K = 64, 128 and 256; a smaller K that is a
+// multiple of 32 runs in the next one up, with its missing k-steps read as 0.
+int64_t k_bucket(int64_t K) { return K <= 64 ? 64 : (K <= 128 ? 128 : 256); }
+
 // waves: the workgroup size in waves; the one-wave-per-tile kernels take
 // a.tile_waves (their default), the others name theirs
 hipError_t launch(void (*kernel)(KernelArgs), const KernelArgs& a, hipStream_t stream, int waves = 0)
@@ -1490,6 +1526,7 @@ hipError_t launch(void (*kernel)(KernelArgs), const KernelArgs& a, hipStream_t s
 template <Elt IN, Elt OUT, bool GATE_SUM>
 hipError_t launch_fused(int64_t K, const KernelArgs& a, hipStream_t stream)
 {
+    K = k_bucket(K);
     if constexpr (GATE_SUM) {
         if (a.split_tiles) {
             switch (K) {
@@ -1529,6 +1566,7 @@ hipError_t launch_fused128_k(const KernelArgs& a, hipStream_t stream)
 template <Elt IN, Elt OUT, bool GATE_SUM>
 hipError_t launch_fused128(int64_t K, const KernelArgs& a, hipStream_t stream)
 {
+    K = k_bucket(K);
     switch (K) {
     case 64: return launch_fused128_k<IN, OUT, 64, GATE_SUM>(a, stream);
     case 128: return launch_fused128_k<IN, OUT, 128, GATE_SUM>(a, stream);
@@ -1556,6 +1594,7 @@ hipError_t launch_fused_out(kkt_dtype_t od, int64_t K, int64_t chunk, const Kern
 template <Elt IN>
 hipError_t launch_scaled_dot(int64_t K, const KernelArgs& a, hipStream_t stream)
 {
+    K = k_bucket(K);
     switch (K) {
     case 64: return launch(kkt_scaled_dot_kernel<IN, 64>, a, stream);
     case 128: return launch(kkt_scaled_dot_kernel<IN, 128>, a, stream);
@@ -1564,6 +1603,7 @@ hipError_t launch_scaled_dot(int64_t K, const KernelArgs& a, hipStream_t stream)
 }
 
 bool valid_dtype(int d) { return d == KKT_DTYPE_F32 || d == KKT_DTYPE_BF16 || d == KKT_DTYPE_F16; }
+
 int64_t dtype_bytes(kkt_dtype_t d) { return d == KKT_DTYPE_F32 ? 4 : 2; }
 
 // Grids up to this many workgroups use the XCD-contiguous tile order; larger
@@ -1596,11 +1636,18 @@ constexpr int64_t kSplitMaxTiles = 256;
 // 80.2; 1876: 20.0 vs 21.0-21.4).
 constexpr int64_t kWave1GroupTilesFused = 1024;  // kkt_solve
 constexpr int64_t kWave1GroupTiles = 512;        // the other entry points
-int64_t split_max_tiles()
+
+// Process-wide options (kkt_set_option).  Their start values come from the
+// environment, read once when the library is loaded: KKT_SPLIT_TILES (the
+// two-wave bound above) and KKT_VALIDATE=1 (check cu_seqlens on the host).
+int64_t env_int(const char* name, int64_t fallback)
 {
-    const char* v = getenv("KKT_SPLIT_TILES");
-    return (v != nullptr && v[0] != '\0') ? strtoll(v, nullptr, 10) : kSplitMaxTiles;
+    const char* v = getenv(name);
+    return (v != nullptr && v[0] != '\0') ? strtoll(v, nullptr, 10) : fallback;
 }
+std::atomic<int64_t> g_split_max_tiles{env_int("KKT_SPLIT_TILES", kSplitMaxTiles)};
+std::atomic<int64_t> g_validate_cu_seqlens{env_int("KKT_VALIDATE", 0) == 1 ? 1 : 0};
+int64_t split_max_tiles() { return g_split_max_tiles.load(std::memory_order_relaxed); }
 
 // Checks shared by every entry point and the launch geometry.  in_row_bytes
 // and out_row_bytes are the strides between consecutive tokens of one head;
@@ -1639,12 +1686,9 @@ kkt_status_t setup(KernelArgs& a, const void* in, const float* g, const float* b
 
     kkt_status_t st = check_device();
     if (st != KKT_OK) return st;
-    if (cu_seqlens != nullptr) {
-        const char* v = getenv("KKT_VALIDATE");
-        if (v != nullptr && v[0] == '1') {
-            st = validate_cu_seqlens(cu_seqlens, num_seqs, T, stream);
-            if (st != KKT_OK) return st;
-        }
+    if (cu_seqlens != nullptr && g_validate_cu_seqlens.load(std::memory_order_relaxed) != 0) {
+        st = validate_cu_seqlens(cu_seqlens, num_seqs, T, stream);
+        if (st != KKT_OK) return st;
     }
 
     a.k = in;
@@ -1671,6 +1715,8 @@ kkt_status_t setup(KernelArgs& a, const void* in, const float* g, const float* b
     a.g_out = nullptr;
     a.split_tiles = split ? 1 : 0;
     a.tile_waves = (int32_t)tiles_per_group;
+    a.k_head_bytes = (uint32_t)(in_row_bytes / H);
+    a.k_steps = (int32_t)(a.k_head_bytes / 64);
     return KKT_OK;
 }
 
@@ -1678,7 +1724,7 @@ kkt_status_t setup(KernelArgs& a, const void* in, const float* g, const float* b
 kkt_status_t check_k_sizes(int64_t B, int64_t T, int64_t H, int64_t K, int64_t num_seqs, const int32_t* cu_seqlens)
 {
     if (B < 1 || H < 1 || K < 1 || T < 0) return fail(KKT_ERR_INVALID_ARGUMENT, "B, H, K must be >= 1 and T >= 0");
-    if (K != 64 && K != 128 && K != 256) return fail(KKT_ERR_UNSUPPORTED, "K must be 64, 128 or 256");
+    if (K % 32 != 0 || K > 256) return fail(KKT_ERR_UNSUPPORTED, "K must be a multiple of 32 up to 256");
     if (cu_seqlens != nullptr && (B != 1 || num_seqs < 1)) {
         return fail(KKT_ERR_INVALID_ARGUMENT, "cu_seqlens needs B == 1 and num_seqs >= 1");
     }
@@ -1805,6 +1851,30 @@ extern "C" kkt_status_t kkt_solve_tril(const float* A, const int32_t* cu_seqlens
     }
     if (e != hipSuccess) return fail(KKT_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(e));
     return KKT_OK;
+}
+
+extern "C" kkt_status_t kkt_set_option(kkt_option_t option, int64_t value)
+{
+    g_last_error.clear();
+    switch (option) {
+    case KKT_OPTION_SPLIT_MAX_TILES:
+        if (value < 0) return fail(KKT_ERR_INVALID_ARGUMENT, "KKT_OPTION_SPLIT_MAX_TILES must be >= 0");
+        g_split_max_tiles.store(value, std::memory_order_relaxed);
+        return KKT_OK;
+    case KKT_OPTION_VALIDATE_CU_SEQLENS:
+        g_validate_cu_seqlens.store(value != 0 ? 1 : 0, std::memory_order_relaxed);
+        return KKT_OK;
+    }
+    return fail(KKT_ERR_INVALID_ARGUMENT, "unknown option");
+}
+
+extern "C" int64_t kkt_get_option(kkt_option_t option)
+{
+    switch (option) {
+    case KKT_OPTION_SPLIT_MAX_TILES: return g_split_max_tiles.load(std::memory_order_relaxed);
+    case KKT_OPTION_VALIDATE_CU_SEQLENS: return g_validate_cu_seqlens.load(std::memory_order_relaxed);
+    }
+    return -1;
 }
 
 extern "C" const char* kkt_last_error(void) { return g_last_error.c_str(); }

@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(_PKG, "libkkt_solve.so")
 
 KKT_DTYPE_F32, KKT_DTYPE_BF16, KKT_DTYPE_F16 = 0, 1, 2
 KKT_OK, KKT_ERR_INVALID_ARGUMENT, KKT_ERR_UNSUPPORTED, KKT_ERR_HIP = 0, 1, 2, 3
+KKT_OPTION_SPLIT_MAX_TILES, KKT_OPTION_VALIDATE_CU_SEQLENS = 0, 1
 
 _TORCH_TO_KKT = {torch.float32: KKT_DTYPE_F32, torch.bfloat16: KKT_DTYPE_BF16, torch.float16: KKT_DTYPE_F16}
 
@@ -37,6 +38,8 @@ SIGNATURES = {
     "kkt_solve_tril": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                       ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                       ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]),
+    "kkt_set_option": (ctypes.c_int, [ctypes.c_int, ctypes.c_int64]),
+    "kkt_get_option": (ctypes.c_int64, [ctypes.c_int]),
     "kkt_last_error": (ctypes.c_char_p, []),
     "kkt_version": (ctypes.c_int, []),
 }
@@ -96,12 +99,47 @@ def kkt_solve_raw(k_ptr, g_ptr, beta_ptr, cu_ptr, num_seqs, B, T, H, K, chunk_si
                          out_dtype, out_ptr, stream_ptr)
 
 
+def set_option(option: int, value: int) -> None:
+    """Process-wide library option (KKT_OPTION_SPLIT_MAX_TILES,
+    KKT_OPTION_VALIDATE_CU_SEQLENS); raises on an invalid option or value."""
+    st = load_library().kkt_set_option(option, int(value))
+    if st != KKT_OK:
+        raise _error(st)
+
+
+def get_option(option: int) -> int:
+    return int(load_library().kkt_get_option(option))
+
+
+class option:
+    """Context manager that sets an option and restores its previous value."""
+
+    def __init__(self, opt: int, value: int):
+        self.opt, self.value, self.old = opt, value, None
+
+    def __enter__(self):
+        self.old = get_option(self.opt)
+        set_option(self.opt, self.value)
+        return self
+
+    def __exit__(self, *exc):
+        set_option(self.opt, self.old)
+        return False
+
+
 def last_error() -> str:
     return load_library().kkt_last_error().decode()
 
 
 def version() -> int:
     return int(load_library().kkt_version())
+
+
+def _check_k(k):
+    if not isinstance(k, torch.Tensor) or k.dim() != 4:
+        raise ValueError("k must be [B, T, H, K]")
+    if not k.is_cuda:
+        raise ValueError("k must be a device tensor")
 
 
 def _k_inputs(k, g, beta, cu_seqlens, chunk_size, chunk_sizes=(64,)):
@@ -143,9 +181,45 @@ def _out_tensor(out, shape, dtype, device):
     return out
 
 
-def _stream_ptr(stream, device):
-    s = stream if stream is not None else torch.cuda.current_stream(device)
-    return ctypes.c_void_p(s.cuda_stream)
+class _OnStream:
+    """Runs a call's copies, allocations and launch on the launch stream.
+
+    With no stream given that is the current stream, and nothing more is
+    needed.  With another stream, that stream first waits for the current
+    one (the caller produced the inputs there), the contiguous copies and
+    the outputs are made under it (so the caching allocator ties them to it),
+    and on exit every caller tensor the launch touches is recorded on it, so
+    its memory is not handed to new work before the launch is done with it.
+    """
+
+    def __init__(self, stream, device):
+        self.device = device
+        self.cur = torch.cuda.current_stream(device)
+        self.stream = stream if stream is not None else self.cur
+        self.side = self.stream != self.cur
+        self.keep = []
+        self._ctx = None
+
+    def __enter__(self):
+        if self.side:
+            self.stream.wait_stream(self.cur)
+        self._ctx = torch.cuda.stream(self.stream)
+        self._ctx.__enter__()
+        return self
+
+    def uses(self, *tensors):
+        """Caller tensors the launch reads or writes (None entries ignored)."""
+        self.keep.extend(t for t in tensors if t is not None)
+
+    def ptr(self):
+        return ctypes.c_void_p(self.stream.cuda_stream)
+
+    def __exit__(self, *exc):
+        self._ctx.__exit__(*exc)
+        if self.side:
+            for t in self.keep:
+                t.record_stream(self.stream)
+        return False
 
 
 def kkt_solve(k: torch.Tensor, g: Optional[torch.Tensor] = None, beta: Optional[torch.Tensor] = None,
@@ -163,15 +237,17 @@ def kkt_solve(k: torch.Tensor, g: Optional[torch.Tensor] = None, beta: Optional[
     [B,T,H,chunk_size]); otherwise it is allocated uninitialised, since the
     kernel writes every element.
     """
-    k, g, beta, cu_seqlens, num_seqs = _k_inputs(k, g, beta, cu_seqlens, chunk_size, (64, 128))
-    B, T, H, K = k.shape
+    _check_k(k)
     odt = k.dtype if output_dtype is None else output_dtype
     if odt not in _TORCH_TO_KKT:
         raise TypeError(f"unsupported output dtype {odt}")
-    out = _out_tensor(out, (B, T, H, chunk_size), odt, k.device)
-    with torch.cuda.device(k.device):
+    with torch.cuda.device(k.device), _OnStream(stream, k.device) as on:
+        on.uses(k, g, beta, cu_seqlens, out)
+        k, g, beta, cu_seqlens, num_seqs = _k_inputs(k, g, beta, cu_seqlens, chunk_size, (64, 128))
+        B, T, H, K = k.shape
+        out = _out_tensor(out, (B, T, H, chunk_size), odt, k.device)
         st = kkt_solve_raw(_ptr(k), _ptr(g), _ptr(beta), _ptr(cu_seqlens), num_seqs, B, T, H, K, chunk_size,
-                           _TORCH_TO_KKT[k.dtype], _TORCH_TO_KKT[odt], _ptr(out), _stream_ptr(stream, k.device))
+                           _TORCH_TO_KKT[k.dtype], _TORCH_TO_KKT[odt], _ptr(out), on.ptr())
     if st != KKT_OK:
         raise _error(st)
     return out
@@ -190,20 +266,23 @@ def kkt_solve_gate_cumsum(k: torch.Tensor, g_decay: torch.Tensor, beta: Optional
     ``kkt_solve``."""
     if g_decay is None:
         raise ValueError("g_decay is required (use kkt_solve without a gate)")
-    k, g_decay, beta, cu_seqlens, num_seqs = _k_inputs(k, g_decay, beta, cu_seqlens, chunk_size, (64, 128))
-    B, T, H, K = k.shape
+    _check_k(k)
     odt = k.dtype if output_dtype is None else output_dtype
     if odt not in _TORCH_TO_KKT:
         raise TypeError(f"unsupported output dtype {odt}")
-    out = _out_tensor(out, (B, T, H, chunk_size), odt, k.device)
-    if g_out is None and return_gate:
-        g_out = torch.empty((B, T, H), dtype=torch.float32, device=k.device)
-    elif g_out is not None:
-        g_out = _out_tensor(g_out, (B, T, H), torch.float32, k.device)
-    with torch.cuda.device(k.device):
+    if g_out is not None and not (g_out.is_contiguous() and g_out.dtype == torch.float32
+                                  and g_out.shape == k.shape[:3] and g_out.device == k.device):
+        raise ValueError(f"g_out must be contiguous {list(k.shape[:3])} of dtype torch.float32 on k's device")
+    with torch.cuda.device(k.device), _OnStream(stream, k.device) as on:
+        on.uses(k, g_decay, beta, cu_seqlens, out, g_out)
+        k, g_decay, beta, cu_seqlens, num_seqs = _k_inputs(k, g_decay, beta, cu_seqlens, chunk_size, (64, 128))
+        B, T, H, K = k.shape
+        out = _out_tensor(out, (B, T, H, chunk_size), odt, k.device)
+        if g_out is None and return_gate:
+            g_out = torch.empty((B, T, H), dtype=torch.float32, device=k.device)
         st = load_library().kkt_solve_gate_cumsum(_ptr(k), _ptr(g_decay), _ptr(beta), _ptr(cu_seqlens), num_seqs,
                                                   B, T, H, K, chunk_size, _TORCH_TO_KKT[k.dtype], _TORCH_TO_KKT[odt],
-                                                  _ptr(out), _ptr(g_out), _stream_ptr(stream, k.device))
+                                                  _ptr(out), _ptr(g_out), on.ptr())
     if st != KKT_OK:
         raise _error(st)
     return (out, g_out) if g_out is not None else out
@@ -217,13 +296,14 @@ def kkt_scaled_dot(k: torch.Tensor, g: Optional[torch.Tensor] = None, beta: Opti
     every 64-token chunk, fp32 [B, T, H, 64], zeros on and above the diagonal
     (MindSpeed-Ops PR #135, PR description: chunk_scaled_dot_kkt_fwd).
     Arguments as for ``kkt_solve``."""
-    k, g, beta, cu_seqlens, num_seqs = _k_inputs(k, g, beta, cu_seqlens, chunk_size)
-    B, T, H, K = k.shape
-    out = _out_tensor(out, (B, T, H, 64), torch.float32, k.device)
-    with torch.cuda.device(k.device):
+    _check_k(k)
+    with torch.cuda.device(k.device), _OnStream(stream, k.device) as on:
+        on.uses(k, g, beta, cu_seqlens, out)
+        k, g, beta, cu_seqlens, num_seqs = _k_inputs(k, g, beta, cu_seqlens, chunk_size)
+        B, T, H, K = k.shape
+        out = _out_tensor(out, (B, T, H, 64), torch.float32, k.device)
         st = load_library().kkt_scaled_dot(_ptr(k), _ptr(g), _ptr(beta), _ptr(cu_seqlens), num_seqs, B, T, H, K,
-                                           chunk_size, _TORCH_TO_KKT[k.dtype], _ptr(out),
-                                           _stream_ptr(stream, k.device))
+                                           chunk_size, _TORCH_TO_KKT[k.dtype], _ptr(out), on.ptr())
     if st != KKT_OK:
         raise _error(st)
     return out
@@ -240,16 +320,17 @@ def kkt_solve_tril(A: torch.Tensor, cu_seqlens: Optional[torch.Tensor] = None, c
         raise ValueError("chunk_size must be 64")
     if A.dim() != 4 or A.shape[3] != 64 or A.dtype != torch.float32 or not A.is_cuda:
         raise ValueError("A must be a float32 device tensor [B, T, H, 64]")
-    A = A.contiguous()
-    B, T, H, _ = A.shape
-    cu_seqlens, num_seqs = _cu_input(cu_seqlens, A.device)
     odt = torch.float32 if output_dtype is None else output_dtype
     if odt not in _TORCH_TO_KKT:
         raise TypeError(f"unsupported output dtype {odt}")
-    out = _out_tensor(out, (B, T, H, 64), odt, A.device)
-    with torch.cuda.device(A.device):
+    with torch.cuda.device(A.device), _OnStream(stream, A.device) as on:
+        on.uses(A, cu_seqlens, out)
+        A = A.contiguous()
+        B, T, H, _ = A.shape
+        cu_seqlens, num_seqs = _cu_input(cu_seqlens, A.device)
+        out = _out_tensor(out, (B, T, H, 64), odt, A.device)
         st = load_library().kkt_solve_tril(_ptr(A), _ptr(cu_seqlens), num_seqs, B, T, H, chunk_size,
-                                           _TORCH_TO_KKT[odt], _ptr(out), _stream_ptr(stream, A.device))
+                                           _TORCH_TO_KKT[odt], _ptr(out), on.ptr())
     if st != KKT_OK:
         raise _error(st)
     return out

@@ -23,7 +23,8 @@
  *   (no pre-zeroed output is needed).
  *
  * Threading: every entry point is thread-safe; the library keeps no state
- * besides a per-thread error string and a per-device architecture cache.
+ * besides a per-thread error string, a per-device architecture cache and the
+ * two process-wide options of kkt_set_option.
  */
 #ifndef KKT_SOLVE_H
 #define KKT_SOLVE_H
@@ -69,11 +70,14 @@ typedef enum {
  *              The kernel clamps every offset into [0, T], so malformed
  *              offsets cannot make it access memory outside the tensors; rows
  *              not covered by any sequence are then left unwritten.  With the
- *              environment variable KKT_VALIDATE=1 the offsets are copied to the
- *              host (synchronously) and checked first.
+ *              option KKT_OPTION_VALIDATE_CU_SEQLENS set (kkt_set_option) the
+ *              offsets are copied to the host (synchronously) and checked
+ *              first.
  *   num_seqs   number of sequences; ignored when cu_seqlens is NULL.
  *   B, T, H, K sizes.  T may be 0 (nothing is launched).
- *              K must be 64, 128 or 256.
+ *              K must be a multiple of 32 from 32 to 256 (any key dtype); the
+ *              PR #135 page shows K = 128 only, the rest is this library's
+ *              range (KKT_ERR_UNSUPPORTED otherwise).
  *   chunk_size 64 or 128 (the chunk length; also the width of an output row).
  *   in_dtype   element type of k.
  *   out_dtype  element type of out.  bf16 / f16 results are rounded to nearest
@@ -95,8 +99,8 @@ typedef enum {
  *
  * Launch form (chunk_size 64): grids of up to 256 chunk-head tiles run each
  * tile on two waves, larger grids one tile per wave; both give bit-identical
- * results.  The environment variable KKT_SPLIT_TILES, read on every call,
- * replaces the 256 (0: always one wave per tile).
+ * results.  The option KKT_OPTION_SPLIT_MAX_TILES replaces the 256 (0: always
+ * one wave per tile).
  *
  * All pointers are owned by the caller; the library allocates nothing and
  * keeps no pointer after the call returns.  The call is asynchronous: it
@@ -184,6 +188,37 @@ kkt_status_t kkt_scaled_dot(const void* k, const float* g, const float* beta,
 kkt_status_t kkt_solve_tril(const float* A, const int32_t* cu_seqlens, int64_t num_seqs,
                             int64_t B, int64_t T, int64_t H, int64_t chunk_size,
                             kkt_dtype_t out_dtype, void* out, hipStream_t stream);
+
+/*
+ * Process-wide options.  They change how calls are carried out, never what
+ * they compute; they exist for tests and debugging.  A value set takes effect
+ * for calls that start after kkt_set_option returns (it is an atomic store;
+ * calls already running on other threads may use either value).  Start
+ * values are read once, when the library is loaded, from the environment
+ * variables named below.
+ *
+ *   KKT_OPTION_SPLIT_MAX_TILES      grids of up to this many 64-token
+ *                                   chunk-head tiles run each tile on two
+ *                                   waves (the launch form above); 0: never.
+ *                                   Default 256 (env KKT_SPLIT_TILES).
+ *   KKT_OPTION_VALIDATE_CU_SEQLENS  nonzero: every call with cu_seqlens first
+ *                                   copies the offsets to the host
+ *                                   (synchronously, on the call's stream) and
+ *                                   returns KKT_ERR_INVALID_ARGUMENT unless
+ *                                   they start at 0, do not decrease and end
+ *                                   at T.  Default 0 (env KKT_VALIDATE=1: on).
+ *
+ * kkt_set_option returns KKT_ERR_INVALID_ARGUMENT for an unknown option or a
+ * negative KKT_OPTION_SPLIT_MAX_TILES; kkt_get_option returns the current
+ * value, or -1 for an unknown option.
+ */
+typedef enum {
+    KKT_OPTION_SPLIT_MAX_TILES = 0,
+    KKT_OPTION_VALIDATE_CU_SEQLENS = 1
+} kkt_option_t;
+
+kkt_status_t kkt_set_option(kkt_option_t option, int64_t value);
+int64_t kkt_get_option(kkt_option_t option);
 
 /* Text of the last non-OK status returned on the calling thread ("" if none).
  * The pointer stays valid until the next kkt_* call on the same thread. */

@@ -21,6 +21,10 @@ import oracle
 from chunked_gated_delta_token_amd import workloads
 
 MAX_ABS_F32 = 2e-4
+# Summed gate (the gate-sum entry point): within GATE_BOUND_ULPS 2^-24 of the
+# running sum of |decay| (a 6-level fp32 tree sum has first-order error at
+# most 6 2^-24 times that sum; 8 leaves room for the higher-order terms).
+GATE_BOUND_ULPS = 8
 MRE_F32 = 1e-5
 FLOOR_16 = 2.0 ** -23
 ONE_BITS = {"bf16": 0x3F80, "f16": 0x3C00}

@@ -33,8 +33,8 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["kkt_last_error", "kkt_scaled_dot", "kkt_solve", "kkt_solve_gate_cumsum",
-                                    "kkt_solve_tril", "kkt_version"]
+    assert declared_functions() == ["kkt_get_option", "kkt_last_error", "kkt_scaled_dot", "kkt_set_option",
+                                    "kkt_solve", "kkt_solve_gate_cumsum", "kkt_solve_tril", "kkt_version"]
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -48,7 +48,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version(lib):
-    assert lib.kkt_version() == 700
+    assert lib.kkt_version() == 800
 
 
 def _call(lib, **over):
@@ -69,7 +69,10 @@ def _call(lib, **over):
     (dict(H=0), 1, ">= 1"),
     (dict(T=-1), 1, ">= 1"),
     (dict(K=100), 2, "K must be"),
+    (dict(K=16), 2, "K must be"),
+    (dict(K=288), 2, "K must be"),
     (dict(K=512), 2, "K must be"),
+    (dict(K=0), 1, ">= 1"),
     (dict(cu=1, num_seqs=2, B=2), 1, "cu_seqlens"),
     (dict(cu=1, num_seqs=0), 1, "cu_seqlens"),
     (dict(k=None), 1, "NULL"),
@@ -86,6 +89,56 @@ def test_invalid_arguments_rejected_on_host(lib, over, status, msg):
     assert msg in kkt.last_error()
 
 
+@pytest.mark.parametrize("K", [32, 64, 96, 128, 160, 192, 224, 256])
+@pytest.mark.parametrize("in_dtype", [0, 1, 2])
+def test_every_multiple_of_32_up_to_256_passes_the_k_check(lib, K, in_dtype):
+    """Every key dtype takes K = 32, 64, ..., 256: the argument checks pass
+    (without a GPU the call then stops at the device query, not at K)."""
+    from chunked_gated_delta_token_amd import kkt
+    st = _call(lib, K=K, in_dtype=in_dtype)
+    assert st != 1 and "K must be" not in kkt.last_error(), (st, kkt.last_error())
+
+
+def test_options_round_trip_and_reject_bad_values(lib):
+    """kkt_set_option / kkt_get_option: values round-trip, an unknown option
+    or a negative two-wave bound is rejected and leaves the option as it was;
+    the Python context manager restores the previous value."""
+    from chunked_gated_delta_token_amd import kkt
+    split0 = kkt.get_option(kkt.KKT_OPTION_SPLIT_MAX_TILES)
+    val0 = kkt.get_option(kkt.KKT_OPTION_VALIDATE_CU_SEQLENS)
+    assert split0 == int(os.environ.get("KKT_SPLIT_TILES") or 256)
+    try:
+        kkt.set_option(kkt.KKT_OPTION_SPLIT_MAX_TILES, 7)
+        assert kkt.get_option(kkt.KKT_OPTION_SPLIT_MAX_TILES) == 7
+        with pytest.raises(kkt.KKTInvalidArgument):
+            kkt.set_option(kkt.KKT_OPTION_SPLIT_MAX_TILES, -1)
+        assert kkt.get_option(kkt.KKT_OPTION_SPLIT_MAX_TILES) == 7
+        with kkt.option(kkt.KKT_OPTION_SPLIT_MAX_TILES, 0):
+            assert kkt.get_option(kkt.KKT_OPTION_SPLIT_MAX_TILES) == 0
+        assert kkt.get_option(kkt.KKT_OPTION_SPLIT_MAX_TILES) == 7
+        kkt.set_option(kkt.KKT_OPTION_VALIDATE_CU_SEQLENS, 5)
+        assert kkt.get_option(kkt.KKT_OPTION_VALIDATE_CU_SEQLENS) == 1
+        assert lib.kkt_set_option(9, 1) == kkt.KKT_ERR_INVALID_ARGUMENT
+        assert "unknown option" in kkt.last_error()
+        assert lib.kkt_get_option(9) == -1
+    finally:
+        kkt.set_option(kkt.KKT_OPTION_SPLIT_MAX_TILES, split0)
+        kkt.set_option(kkt.KKT_OPTION_VALIDATE_CU_SEQLENS, val0)
+
+
+def test_options_start_from_the_environment(tmp_path):
+    """The start values come from KKT_SPLIT_TILES and KKT_VALIDATE, read when
+    the library is loaded (a fresh process here)."""
+    code = ("import ctypes, sys; lib = ctypes.CDLL(sys.argv[1]); lib.kkt_get_option.restype = ctypes.c_int64; "
+            "print(lib.kkt_get_option(0), lib.kkt_get_option(1))")
+    env = dict(os.environ, KKT_SPLIT_TILES="33", KKT_VALIDATE="1")
+    out = subprocess.run(["python3", "-c", code, LIB], capture_output=True, text=True, env=env, check=True)
+    assert out.stdout.split() == ["33", "1"]
+    env = {k: v for k, v in os.environ.items() if k not in ("KKT_SPLIT_TILES", "KKT_VALIDATE")}
+    out = subprocess.run(["python3", "-c", code, LIB], capture_output=True, text=True, env=env, check=True)
+    assert out.stdout.split() == ["256", "0"]
+
+
 def _call_scaled_dot(lib, **over):
     args = dict(k=16, g=None, beta=None, cu=None, num_seqs=0, B=1, T=64, H=1, K=128, chunk_size=64,
                 in_dtype=1, A=16, stream=None)
@@ -99,7 +152,7 @@ def _call_scaled_dot(lib, **over):
     (dict(chunk_size=128), 2, "chunk_size"),
     (dict(in_dtype=5), 1, "dtype"),
     (dict(H=0), 1, ">= 1"),
-    (dict(K=96), 2, "K must be"),
+    (dict(K=80), 2, "K must be"),
     (dict(cu=16, num_seqs=1, B=3), 1, "cu_seqlens"),
     (dict(k=None), 1, "NULL"),
     (dict(A=None), 1, "NULL"),

@@ -18,13 +18,12 @@ import pytest
 
 import oracle
 from chunked_gated_delta_token_amd import workloads as W
-from tests._compare import compare
+from tests._compare import GATE_BOUND_ULPS, compare
 from tests._gpu_util import TORCH_DT, from_device, load_kkt, say, to_device
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
-GATE_BOUND_ULPS = 8
 
 
 @pytest.fixture(scope="module")
@@ -111,6 +110,12 @@ def test_gate_cumsum_strong_decay_takes_the_clamp(kkt):
 def test_gate_cumsum_dtypes(kkt, in_dtype, out_dtype):
     inp = W.generate("T256_H8_bf16_f32", B=2, T=150, H=3, in_dtype=in_dtype, seed=2300)
     check(kkt, inp, out_dtype, f"{in_dtype}->{out_dtype}")
+
+
+@pytest.mark.parametrize("K,in_dtype,chunk", [(96, "bf16", 64), (160, "f32", 64), (32, "f16", 128), (192, "bf16", 128)])
+def test_gate_cumsum_head_dims(kkt, K, in_dtype, chunk):
+    inp = W.generate("T256_H8_bf16_f32", B=2, T=300, H=3, K=K, in_dtype=in_dtype, seed=2310 + K)
+    check(kkt, inp, "f32", f"K={K} {in_dtype}", chunk=chunk)
 
 
 def test_gate_cumsum_in_place_and_without_gate_output(kkt):

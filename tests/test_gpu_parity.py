@@ -40,6 +40,15 @@ def reference(inp: W.Inputs) -> np.ndarray:
     return oracle.kkt_solve_ref(inp.k64(), inp.g, inp.beta, inp.cu_seqlens)
 
 
+def check_bits(kkt, inp: W.Inputs, out_dtype: str, label: str) -> np.ndarray:
+    """check(), returning the GPU output."""
+    w = inp.workload
+    say(f"[case] {label}: B={w.B} T={w.T} H={w.H} K={w.K} in={w.in_dtype} out={out_dtype}")
+    got = run_gpu(kkt, inp, out_dtype)
+    say("[ok] " + json.dumps(compare(got, reference(inp), out_dtype, inp.cu_seqlens, label)))
+    return got
+
+
 def check(kkt, inp: W.Inputs, out_dtype: str, label: str) -> dict:
     w = inp.workload
     say(f"[case] {label}: B={w.B} T={w.T} H={w.H} K={w.K} in={w.in_dtype} out={out_dtype} "
@@ -83,11 +92,27 @@ def test_gate_beta_variants(kkt, gate, beta):
     check(kkt, inp, "bf16", f"gate={gate} beta={beta} bf16 out")
 
 
-@pytest.mark.parametrize("K", [64, 256])
-@pytest.mark.parametrize("in_dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("K", [32, 64, 96, 160, 192, 224, 256])
+@pytest.mark.parametrize("in_dtype", ["bf16", "f16", "f32"])
 def test_other_head_dims(kkt, K, in_dtype):
+    """Every multiple of 32 up to 256 (K = 128 is every workload's): the
+    kernels are built for 64, 128 and 256 and read the k-steps beyond a
+    smaller K as zeros.  The grid (6 tiles) takes the two-wave tiles; the
+    one-wave form is forced on the same inputs and must give the same bits."""
     inp = W.generate("T256_H8_bf16_f32", T=130, H=2, K=K, in_dtype=in_dtype, seed=400 + K)
-    check(kkt, inp, "f32", f"K={K} {in_dtype}")
+    two = check_bits(kkt, inp, "f32", f"K={K} {in_dtype}")
+    with kkt.option(kkt.KKT_OPTION_SPLIT_MAX_TILES, 0):
+        one = run_gpu(kkt, inp, "f32")
+    assert np.array_equal(one.view(np.uint32), two.view(np.uint32))
+
+
+@pytest.mark.parametrize("K", [96, 160])
+def test_other_head_dims_one_wave_grid(kkt, K):
+    """A K below its kernel's on a grid of one-wave tiles with bf16 output and
+    packed sequences (the last key row of the last head ends the tensor, so
+    the key resource must end at K, not at the kernel's K)."""
+    inp = W.generate("T256_H8_bf16_f32", lengths=[900, 1, 64, 700, 63], H=3, K=K, seed=410 + K)
+    check(kkt, inp, "bf16", f"packed K={K}")
 
 
 def test_large_gate_spread(kkt):
@@ -167,16 +192,22 @@ def test_varlen(kkt, case):
         assert np.array_equal(single.view(np.uint32), packed[:, a:b].view(np.uint32)), f"sequence {s}"
 
 
-def test_varlen_validate_env_rejects_bad_offsets(kkt, monkeypatch):
-    """KKT_VALIDATE=1 copies cu_seqlens to the host and rejects malformed
-    offsets before launching anything."""
-    monkeypatch.setenv("KKT_VALIDATE", "1")
+def test_varlen_validate_option_rejects_bad_offsets(kkt):
+    """With KKT_OPTION_VALIDATE_CU_SEQLENS set, cu_seqlens is copied to the
+    host and malformed offsets are rejected before anything is launched;
+    valid offsets pass and give the same bits as without the check."""
     inp = W.generate("T256_H8_bf16_f32", lengths=[10, 20], H=2, seed=501)
-    k, g, b, _ = to_device(inp)
+    k, g, b, cu = to_device(inp)
     bad = torch.tensor([0, 25, 20], dtype=torch.int32, device=k.device)  # decreasing, ends != T
-    with pytest.raises(kkt.KKTError) as e:
-        kkt.kkt_solve(k, g, b, bad)
-    assert e.value.status == kkt.KKT_ERR_INVALID_ARGUMENT
+    plain = kkt.kkt_solve(k, g, b, cu, output_dtype=torch.float32)
+    with kkt.option(kkt.KKT_OPTION_VALIDATE_CU_SEQLENS, 1):
+        with pytest.raises(kkt.KKTError) as e:
+            kkt.kkt_solve(k, g, b, bad)
+        assert e.value.status == kkt.KKT_ERR_INVALID_ARGUMENT
+        checked = kkt.kkt_solve(k, g, b, cu, output_dtype=torch.float32)
+    assert kkt.get_option(kkt.KKT_OPTION_VALIDATE_CU_SEQLENS) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(plain.view(torch.int32), checked.view(torch.int32))
 
 
 def test_varlen_offsets_are_clamped(kkt):
@@ -295,6 +326,49 @@ def test_repeatable_and_stream(kkt):
     with torch.cuda.stream(s):
         b = run_gpu(kkt, inp, "f32", stream=s, tensors=t)
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_side_stream_noncontiguous_inputs(kkt):
+    """A call on a stream other than the current one, with inputs that are
+    strided views (so the binding copies them) produced on the current
+    stream just before the call: the launch stream waits for the producer,
+    the copies and the output are made on it, and the caller's tensors are
+    recorded on it.  Every entry point gives the bits of the same call made
+    on the current stream with contiguous inputs; the inputs are freed right
+    after the call, before the side stream is synchronised."""
+    inp = W.generate("T256_H8_bf16_f32", B=2, T=1500, H=6, seed=611)
+    say("[case] side stream, transposed-view inputs: B=2 T=1500 H=6 K=128 bf16")
+    k, g, b, _ = to_device(inp)
+    ref = kkt.kkt_solve(k, g, b, output_dtype=torch.float32)
+    ref_gs = kkt.kkt_solve_gate_cumsum(k, g, b, output_dtype=torch.float32, return_gate=True)
+    ref_A = kkt.kkt_scaled_dot(k, g, b)
+    ref_X = kkt.kkt_solve_tril(ref_A, output_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    for rep in range(3):
+        # produced on the current stream: [B,H,T,K] buffers viewed as [B,T,H,K]
+        kt = torch.empty((k.shape[0], k.shape[2], k.shape[1], k.shape[3]), dtype=k.dtype, device=k.device)
+        kt.copy_(k.permute(0, 2, 1, 3))
+        gt = torch.empty((g.shape[0], g.shape[2], g.shape[1]), dtype=g.dtype, device=g.device)
+        gt.copy_(g.permute(0, 2, 1))
+        bt = torch.empty_like(gt)
+        bt.copy_(b.permute(0, 2, 1))
+        At = torch.empty((ref_A.shape[0], ref_A.shape[2], ref_A.shape[1], 64), dtype=torch.float32, device=k.device)
+        At.copy_(ref_A.permute(0, 2, 1, 3))
+        kv, gv, bv, Av = kt.permute(0, 2, 1, 3), gt.permute(0, 2, 1), bt.permute(0, 2, 1), At.permute(0, 2, 1, 3)
+        assert not kv.is_contiguous()
+        x = kkt.kkt_solve(kv, gv, bv, output_dtype=torch.float32, stream=s)
+        xg, gg = kkt.kkt_solve_gate_cumsum(kv, gv, bv, output_dtype=torch.float32, return_gate=True, stream=s)
+        A = kkt.kkt_scaled_dot(kv, gv, bv, stream=s)
+        X = kkt.kkt_solve_tril(Av, output_dtype=torch.bfloat16, stream=s)
+        del kt, gt, bt, At, kv, gv, bv, Av
+        # new work on the current stream may now reuse freed memory
+        junk = [torch.full((1 << 20,), float("nan"), device=k.device) for _ in range(8)]
+        s.synchronize()
+        del junk
+        for got, want in ((x, ref), (xg, ref_gs[0]), (gg, ref_gs[1]), (A, ref_A)):
+            assert torch.equal(got.view(torch.int32), want.view(torch.int32)), f"rep {rep}"
+        assert torch.equal(X.view(torch.int16), ref_X.view(torch.int16)), f"rep {rep}"
 
 
 def test_concurrent_host_threads(kkt):

@@ -124,7 +124,7 @@ def test_chain_equals_fused_full(kkt, name):
 
 # ---------------------------------------------------------------- dtypes, head dims, shapes
 @pytest.mark.parametrize("in_dtype", ["bf16", "f16", "f32"])
-@pytest.mark.parametrize("K", [64, 128, 256])
+@pytest.mark.parametrize("K", [32, 64, 96, 128, 224, 256])
 def test_scaled_dot_dtypes_and_head_dims(kkt, in_dtype, K):
     inp = W.generate("T256_H8_bf16_f32", B=2, T=150, H=3, K=K, in_dtype=in_dtype, seed=1100 + K)
     check_scaled_dot(kkt, inp, f"{in_dtype} K={K}")

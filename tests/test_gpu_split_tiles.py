@@ -4,14 +4,13 @@ Small grids run each 64-token tile on a two-wave workgroup (the first wave
 finishes block rows 0..2, the second block row 3, exchanging the diagonal
 inverses and X10, X21, X20 through LDS); large grids run one tile per wave.
 Both form every block by the same operations in the same order, so their
-outputs must be bit-identical.  KKT_SPLIT_TILES (read by the library on every
-call) forces one form or the other on the same inputs; each case is also
-checked against the fp64 oracle.
+outputs must be bit-identical.  The library option KKT_OPTION_SPLIT_MAX_TILES
+forces one form or the other on the same inputs; each case is also checked
+against the fp64 oracle.
 """
 from __future__ import annotations
 
 import json
-import os
 
 import numpy as np
 import pytest
@@ -24,6 +23,8 @@ from tests._gpu_util import TORCH_DT, from_device, load_kkt, say, to_device
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
+SPLIT_ALL = 1_000_000_000  # a two-wave bound above every grid here
+
 
 @pytest.fixture(scope="module")
 def kkt():
@@ -33,17 +34,10 @@ def kkt():
 def run_form(kkt, t, out_dtype: str, split: bool) -> np.ndarray:
     k, g, b, cu = t
     B, T, H, _ = k.shape
-    old = os.environ.get("KKT_SPLIT_TILES")
-    os.environ["KKT_SPLIT_TILES"] = "1000000000" if split else "0"
-    try:
+    with kkt.option(kkt.KKT_OPTION_SPLIT_MAX_TILES, SPLIT_ALL if split else 0):
         out = torch.full((B, T, H, 64), float("nan"), dtype=TORCH_DT[out_dtype], device=k.device)
         kkt.kkt_solve(k, g, b, cu, output_dtype=TORCH_DT[out_dtype], out=out)
         torch.cuda.synchronize()
-    finally:
-        if old is None:
-            del os.environ["KKT_SPLIT_TILES"]
-        else:
-            os.environ["KKT_SPLIT_TILES"] = old
     return from_device(out, out_dtype)
 
 
@@ -115,19 +109,12 @@ def test_split_tiles_packed_short_sequences(kkt):
 def run_gate_sum_form(kkt, inp: W.Inputs, split: bool, in_place: bool):
     k, _, b, cu = to_device(inp)
     g_raw = torch.from_numpy(inp.g_raw).to(k.device)
-    old = os.environ.get("KKT_SPLIT_TILES")
-    os.environ["KKT_SPLIT_TILES"] = "1000000000" if split else "0"
-    try:
+    with kkt.option(kkt.KKT_OPTION_SPLIT_MAX_TILES, SPLIT_ALL if split else 0):
         B, T, H, _ = k.shape
         out = torch.full((B, T, H, 64), float("nan"), dtype=torch.float32, device=k.device)
         g_out = g_raw if in_place else torch.full((B, T, H), float("nan"), dtype=torch.float32, device=k.device)
         kkt.kkt_solve_gate_cumsum(k, g_raw, b, cu, output_dtype=torch.float32, out=out, g_out=g_out)
         torch.cuda.synchronize()
-    finally:
-        if old is None:
-            del os.environ["KKT_SPLIT_TILES"]
-        else:
-            os.environ["KKT_SPLIT_TILES"] = old
     return out.cpu().numpy(), g_out.cpu().numpy()
 
 
@@ -186,19 +173,12 @@ def test_split_tiles_solve_tril(kkt, shape, out_dtype):
     k, g, b, cu = to_device(inp)
     A = kkt.kkt_scaled_dot(k, g, b, cu)
     torch.cuda.synchronize()
-    old = os.environ.get("KKT_SPLIT_TILES")
-    try:
-        res = []
-        for split in (False, True):
-            os.environ["KKT_SPLIT_TILES"] = "1000000000" if split else "0"
+    res = []
+    for split in (False, True):
+        with kkt.option(kkt.KKT_OPTION_SPLIT_MAX_TILES, SPLIT_ALL if split else 0):
             X = kkt.kkt_solve_tril(A, cu, output_dtype=TORCH_DT[out_dtype])
             torch.cuda.synchronize()
-            res.append(from_device(X, out_dtype))
-    finally:
-        if old is None:
-            del os.environ["KKT_SPLIT_TILES"]
-        else:
-            os.environ["KKT_SPLIT_TILES"] = old
+        res.append(from_device(X, out_dtype))
     view = np.uint32 if out_dtype == "f32" else np.uint16
     assert np.array_equal(res[0].view(view), res[1].view(view))
     fused = run_form(kkt, (k, g, b, cu), out_dtype, split=True)
