@@ -22,15 +22,17 @@ def hipcc() -> str:
     return path if os.path.exists(path) else "hipcc"
 
 
-def build(verbose: bool = False, extra_flags=()) -> str:
-    """Build the shared library; returns its path.  Raises on failure."""
+def build(verbose: bool = False, extra_flags=(), out: str = None) -> str:
+    """Build the shared library (at ``out``, default the package's
+    ``libkkt_solve.so``); returns its path.  Raises on failure."""
+    lib = out or LIB
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
            # packed fp32 VALU ops stay off (see the kernel notes); hipcc's host
            # pass warns that it does not know the feature, which is harmless
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
            # MFMA results in ordinary VGPRs: no accumulator-register copies
            "-mllvm", "-amdgpu-mfma-vgpr-form=1",
-           "-Wall", "-I", INCLUDE, "-o", LIB + ".tmp", SRC, *extra_flags]
+           "-Wall", "-I", INCLUDE, "-o", lib + ".tmp", SRC, *extra_flags]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -39,8 +41,8 @@ def build(verbose: bool = False, extra_flags=()) -> str:
         raise RuntimeError("HIP build failed:\n" + res.stdout + err)
     if verbose and err.strip():
         print(err, file=sys.stderr)
-    os.replace(LIB + ".tmp", LIB)
-    return LIB
+    os.replace(lib + ".tmp", lib)
+    return lib
 
 
 if __name__ == "__main__":

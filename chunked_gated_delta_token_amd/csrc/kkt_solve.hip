@@ -1604,6 +1604,19 @@ hipError_t launch_scaled_dot(int64_t K, const KernelArgs& a, hipStream_t stream)
 
 bool valid_dtype(int d) { return d == KKT_DTYPE_F32 || d == KKT_DTYPE_BF16 || d == KKT_DTYPE_F16; }
 
+// The integer a C caller passed for an enum parameter.  C lets any int
+// through an enum type; in C++ reading a value outside the enumerators'
+// range as the enum type is undefined, so the bytes are read as an int and
+// only a validated value is used as the enum.
+template <typename E>
+int enum_code(const E& e)
+{
+    static_assert(sizeof(E) == sizeof(int), "C enums are int-sized here");
+    int v;
+    memcpy(&v, &e, sizeof v);
+    return v;
+}
+
 int64_t dtype_bytes(kkt_dtype_t d) { return d == KKT_DTYPE_F32 ? 4 : 2; }
 
 // Grids up to this many workgroups use the XCD-contiguous tile order; larger
@@ -1736,13 +1749,17 @@ kkt_status_t check_k_sizes(int64_t B, int64_t T, int64_t H, int64_t K, int64_t n
 extern "C" kkt_status_t kkt_solve(const void* k, const float* g, const float* beta,
                                   const int32_t* cu_seqlens, int64_t num_seqs,
                                   int64_t B, int64_t T, int64_t H, int64_t K,
-                                  int64_t chunk_size, kkt_dtype_t in_dtype, kkt_dtype_t out_dtype,
+                                  int64_t chunk_size, kkt_dtype_t in_dtype_arg, kkt_dtype_t out_dtype_arg,
                                   void* out, hipStream_t stream)
 {
     g_last_error.clear();
     // ---- argument checks: no HIP call before they pass
     if (chunk_size != kChunk && chunk_size != 2 * kChunk) return fail(KKT_ERR_UNSUPPORTED, "chunk_size must be 64 or 128");
-    if (!valid_dtype((int)in_dtype) || !valid_dtype((int)out_dtype)) return fail(KKT_ERR_INVALID_ARGUMENT, "unknown dtype");
+    if (!valid_dtype(enum_code(in_dtype_arg)) || !valid_dtype(enum_code(out_dtype_arg))) {
+        return fail(KKT_ERR_INVALID_ARGUMENT, "unknown dtype");
+    }
+    const kkt_dtype_t in_dtype = (kkt_dtype_t)enum_code(in_dtype_arg);
+    const kkt_dtype_t out_dtype = (kkt_dtype_t)enum_code(out_dtype_arg);
     kkt_status_t st = check_k_sizes(B, T, H, K, num_seqs, cu_seqlens);
     if (st != KKT_OK) return st;
     if (T == 0) return KKT_OK;
@@ -1764,12 +1781,16 @@ extern "C" kkt_status_t kkt_solve(const void* k, const float* g, const float* be
 extern "C" kkt_status_t kkt_solve_gate_cumsum(const void* k, const float* g_decay, const float* beta,
                                               const int32_t* cu_seqlens, int64_t num_seqs,
                                               int64_t B, int64_t T, int64_t H, int64_t K,
-                                              int64_t chunk_size, kkt_dtype_t in_dtype, kkt_dtype_t out_dtype,
+                                              int64_t chunk_size, kkt_dtype_t in_dtype_arg, kkt_dtype_t out_dtype_arg,
                                               void* out, float* g_out, hipStream_t stream)
 {
     g_last_error.clear();
     if (chunk_size != kChunk && chunk_size != 2 * kChunk) return fail(KKT_ERR_UNSUPPORTED, "chunk_size must be 64 or 128");
-    if (!valid_dtype((int)in_dtype) || !valid_dtype((int)out_dtype)) return fail(KKT_ERR_INVALID_ARGUMENT, "unknown dtype");
+    if (!valid_dtype(enum_code(in_dtype_arg)) || !valid_dtype(enum_code(out_dtype_arg))) {
+        return fail(KKT_ERR_INVALID_ARGUMENT, "unknown dtype");
+    }
+    const kkt_dtype_t in_dtype = (kkt_dtype_t)enum_code(in_dtype_arg);
+    const kkt_dtype_t out_dtype = (kkt_dtype_t)enum_code(out_dtype_arg);
     kkt_status_t st = check_k_sizes(B, T, H, K, num_seqs, cu_seqlens);
     if (st != KKT_OK) return st;
     if (T == 0) return KKT_OK;
@@ -1794,11 +1815,12 @@ extern "C" kkt_status_t kkt_solve_gate_cumsum(const void* k, const float* g_deca
 extern "C" kkt_status_t kkt_scaled_dot(const void* k, const float* g, const float* beta,
                                        const int32_t* cu_seqlens, int64_t num_seqs,
                                        int64_t B, int64_t T, int64_t H, int64_t K,
-                                       int64_t chunk_size, kkt_dtype_t in_dtype, float* A, hipStream_t stream)
+                                       int64_t chunk_size, kkt_dtype_t in_dtype_arg, float* A, hipStream_t stream)
 {
     g_last_error.clear();
     if (chunk_size != kChunk) return fail(KKT_ERR_UNSUPPORTED, "chunk_size must be 64");
-    if (!valid_dtype((int)in_dtype)) return fail(KKT_ERR_INVALID_ARGUMENT, "unknown dtype");
+    if (!valid_dtype(enum_code(in_dtype_arg))) return fail(KKT_ERR_INVALID_ARGUMENT, "unknown dtype");
+    const kkt_dtype_t in_dtype = (kkt_dtype_t)enum_code(in_dtype_arg);
     kkt_status_t st = check_k_sizes(B, T, H, K, num_seqs, cu_seqlens);
     if (st != KKT_OK) return st;
     if (T == 0) return KKT_OK;
@@ -1819,11 +1841,12 @@ extern "C" kkt_status_t kkt_scaled_dot(const void* k, const float* g, const floa
 
 extern "C" kkt_status_t kkt_solve_tril(const float* A, const int32_t* cu_seqlens, int64_t num_seqs,
                                        int64_t B, int64_t T, int64_t H, int64_t chunk_size,
-                                       kkt_dtype_t out_dtype, void* out, hipStream_t stream)
+                                       kkt_dtype_t out_dtype_arg, void* out, hipStream_t stream)
 {
     g_last_error.clear();
     if (chunk_size != kChunk) return fail(KKT_ERR_UNSUPPORTED, "chunk_size must be 64");
-    if (!valid_dtype((int)out_dtype)) return fail(KKT_ERR_INVALID_ARGUMENT, "unknown dtype");
+    if (!valid_dtype(enum_code(out_dtype_arg))) return fail(KKT_ERR_INVALID_ARGUMENT, "unknown dtype");
+    const kkt_dtype_t out_dtype = (kkt_dtype_t)enum_code(out_dtype_arg);
     if (B < 1 || H < 1 || T < 0) return fail(KKT_ERR_INVALID_ARGUMENT, "B, H must be >= 1 and T >= 0");
     if (cu_seqlens != nullptr && (B != 1 || num_seqs < 1)) {
         return fail(KKT_ERR_INVALID_ARGUMENT, "cu_seqlens needs B == 1 and num_seqs >= 1");
@@ -1853,10 +1876,10 @@ extern "C" kkt_status_t kkt_solve_tril(const float* A, const int32_t* cu_seqlens
     return KKT_OK;
 }
 
-extern "C" kkt_status_t kkt_set_option(kkt_option_t option, int64_t value)
+extern "C" kkt_status_t kkt_set_option(kkt_option_t option_arg, int64_t value)
 {
     g_last_error.clear();
-    switch (option) {
+    switch (enum_code(option_arg)) {
     case KKT_OPTION_SPLIT_MAX_TILES:
         if (value < 0) return fail(KKT_ERR_INVALID_ARGUMENT, "KKT_OPTION_SPLIT_MAX_TILES must be >= 0");
         g_split_max_tiles.store(value, std::memory_order_relaxed);
@@ -1868,9 +1891,9 @@ extern "C" kkt_status_t kkt_set_option(kkt_option_t option, int64_t value)
     return fail(KKT_ERR_INVALID_ARGUMENT, "unknown option");
 }
 
-extern "C" int64_t kkt_get_option(kkt_option_t option)
+extern "C" int64_t kkt_get_option(kkt_option_t option_arg)
 {
-    switch (option) {
+    switch (enum_code(option_arg)) {
     case KKT_OPTION_SPLIT_MAX_TILES: return g_split_max_tiles.load(std::memory_order_relaxed);
     case KKT_OPTION_VALIDATE_CU_SEQLENS: return g_validate_cu_seqlens.load(std::memory_order_relaxed);
     }

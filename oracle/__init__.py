@@ -30,30 +30,38 @@ _LIB = os.path.join(_HERE, "libkkt_oracle.so")
 _lib = None
 
 
-def build(quiet: bool = True) -> str:
+def build(quiet: bool = True, out: str = None, src: str = None, sanitize: bool = False) -> str:
     """Compile ``kkt_oracle.c`` into ``libkkt_oracle.so`` (gcc, OpenMP, fp64).
 
     -O2 without fast-math: the compiler keeps the written order of every
-    floating-point operation.
+    floating-point operation.  ``out`` / ``src`` build another path or source
+    (the tests' planted-mistake copies); ``sanitize`` adds AddressSanitizer
+    and UndefinedBehaviorSanitizer (aborting on the first report), for the
+    tests that run the pins on such a build.
     """
+    out = out or _LIB
     cmd = ["gcc", "-std=c11", "-O2", "-fno-fast-math", "-ffp-contract=off", "-fopenmp",
-           "-fPIC", "-shared", "-Wall", "-Wextra", "-o", _LIB + ".tmp", _SRC, "-lm"]
+           "-fPIC", "-shared", "-Wall", "-Wextra"]
+    if sanitize:
+        cmd += ["-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined", "-fno-sanitize-recover=all"]
+    cmd += ["-o", out + ".tmp", src or _SRC, "-lm"]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("oracle build failed:\n" + res.stdout + res.stderr)
-    os.replace(_LIB + ".tmp", _LIB)
+    os.replace(out + ".tmp", out)
     if not quiet:
-        print("built", _LIB)
-    return _LIB
+        print("built", out)
+    return out
 
 
 def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB):
+    path = os.environ.get("KKT_ORACLE_LIB") or _LIB  # (another build of the same source, e.g. sanitized)
+    if path == _LIB and not os.path.exists(_LIB):
         build()
-    lib = ctypes.CDLL(_LIB)
+    lib = ctypes.CDLL(path)
     dp = ctypes.POINTER(ctypes.c_double)
     ip = ctypes.POINTER(ctypes.c_int32)
     lib.kkt_oracle_solve.argtypes = [dp, dp, dp, ip, ctypes.c_int64,

@@ -92,11 +92,13 @@ def test_invalid_arguments_rejected_on_host(lib, over, status, msg):
 @pytest.mark.parametrize("K", [32, 64, 96, 128, 160, 192, 224, 256])
 @pytest.mark.parametrize("in_dtype", [0, 1, 2])
 def test_every_multiple_of_32_up_to_256_passes_the_k_check(lib, K, in_dtype):
-    """Every key dtype takes K = 32, 64, ..., 256: the argument checks pass
-    (without a GPU the call then stops at the device query, not at K)."""
+    """Every key dtype takes K = 32, 64, ..., 256: with T = 0 the call passes
+    every argument check and returns KKT_OK without launching anything (so
+    this never touches a GPU, even where one is present)."""
     from chunked_gated_delta_token_amd import kkt
-    st = _call(lib, K=K, in_dtype=in_dtype)
-    assert st != 1 and "K must be" not in kkt.last_error(), (st, kkt.last_error())
+    for chunk in (64, 128):
+        assert _call(lib, K=K, in_dtype=in_dtype, T=0, chunk_size=chunk) == kkt.KKT_OK, kkt.last_error()
+    assert _call_scaled_dot(lib, K=K, in_dtype=in_dtype, T=0) == kkt.KKT_OK, kkt.last_error()
 
 
 def test_options_round_trip_and_reject_bad_values(lib):
