@@ -254,6 +254,25 @@ __device__ __forceinline__ f32x4 gram_bf16x3(const Bf16x3& a, const Bf16x3& b, f
 //                     one L2.
 enum XcdOrder { kHardwareOrder = 0, kContiguous = 1, kChunkRoundRobin = 2 };
 
+// Unsigned division by a launch constant d >= 1 for dividends n < 2^31, as a
+// multiply-high and a shift (set up on the host by make_fastdiv):
+//   d a power of two:  magic = 0, n / d = n >> shift;
+//   otherwise:         shift = floor(log2 d), magic = ceil(2^(32 + shift) / d)
+//                      (in (2^31, 2^32) since 2^shift < d < 2^(shift+1)),
+//                      n / d = mulhi(n, magic) >> shift.
+// Exact: with magic = (2^(32+s) + e) / d, 0 <= e < d < 2^(s+1), the estimate
+// exceeds n / d by n e / (d 2^(32+s)) < 2^31 2^(s+1) / (d 2^(32+s)) = 1 / d,
+// which never carries past the next integer since frac(n / d) <= 1 - 1 / d.
+struct FastDiv {
+    uint32_t magic;
+    uint32_t shift;
+};
+
+__device__ __forceinline__ uint32_t fast_div(uint32_t n, FastDiv d)
+{
+    return (d.magic == 0) ? (n >> d.shift) : (__umulhi(n, d.magic) >> d.shift);
+}
+
 struct KernelArgs {
     const void* k;
     const float* g;
@@ -277,6 +296,8 @@ struct KernelArgs {
     int32_t k_steps;            // 64-byte k-steps of one key row (K * element size / 64); the
                                 // kernel's template K may be larger: its further steps read as 0
     uint32_t k_head_bytes;      // bytes of one key row of one head (K * element size)
+    FastDiv div_H;              // division by H (tile -> chunk, head)
+    FastDiv div_chunks;         // division by chunks_per_row (chunk -> batch row, chunk in row)
 };
 
 // ---------------------------------------------------------------- tile map (a1)
@@ -367,9 +388,16 @@ __device__ Tile varlen_tile(const int32_t* __restrict__ cu, int32_t num_seqs, in
 // argument loads are issued together.
 __device__ __forceinline__ uint32_t workgroup_order(const KernelArgs& args)
 {
-    // (the empty statement makes the tensor pointers live here, so that their
-    // loads are issued with the ones the order needs, in one round trip)
-    asm volatile("" ::"s"(args.k), "s"(args.out), "s"(args.g), "s"(args.beta));
+    // (the empty statements make every argument the tile's path reads live
+    // here, so that all of them are loaded with the ones the order needs, in
+    // one round trip: a kernel-argument load issued later waits behind the
+    // whole chip's memory traffic, up to microseconds, right before the key
+    // loads it gates)
+    asm volatile("" ::"s"(args.k), "s"(args.out), "s"(args.g), "s"(args.beta), "s"(args.cu_seqlens));
+    asm volatile("" ::"s"(args.T), "s"(args.num_seqs), "s"(args.H), "s"(args.chunks_per_row), "s"(args.n_tiles),
+                 "s"(args.k_row_bytes), "s"(args.o_row_bytes), "s"(args.tile_waves), "s"(args.k_steps),
+                 "s"(args.k_head_bytes), "s"(args.div_H.magic), "s"(args.div_H.shift), "s"(args.div_chunks.magic),
+                 "s"(args.div_chunks.shift));
     const uint32_t n_groups = args.n_groups;
     const uint32_t hw = blockIdx.x;
     const uint32_t xcd = hw % 8, slot = hw / 8;
@@ -390,8 +418,8 @@ __device__ __forceinline__ Tile chunk_tile(const KernelArgs& args, uint32_t chun
 {
     Tile tile;
     if (args.cu_seqlens == nullptr) {
-        const uint32_t b = chunk / (uint32_t)args.chunks_per_row;
-        const uint32_t c = chunk % (uint32_t)args.chunks_per_row;
+        const uint32_t b = fast_div(chunk, args.div_chunks);
+        const uint32_t c = chunk - b * (uint32_t)args.chunks_per_row;
         const int64_t t0 = (int64_t)c * CH;
         tile.row0 = (int64_t)b * args.T + t0;
         tile.len = (int)((args.T - t0) < CH ? (args.T - t0) : CH);
@@ -520,7 +548,8 @@ __device__ __forceinline__ void chunk_rows(const KernelArgs& args, WaveLds& lds,
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const uint32_t voff = (uint32_t)(16 * i + 4 * q + r) * args.k_row_bytes + (16 * j + m) * 4;
-                    A[i][j][r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(a_rsrc, voff, 0, 0));
+                    const float a = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(a_rsrc, voff, 0, 0));
+                    A[i][j][r] = (j < i) ? -a : a;  // off-diagonal blocks negated, as the fused op forms them
                 }
             }
         }
@@ -666,13 +695,17 @@ __device__ __forceinline__ void chunk_rows(const KernelArgs& args, WaveLds& lds,
         }
 
         // ---- a5: epilogue (the scales are in LDS already)
+        // (for the solve, the off-diagonal blocks are formed negated: a
+        // negated factor negates the rounded product exactly; A itself, for
+        // kkt_scaled_dot, keeps its sign)
+        constexpr float kOff = (MODE == Mode::ScaledDot) ? 1.0f : -1.0f;
         if (!has_g) {
             // A = beta_i S (rows >= L have beta 0 and zero keys)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const f32x4 rr = *reinterpret_cast<const f32x4*>(&lds.row_scale[16 * i + 4 * q]);
 #pragma unroll
-                for (int j = 0; j <= i; ++j) A[i][j] = rr * S[i][j];
+                for (int j = 0; j <= i; ++j) A[i][j] = (j < i ? kOff * rr : rr) * S[i][j];
             }
         } else if (factored) {
             // A = (r_i S) c_j: both factors are zero outside the chunk's L rows
@@ -683,7 +716,7 @@ __device__ __forceinline__ void chunk_rows(const KernelArgs& args, WaveLds& lds,
             for (int i = 0; i < 4; ++i) {
                 const f32x4 rr = *reinterpret_cast<const f32x4*>(&lds.row_scale[16 * i + 4 * q]);
 #pragma unroll
-                for (int j = 0; j <= i; ++j) A[i][j] = (rr * S[i][j]) * cc[j];
+                for (int j = 0; j <= i; ++j) A[i][j] = (rr * S[i][j]) * (j < i ? kOff * cc[j] : cc[j]);
             }
         } else {
             // A = beta_i S exp(clamp(g_i - g_j)); the clamp bounds the gate, so
@@ -700,7 +733,7 @@ __device__ __forceinline__ void chunk_rows(const KernelArgs& args, WaveLds& lds,
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const float d = fminf(fmaxf(gr[r] - gc[j], -kGateClamp), kGateClamp);
-                        A[i][j][r] = rr[r] * (S[i][j][r] * __expf(d));
+                        A[i][j][r] = (j < i ? kOff * rr[r] : rr[r]) * (S[i][j][r] * __expf(d));
                     }
                 }
             }
@@ -895,6 +928,13 @@ __device__ __forceinline__ void chunk_rows(const KernelArgs& args, WaveLds& lds,
         for (int r = 0; r < 4; ++r) xa[d][r] = blk[d][4 * q + r][m];
     }
 
+    // ---- a7: merge.  The off-diagonal blocks of A arrive negated (the
+    // epilogue's column factor, or the solve's load, carries the sign), so
+    // wt_ik = -(X_ii A_ik)^T, whose result layout is the left-operand layout
+    // of -W_ik, and every X_ij = -sum_k W_ik X_kj is a plain accumulation
+    // (the same value, bit for bit, as 0 - sum: negating every product
+    // negates the rounded sum, and an all-zero sum stays +0.0 from the +0.0
+    // start).
     if constexpr (SPLIT == 1) {
         // block rows 0..2; X10 and X21 go to the other wave before the
         // second barrier, X20 before the third
@@ -902,14 +942,14 @@ __device__ __forceinline__ void chunk_rows(const KernelArgs& args, WaveLds& lds,
         const f32x4 wt10 = mm16(A[1][0], xa[1], zero4);
         const f32x4 wt20 = mm16(A[2][0], xa[2], zero4);
         const f32x4 wt21 = mm16(A[2][1], xa[2], zero4);
-        const f32x4 x10 = zero4 - mm16(wt10, xd[0], zero4);
-        const f32x4 x21 = zero4 - mm16(wt21, xd[1], zero4);
+        const f32x4 x10 = mm16(wt10, xd[0], zero4);
+        const f32x4 x21 = mm16(wt21, xd[1], zero4);
         const f32x4 p20 = mm16(wt20, xd[0], zero4);
         xchg[0][lane] = x10;
         xchg[1][lane] = x21;
         __syncthreads();
         store_block_row(1, x10, xd[1], zero4, zero4);
-        const f32x4 x20 = zero4 - mm16(wt21, x10, p20);
+        const f32x4 x20 = mm16(wt21, x10, p20);
         xchg[2][lane] = x20;
         __syncthreads();
         store_block_row(2, x20, x21, xd[2], zero4);
@@ -919,26 +959,21 @@ __device__ __forceinline__ void chunk_rows(const KernelArgs& args, WaveLds& lds,
         const f32x4 wt30 = mm16(A[3][0], xa[3], zero4);
         const f32x4 wt31 = mm16(A[3][1], xa[3], zero4);
         const f32x4 wt32 = mm16(A[3][2], xa[3], zero4);
-        const f32x4 x32 = zero4 - mm16(wt32, xd[2], zero4);
+        const f32x4 x32 = mm16(wt32, xd[2], zero4);
         const f32x4 p31 = mm16(wt31, xd[1], zero4);
         f32x4 p30 = mm16(wt30, xd[0], zero4);
         __syncthreads();
         const f32x4 x10 = xchg[0][lane];
         const f32x4 x21 = xchg[1][lane];
         p30 = mm16(wt31, x10, p30);
-        const f32x4 x31 = zero4 - mm16(wt32, x21, p31);
+        const f32x4 x31 = mm16(wt32, x21, p31);
         __syncthreads();
         const f32x4 x20 = xchg[2][lane];
-        const f32x4 x30 = zero4 - mm16(wt32, x20, p30);
+        const f32x4 x30 = mm16(wt32, x20, p30);
         store_block_row(3, x30, x31, x32, xd[3]);
         return;
     }
 
-    // block row 0 is final already
-    store_block_row(0, xd[0], zero4, zero4, zero4);
-
-    // ---- a7: merge.  wt_ik = (X_ii A_ik)^T; its result layout is the left
-    // operand layout of W_ik.
     const f32x4 wt10 = mm16(A[1][0], xa[1], zero4);
     const f32x4 wt20 = mm16(A[2][0], xa[2], zero4);
     const f32x4 wt21 = mm16(A[2][1], xa[2], zero4);
@@ -946,37 +981,48 @@ __device__ __forceinline__ void chunk_rows(const KernelArgs& args, WaveLds& lds,
     const f32x4 wt31 = mm16(A[3][1], xa[3], zero4);
     const f32x4 wt32 = mm16(A[3][2], xa[3], zero4);
 
-    // X_ij = 0 - sum(...): exact negation that turns an all-zero sum into +0.0.
-    // The partial products that do not wait on this level's results are
-    // issued before each block-row store, so the MFMA pipe works through them
-    // while the store's LDS and memory instructions execute.
-    const f32x4 x10 = zero4 - mm16(wt10, xd[0], zero4);
-    const f32x4 x21 = zero4 - mm16(wt21, xd[1], zero4);
-    const f32x4 x32 = zero4 - mm16(wt32, xd[2], zero4);
-    const f32x4 p20 = mm16(wt20, xd[0], zero4);
-    const f32x4 p31 = mm16(wt31, xd[1], zero4);
-    f32x4 p30 = mm16(wt30, xd[0], zero4);
-    store_block_row(1, x10, xd[1], zero4, zero4);
+    {
+        // The blocks are formed in the result layout and each block row is
+        // staged through LDS, so that every store instruction writes whole
+        // output rows (4 rows of 256 bytes, or 8 of 128).  Stored straight
+        // from registers, each instruction writes a 64- or 32-byte piece of
+        // 16 rows, twice or four times the cache lines per instruction: that
+        // measured slower in the store phase on the bench workload and 1.6
+        // times slower overall on the (2,16384,32,128) workload.  With
+        // 128-token chunks this half's blocks also go to the rest of the
+        // workgroup.
+        store_block_row(0, xd[0], zero4, zero4, zero4);
+        // The partial products that do not wait on this level's results are
+        // issued before each block-row store, so the MFMA pipe works through
+        // them while the store's LDS and memory instructions execute.
+        const f32x4 x10 = mm16(wt10, xd[0], zero4);
+        const f32x4 x21 = mm16(wt21, xd[1], zero4);
+        const f32x4 x32 = mm16(wt32, xd[2], zero4);
+        const f32x4 p20 = mm16(wt20, xd[0], zero4);
+        const f32x4 p31 = mm16(wt31, xd[1], zero4);
+        f32x4 p30 = mm16(wt30, xd[0], zero4);
+        store_block_row(1, x10, xd[1], zero4, zero4);
 
-    const f32x4 x20 = zero4 - mm16(wt21, x10, p20);
-    const f32x4 x31 = zero4 - mm16(wt32, x21, p31);
-    p30 = mm16(wt31, x10, p30);
-    store_block_row(2, x20, x21, xd[2], zero4);
+        const f32x4 x20 = mm16(wt21, x10, p20);
+        const f32x4 x31 = mm16(wt32, x21, p31);
+        p30 = mm16(wt31, x10, p30);
+        store_block_row(2, x20, x21, xd[2], zero4);
 
-    const f32x4 x30 = zero4 - mm16(wt32, x20, p30);
-    store_block_row(3, x30, x31, x32, xd[3]);
+        const f32x4 x30 = mm16(wt32, x20, p30);
+        store_block_row(3, x30, x31, x32, xd[3]);
 
-    if constexpr (CH == 128) {
-        __syncthreads();  // end of the first phase: the exchange area overlaps its areas
-        // hand the block to the workgroup: X11 as result-layout register
-        // images, X22 transposed (its rows are read as left operands)
-        const f32x4 blocks[10] = {xd[0], x10, xd[1], x20, x21, xd[2], x30, x31, x32, xd[3]};
-        if (half == 0) {
+        if constexpr (CH == 128) {
+            __syncthreads();  // end of the first phase: the exchange area overlaps its areas
+            // hand the block to the workgroup: X11 as result-layout register
+            // images, X22 transposed (its rows are read as left operands)
+            const f32x4 blocks[10] = {xd[0], x10, xd[1], x20, x21, xd[2], x30, x31, x32, xd[3]};
+            if (half == 0) {
 #pragma unroll
-            for (int b = 0; b < 10; ++b) ex->cross.x11[b][lane] = blocks[b];
-        } else {
+                for (int b = 0; b < 10; ++b) ex->cross.x11[b][lane] = blocks[b];
+            } else {
 #pragma unroll
-            for (int b = 0; b < 10; ++b) *reinterpret_cast<f32x4*>(&ex->x22t[b][m][4 * q]) = blocks[b];
+                for (int b = 0; b < 10; ++b) *reinterpret_cast<f32x4*>(&ex->x22t[b][m][4 * q]) = blocks[b];
+            }
         }
     }
 }
@@ -995,8 +1041,9 @@ __device__ __forceinline__ void run_tile(const KernelArgs& args, WaveLds* lds_al
 
     // ---- a1: tile map
     const int H = args.H;
-    const int h = (int)(tile_id % (uint32_t)H);
-    const Tile tile = chunk_tile<kChunk>(args, tile_id / (uint32_t)H, lane);
+    const uint32_t chunk = fast_div(tile_id, args.div_H);
+    const int h = (int)(tile_id - chunk * (uint32_t)H);
+    const Tile tile = chunk_tile<kChunk>(args, chunk, lane);
     if (tile.len <= 0) return;  // wave-uniform
     chunk_rows<MODE, IN, OUT, K, GATE_SUM, kChunk>(args, lds_all[wave], lds_all[wave].blk, nullptr, lane,
                                                    tile.row0 * H + h, tile.len, 0, nullptr);
@@ -1022,8 +1069,9 @@ __device__ __forceinline__ void run_split_tile(const KernelArgs& args, SplitLds&
     const uint32_t tile_id = workgroup_order(args);
     if (tile_id >= (uint32_t)args.n_tiles) return;  // workgroup-uniform
     const int H = args.H;
-    const int h = (int)(tile_id % (uint32_t)H);
-    const Tile tile = chunk_tile<kChunk>(args, tile_id / (uint32_t)H, lane);
+    const uint32_t chunk = fast_div(tile_id, args.div_H);
+    const int h = (int)(tile_id - chunk * (uint32_t)H);
+    const Tile tile = chunk_tile<kChunk>(args, chunk, lane);
     if (tile.len <= 0) return;  // workgroup-uniform
     const int64_t tok = tile.row0 * H + h;
     if (wave == 0) {
@@ -1308,8 +1356,9 @@ void kkt_solve128_kernel(const KernelArgs args)
     const uint32_t tile_id = workgroup_order(args);
     if (tile_id >= (uint32_t)args.n_tiles) return;  // workgroup-uniform
     const int H = args.H;
-    const int h = (int)(tile_id % (uint32_t)H);
-    const Tile tile = chunk_tile<2 * kChunk>(args, tile_id / (uint32_t)H, lane);
+    const uint32_t chunk = fast_div(tile_id, args.div_H);
+    const int h = (int)(tile_id - chunk * (uint32_t)H);
+    const Tile tile = chunk_tile<2 * kChunk>(args, chunk, lane);
     if (tile.len <= 0) return;  // workgroup-uniform
     const int L = tile.len;
     const int64_t tok = tile.row0 * H + h;
@@ -1662,6 +1711,15 @@ std::atomic<int64_t> g_split_max_tiles{env_int("KKT_SPLIT_TILES", kSplitMaxTiles
 std::atomic<int64_t> g_validate_cu_seqlens{env_int("KKT_VALIDATE", 0) == 1 ? 1 : 0};
 int64_t split_max_tiles() { return g_split_max_tiles.load(std::memory_order_relaxed); }
 
+FastDiv make_fastdiv(uint32_t d)
+{
+    uint32_t s = 0;
+    while ((2ull << s) <= d) ++s;  // s = floor(log2 d)
+    if ((1ull << s) == d) return FastDiv{0u, s};
+    const uint64_t magic = ((1ull << (32 + s)) + d - 1) / d;  // ceil(2^(32+s) / d) < 2^32
+    return FastDiv{(uint32_t)magic, s};
+}
+
 // Checks shared by every entry point and the launch geometry.  in_row_bytes
 // and out_row_bytes are the strides between consecutive tokens of one head;
 // chunk is 64 (one tile per wave) or 128 (one tile per workgroup).
@@ -1730,6 +1788,8 @@ kkt_status_t setup(KernelArgs& a, const void* in, const float* g, const float* b
     a.tile_waves = (int32_t)tiles_per_group;
     a.k_head_bytes = (uint32_t)(in_row_bytes / H);
     a.k_steps = (int32_t)(a.k_head_bytes / 64);
+    a.div_H = make_fastdiv((uint32_t)H);
+    a.div_chunks = make_fastdiv((uint32_t)(chunks_per_row > 0 ? chunks_per_row : 1));
     return KKT_OK;
 }
 
