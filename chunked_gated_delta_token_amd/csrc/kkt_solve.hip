@@ -445,7 +445,7 @@ struct Chunk128Lds {
             u32x4 kimg[4][4][kWave];           // rows 0..63: key fragments (16-row block, k-step, lane)
         };
         struct {
-            float x22t[10][16][kBlockLd];      // X22 blocks, transposed: x22t[b][col][row]
+            float x22[10][16][kBlockLd];       // X22 blocks, row-major: x22[b][row][col]
             union {
                 struct {
                     f32x4 x11[10][kWave];      // X11 blocks, result-layout register images
@@ -538,6 +538,11 @@ __device__ __forceinline__ void chunk_rows(const KernelArgs& args, WaveLds& lds,
     f32x4 A[4][4];
     if constexpr (MODE == Mode::SolveTril) {
         // ---- A from memory (fp32 rows of 64; the kernel argument k carries A)
+        // The first row of a diagonal block has no strictly lower entry in
+        // it: those lanes read past the resource's end (zeros, no memory
+        // access), so rows 0 and 32, whose lines no other block of their
+        // row touches, cost no fetch.  (The range is below 2^31: the host
+        // checks chunk * row stride.)
         const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(
             static_cast<const char*>(args.k) + tok * (int64_t)(CH * 4),
             (uint32_t)(L - 1) * args.k_row_bytes + CH * 4);
@@ -547,7 +552,8 @@ __device__ __forceinline__ void chunk_rows(const KernelArgs& args, WaveLds& lds,
             for (int j = 0; j <= i; ++j) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const uint32_t voff = (uint32_t)(16 * i + 4 * q + r) * args.k_row_bytes + (16 * j + m) * 4;
+                    uint32_t voff = (uint32_t)(16 * i + 4 * q + r) * args.k_row_bytes + (16 * j + m) * 4;
+                    if (j == i && r == 0 && q == 0) voff = 0x80000000u;
                     const float a = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(a_rsrc, voff, 0, 0));
                     A[i][j][r] = (j < i) ? -a : a;  // off-diagonal blocks negated, as the fused op forms them
                 }
@@ -1014,14 +1020,18 @@ __device__ __forceinline__ void chunk_rows(const KernelArgs& args, WaveLds& lds,
         if constexpr (CH == 128) {
             __syncthreads();  // end of the first phase: the exchange area overlaps its areas
             // hand the block to the workgroup: X11 as result-layout register
-            // images, X22 transposed (its rows are read as left operands)
+            // images, X22 row-major (each lane of a reader then takes 4
+            // consecutive entries of one row, a left operand, in one load)
             const f32x4 blocks[10] = {xd[0], x10, xd[1], x20, x21, xd[2], x30, x31, x32, xd[3]};
             if (half == 0) {
 #pragma unroll
                 for (int b = 0; b < 10; ++b) ex->cross.x11[b][lane] = blocks[b];
             } else {
 #pragma unroll
-                for (int b = 0; b < 10; ++b) *reinterpret_cast<f32x4*>(&ex->x22t[b][m][4 * q]) = blocks[b];
+                for (int b = 0; b < 10; ++b) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) ex->x22[b][4 * q + r][m] = blocks[b][r];
+                }
             }
         }
     }
@@ -1086,8 +1096,10 @@ __device__ __forceinline__ void run_split_tile(const KernelArgs& args, SplitLds&
 // 128-token chunks: the 64x64 block A21 of A (rows 64..127, columns 0..63)
 // for two of its four 16-row block rows (w2 = 0: rows 64..95, 1: rows
 // 96..127), left in the workgroup's LDS as left-operand-layout images.
-// A21[i][j] = beta_i (k_i . k_j) exp(clamp(g_i - g_j)): every element takes
-// its own clamped exponential (rows and columns come from different halves).
+// A21[i][j] = beta_i (k_i . k_j) exp(clamp(g_i - g_j)), formed like the
+// diagonal blocks: as a row and a column factor around the Gram when the
+// chunk's gates lie within half the clamp of its first row's, else with a
+// clamped exponential per element.
 struct CrossIn {
     float g_lo;  // gate of first-half row `lane` (a column of A21)
     float g_hi;  // gate of second-half row 64 + lane
@@ -1125,32 +1137,54 @@ __device__ __forceinline__ void cross_gate_sum(CrossIn& c, int lane)
 // acc[bi][bj]: S21 block (2 w2 + bi, bj) in left-operand layout, i.e. lane
 // (q, m) holds S21[m][4q + r]: second-half row 32 w2 + 16 bi + m, first-half
 // column 16 bj + 4q + r.  Turned into the A21 blocks in place.
-__device__ __forceinline__ void cross_scale(const KernelArgs& args, GateLds& lds, int lane, int w2, const CrossIn& in,
-                                            f32x4 (&acc)[2][4])
+__device__ __forceinline__ void cross_scale(const KernelArgs& args, GateLds& lds, int lane, int w2, int L,
+                                            const CrossIn& in, f32x4 (&acc)[2][4])
 {
     const int q = lane / 16;
     const int m = lane % 16;
-    lds.row_scale[lane] = in.b_hi;
-    lds.gate[lane] = in.g_hi;
-    lds.col_scale[lane] = in.g_lo;
+    const bool has_g = args.g != nullptr;
+    const bool valid_lo = lane < L, valid_hi = 64 + lane < L;
+    // Factored gate, as in the 64-row epilogue: with every valid gate of the
+    // chunk within 25 of row 0's, A21_ij = (r_i S21_ij) c_j with
+    // r_i = beta_i exp(g_i - g_0) and c_j = exp(g_0 - g_j) (the clamp
+    // cannot bind); otherwise each element takes its clamped exponential.
+    bool factored = false;
+    if (has_g) {
+        const float gref = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, in.g_lo)));
+        factored = __all((!valid_lo || fabsf(in.g_lo - gref) <= 0.5f * kGateClamp) &&
+                         (!valid_hi || fabsf(in.g_hi - gref) <= 0.5f * kGateClamp));
+        if (factored) {
+            lds.row_scale[lane] = valid_hi ? in.b_hi * __expf(in.g_hi - gref) : 0.0f;
+            lds.col_scale[lane] = valid_lo ? __expf(gref - in.g_lo) : 0.0f;
+        } else {
+            lds.row_scale[lane] = in.b_hi;
+            lds.gate[lane] = in.g_hi;
+            lds.col_scale[lane] = in.g_lo;
+        }
+    } else {
+        lds.row_scale[lane] = in.b_hi;
+    }
     wave_lds_sync();
 #pragma unroll
     for (int bi = 0; bi < 2; ++bi) {
         const int row = 32 * w2 + 16 * bi + m;
         const float br = lds.row_scale[row];
-        const float gr = lds.gate[row];
 #pragma unroll
         for (int bj = 0; bj < 4; ++bj) {
             f32x4 a;
-            if (args.g != nullptr) {
+            if (!has_g) {
+                a = br * acc[bi][bj];
+            } else if (factored) {
+                const f32x4 cc = *reinterpret_cast<const f32x4*>(&lds.col_scale[16 * bj + 4 * q]);
+                a = (br * acc[bi][bj]) * cc;
+            } else {
+                const float gr = lds.gate[row];
                 const f32x4 gc = *reinterpret_cast<const f32x4*>(&lds.col_scale[16 * bj + 4 * q]);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const float d = fminf(fmaxf(gr - gc[r], -kGateClamp), kGateClamp);
                     a[r] = br * (acc[bi][bj][r] * __expf(d));
                 }
-            } else {
-                a = br * acc[bi][bj];
             }
             acc[bi][bj] = a;
         }
@@ -1248,7 +1282,7 @@ __device__ __forceinline__ void cross_block_rows(const KernelArgs& args, GateLds
         cross_gram<IN, kPass>(fr, fc, acc);
         __builtin_amdgcn_sched_barrier(0);
     }
-    cross_scale(args, lds, lane, w2, in, acc);
+    cross_scale(args, lds, lane, w2, L, in, acc);
 }
 
 // The one-wave-per-tile kernels size their LDS at launch: one WaveLds per
@@ -1412,7 +1446,7 @@ void kkt_solve128_kernel(const KernelArgs args)
                 }
                 cross_gram<IN, kPer>(fs, fc, acc);
             }
-            cross_scale(args, ex.cross_gate[w2], lane, w2, cin, acc);
+            cross_scale(args, ex.cross_gate[w2], lane, w2, L, cin, acc);
         } else {
             cross_block_rows<IN, K, GATE_SUM>(args, ex.cross_gate[w2], lane, tok, L, w2, acc, cin);
         }
@@ -1463,9 +1497,8 @@ void kkt_solve128_kernel(const KernelArgs args)
             f32x4 sum = zero4;
 #pragma unroll
             for (int k = 0; k <= i; ++k) {
-                f32x4 xa;  // X22_ik in left-operand layout: row m, columns 4q .. 4q+3
-#pragma unroll
-                for (int r = 0; r < 4; ++r) xa[r] = ex.x22t[tri(i, k)][4 * q + r][m];
+                // X22_ik in left-operand layout: row m, columns 4q .. 4q+3
+                const f32x4 xa = *reinterpret_cast<const f32x4*>(&ex.x22[tri(i, k)][m][4 * q]);
                 sum = mm16(xa, pc[k], sum);
             }
             x21[i] = zero4 - sum;
