@@ -13,7 +13,9 @@ step reads its keys from HBM.
 --op picks what one step is: the fused op (default), or one step of the
 unfused two-step chain on its own (scaled_dot: k, g, beta -> A in fp32;
 solve_tril: A -> (I+A)^{-1}), or the whole chain (both launches, A through
-HBM).
+HBM), or the memory-traffic reference (floor: libkkt_floor.so's kernel,
+which moves the fused op's bytes in its access pattern with no arithmetic;
+sequences of whole 64-token chunks only).
 
 Timed region: K steps captured in one HIP graph (launch overhead of the
 Python/ctypes call path is not the op's), bracketed by a device
@@ -49,11 +51,11 @@ KERNEL_SRC = os.path.join(ROOT, "chunked_gated_delta_token_amd", "csrc", "kkt_so
 KERNELS = {"fused": "kkt_solve_kernel", "scaled_dot": "kkt_scaled_dot_kernel",
            "solve_tril": "kkt_solve_tril_kernel", "chain": "kkt_scaled_dot_kernel+kkt_solve_tril_kernel",
            "gate_cumsum": "kkt_solve_gate_cumsum_kernel", "fused128": "kkt_solve128_kernel",
-           "gate_cumsum128": "kkt_solve128_kernel"}
+           "gate_cumsum128": "kkt_solve128_kernel", "floor": "stream_floor_kernel"}
 # names of the profile files (fused128 / gate_cumsum128: those ops with 128-token chunks)
 ENTRY = {"fused": "kkt_solve", "scaled_dot": "kkt_scaled_dot", "solve_tril": "kkt_solve_tril",
          "gate_cumsum": "kkt_solve_gate_cumsum", "fused128": "kkt_solve128",
-         "gate_cumsum128": "kkt_solve_gate_cumsum128"}
+         "gate_cumsum128": "kkt_solve_gate_cumsum128", "floor": "stream_floor"}
 
 
 SPLIT_MAX_TILES = 256          # the library's bound for two-wave tiles of the fused op (KKT_SPLIT_TILES overrides it)
@@ -111,7 +113,7 @@ def algorithmic_bytes(w, n_tokens: int, op: str = "fused", cu_seqlens=None, chun
     H, K = w.H, w.K
     k_gb = H * K * ESIZE[w.in_dtype] + H * 4 * (int(w.gate) + int(w.beta))
     out = H * chunk * ESIZE[w.out_dtype]
-    if op in ("fused", "chain"):
+    if op in ("fused", "chain", "floor"):
         return (k_gb + out) * n_tokens
     if op == "gate_cumsum":
         return (k_gb + out + H * 4) * n_tokens
@@ -121,8 +123,28 @@ def algorithmic_bytes(w, n_tokens: int, op: str = "fused", cu_seqlens=None, chun
     return lower + out * n_tokens
 
 
-def source_digest() -> str:
-    with open(KERNEL_SRC, "rb") as f:
+FLOOR_LIB = os.path.join(ROOT, "chunked_gated_delta_token_amd", "libkkt_floor.so")
+
+
+def load_floor():
+    """kkt_floor_copy from the in-tree libkkt_floor.so (raises if it is not built)."""
+    if not os.path.exists(FLOOR_LIB):
+        raise SystemExit(f"{FLOOR_LIB} is missing: build it with `python -m chunked_gated_delta_token_amd.build`")
+    lib = ctypes.CDLL(FLOOR_LIB)
+    fn = lib.kkt_floor_copy
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                   ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    return fn
+
+
+FLOOR_SRC = os.path.join(ROOT, "chunked_gated_delta_token_amd", "csrc", "stream_floor.hip")
+
+
+def source_digest(op: str = "fused") -> str:
+    """Digest of the source of the kernel an op runs (the memory-traffic
+    reference has its own source file)."""
+    with open(FLOOR_SRC if op == "floor" else KERNEL_SRC, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
@@ -263,7 +285,7 @@ def summarize_traffic(dirs, copy_bytes: int, op: str, workload: str, chunk: int 
         f"#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d <copy_fetch> -o p -- python -u $R/bench.py --copy-calibration {copy_bytes} --steps 20",
         f"#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d <copy_write> -o p -- python -u $R/bench.py --copy-calibration {copy_bytes} --steps 20",
         f"#   python $R/bench.py --summarize-traffic <op_fetch> <op_write> <copy_fetch> <copy_write> --copy-bytes {copy_bytes} {sel}",
-        f"kernel_source_sha256_16: {source_digest()}",
+        f"kernel_source_sha256_16: {source_digest(op)}",
         f"op_fetch_size_kib_median: {op_fetch:.1f}",
         f"op_write_size_kib_median: {op_write:.1f}",
         f"copy_bytes: {copy_bytes}",
@@ -308,7 +330,7 @@ def summarize_mfma(directory: str, op: str, workload: str, chunk: int = 64):
         f"{sel} --timing eager --steps 10 --warmup 2 --no-cpu-baseline",
         f"#   python $R/bench.py --summarize-mfma <dir> {sel}",
         "# busy cycles are summed over the SIMDs; one MFMA operation (MOPS) is 512 flop",
-        f"kernel_source_sha256_16: {source_digest()}",
+        f"kernel_source_sha256_16: {source_digest(op)}",
         f"mfma_busy_cycles_per_launch: {med['SQ_VALU_MFMA_BUSY_CYCLES']:.0f}",
         f"mfma_flop_bf16_per_launch: {512 * med['SQ_INSTS_VALU_MFMA_MOPS_BF16']:.0f}",
         f"mfma_flop_f16_per_launch: {512 * med['SQ_INSTS_VALU_MFMA_MOPS_F16']:.0f}",
@@ -389,7 +411,7 @@ def summarize_trace(directory: str, op: str, workload: str, run_log: str = None,
         "--steps 200 --warmup 20 --no-cpu-baseline > <run_log>",
         f"#   python -u $R/bench.py {sel} --no-cpu-baseline > <plain_log>",
         f"#   python $R/bench.py --summarize-trace <dir> {sel} --run-log <run_log> --plain-log <plain_log>",
-        f"kernel_source_sha256_16: {source_digest()}",
+        f"kernel_source_sha256_16: {source_digest(op)}",
         f"kernel: {st['Name']}",
         f"calls: {st['Calls']}",
         f"average_ns: {avg:.1f}",
@@ -461,6 +483,11 @@ def measure(name: str, op: str, chunk: int, steps: int, warmup: int, timing: str
         g0 = torch.from_numpy(inp.g_raw).to(dev)  # per-token log-decays, summed by the kernel
     if chunk != 64 and op not in ("fused", "gate_cumsum"):
         raise SystemExit("--chunk 128 applies to the fused op and its gate-sum form only")
+    floor_fn = None
+    if op == "floor":
+        if inp.cu_seqlens is not None or w.T % 64:
+            raise SystemExit("--op floor: sequences of whole 64-token chunks only")
+        floor_fn = load_floor()
     nbytes = algorithmic_bytes(w, n_tokens, op, inp.cu_seqlens, chunk)
     num_seqs = 0 if inp.cu_seqlens is None else len(inp.cu_seqlens) - 1
     stream = torch.cuda.Stream(dev)
@@ -478,7 +505,7 @@ def measure(name: str, op: str, chunk: int, steps: int, warmup: int, timing: str
     a_bytes = int(np.prod(shape)) * 4
     out_bytes = int(np.prod(shape)) * ESIZE[w.out_dtype]
     set_bytes = {"fused": nbytes, "gate_cumsum": nbytes, "scaled_dot": nbytes, "chain": nbytes + a_bytes,
-                 "solve_tril": a_bytes + out_bytes}[op]
+                 "solve_tril": a_bytes + out_bytes, "floor": nbytes}[op]
     R = max(2, -(-2 * MALL_BYTES // set_bytes))
     sets = []
     for _ in range(R):
@@ -513,6 +540,9 @@ def measure(name: str, op: str, chunk: int, steps: int, warmup: int, timing: str
         if op == "gate_cumsum":
             kargs_c = kargs[:9] + (chunk,) + kargs[10:]
             return [(lib.kkt_solve_gate_cumsum, kargs_c + (kdt[w.out_dtype], ptr(s_["out"]), ptr(s_["g_out"]), sp))]
+        if op == "floor":
+            return [(floor_fn, (ptr(s_["k"]), ptr(s_.get("g")), ptr(s_.get("b")), w.B, w.T, w.H,
+                                w.K * ESIZE[w.in_dtype], 64 * ESIZE[w.out_dtype], ptr(s_["out"]), sp))]
         tril = (lib.kkt_solve_tril, (ptr(s_["A"]), ptr(s_["cu"]), num_seqs, w.B, w.T, w.H, 64, kdt[w.out_dtype],
                                      ptr(s_.get("out")), sp))
         dot = (lib.kkt_scaled_dot, kargs + (ptr(s_["A"]), sp))
@@ -524,15 +554,16 @@ def measure(name: str, op: str, chunk: int, steps: int, warmup: int, timing: str
         for fn, a in calls[i % R]:
             st = fn(*a)
             if st != 0:
-                raise RuntimeError(f"{fn.__name__} status {st}: {kkt.last_error()}")
+                raise RuntimeError(f"{fn.__name__} status {st}" + ("" if op == "floor" else f": {kkt.last_error()}"))
 
     # correctness guard on the bench inputs (cheap structural check, no oracle)
     with torch.cuda.stream(stream):
         launch(0)
     torch.cuda.synchronize()
-    o = sets[0]["A" if op == "scaled_dot" else "out"].float()
-    assert torch.isfinite(o).all().item(), "non-finite output"
-    del o
+    if op != "floor":  # (the reference's output is the key bytes)
+        o = sets[0]["A" if op == "scaled_dot" else "out"].float()
+        assert torch.isfinite(o).all().item(), "non-finite output"
+        del o
 
     for i in range(warmup):
         launch(i)
@@ -601,8 +632,9 @@ def main():
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=None)
-    ap.add_argument("--op", choices=["fused", "gate_cumsum", "scaled_dot", "solve_tril", "chain"], default="fused",
-                    help="what one step runs (default: the fused op)")
+    ap.add_argument("--op", choices=["fused", "gate_cumsum", "scaled_dot", "solve_tril", "chain", "floor"],
+                    default="fused", help="what one step runs (default: the fused op; floor: the memory-traffic "
+                                          "reference kernel)")
     ap.add_argument("--chunk", type=int, choices=[64, 128], default=64,
                     help="chunk size of the fused op (128: the 128-token variant)")
     ap.add_argument("--timing", choices=["graph", "eager"], default="graph")
@@ -611,6 +643,8 @@ def main():
     ap.add_argument("--no-second-target", action="store_true",
                     help="time only the headline workload (by default the fused op's run also times "
                          "(2,16384,32,128) and reports it under second_target)")
+    ap.add_argument("--no-floor", action="store_true",
+                    help="skip the memory-traffic reference that the fused op's default run also times")
     ap.add_argument("--detail", action="store_true", help="also print per-launch event timings to stderr")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="instead of the op, run --steps plain device copies of BYTES bytes (the reference "
@@ -664,7 +698,7 @@ def main():
     ms_per_step, ev_ms, n_tiles, key = m["ms_per_step"], m["ev_ms"], m["n_tiles"], m["key"]
     K = args.steps
     achieved = nbytes / (ev_ms * 1e-3) / 1e9
-    digest = source_digest()
+    digest = source_digest(op)
     traffic = None if op == "chain" else read_traffic(digest, traffic_file(key, name))
     value = nbytes / (ms_per_step * 1e-3) / 1e9
     metric = METRIC if (op == "fused" and chunk == 64 and name == W.BENCH_WORKLOAD) else {
@@ -674,7 +708,9 @@ def main():
                        f"sum in the kernel ms/iter & achieved HBM GB/s on {name}, 1 GPU",
         "scaled_dot": "KKT A alone (first step of the unfused chain) ms/iter & achieved HBM GB/s, 1 GPU",
         "solve_tril": "solve of a given A (second step of the unfused chain) ms/iter & achieved HBM GB/s, 1 GPU",
-        "chain": "unfused two-step chain (A through HBM) ms/iter & GB/s of the fused op's bytes, 1 GPU"}[op]
+        "chain": "unfused two-step chain (A through HBM) ms/iter & GB/s of the fused op's bytes, 1 GPU",
+        "floor": f"memory-traffic reference (the fused op's bytes and access pattern, no arithmetic) ms/iter & "
+                 f"HBM GB/s on {name}, 1 GPU"}[op]
     pages_ms = {"fused": PAGES_FUSED_MS, "chain": PAGES_TWO_OP_MS}.get(op) if chunk == 64 else None
     line = {
         "metric": metric,
@@ -726,7 +762,18 @@ def main():
             "gram_frac_of_16bit_peak": round(gram / (ev_ms * 1e-3) / 2.5e15, 4) if gram else None,
             "f32_tflops": round(mf["mfma_flop_f32_per_launch"] / (ev_ms * 1e-3) / 1e12, 2),
         }
-    if not args.no_cpu_baseline:
+    if op == "fused" and chunk == 64 and name == W.BENCH_WORKLOAD and not args.no_floor:
+        # the memory-traffic reference on the same workloads, timed the same
+        # way: what the same bytes in the same pattern take with no arithmetic
+        for wl, obj in ((name, line["roofline"]), (SECOND_TARGET, line.get("second_target"))):
+            if obj is None:
+                continue
+            mfl = measure(wl, "floor", 64, args.steps, min(args.warmup, 20), args.timing)
+            achf = mfl["nbytes"] / (mfl["ev_ms"] * 1e-3) / 1e9
+            obj["floor"] = {"kernel": mfl["kernel"], "event_ms_per_step": round(mfl["ev_ms"], 6),
+                            "achieved": round(achf, 2), "frac": round(achf / HBM_PEAK_GBS, 4),
+                            "kernel_source_sha256_16": source_digest("floor")}
+    if not args.no_cpu_baseline and op != "floor":
         line["cpu_baseline"] = cpu_baseline(inp, nbytes, args.cpu_seconds, op, chunk)
     print(json.dumps(line), flush=True)
 

@@ -1,4 +1,6 @@
-"""Compile the HIP library ``libkkt_solve.so`` for gfx950, in-tree.
+"""Compile the HIP libraries for gfx950, in-tree: ``libkkt_solve.so`` (the
+operation) and ``libkkt_floor.so`` (the memory-traffic reference the
+benchmark times beside it).
 
     python -m chunked_gated_delta_token_amd.build
 """
@@ -13,6 +15,8 @@ ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc", "kkt_solve.hip")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libkkt_solve.so")
+FLOOR_SRC = os.path.join(PKG, "csrc", "stream_floor.hip")
+FLOOR_LIB = os.path.join(PKG, "libkkt_floor.so")
 ARCH = "gfx950"
 
 
@@ -22,9 +26,10 @@ def hipcc() -> str:
     return path if os.path.exists(path) else "hipcc"
 
 
-def build(verbose: bool = False, extra_flags=(), out: str = None) -> str:
-    """Build the shared library (at ``out``, default the package's
-    ``libkkt_solve.so``); returns its path.  Raises on failure."""
+def build(verbose: bool = False, extra_flags=(), out: str = None, src: str = None) -> str:
+    """Build the shared library of ``src`` (default the operation's source)
+    at ``out`` (default the package's ``libkkt_solve.so``); returns its path.
+    Raises on failure."""
     lib = out or LIB
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
            # packed fp32 VALU ops stay off (see the kernel notes); hipcc's host
@@ -32,7 +37,7 @@ def build(verbose: bool = False, extra_flags=(), out: str = None) -> str:
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
            # MFMA results in ordinary VGPRs: no accumulator-register copies
            "-mllvm", "-amdgpu-mfma-vgpr-form=1",
-           "-Wall", "-I", INCLUDE, "-o", lib + ".tmp", SRC, *extra_flags]
+           "-Wall", "-I", INCLUDE, "-o", lib + ".tmp", src or SRC, *extra_flags]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -45,5 +50,11 @@ def build(verbose: bool = False, extra_flags=(), out: str = None) -> str:
     return lib
 
 
+def build_floor(verbose: bool = False) -> str:
+    """Build ``libkkt_floor.so``, the memory-traffic reference; returns its path."""
+    return build(verbose=verbose, out=FLOOR_LIB, src=FLOOR_SRC)
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_floor(verbose=True))
