@@ -68,7 +68,7 @@
 
 #include "kkt_solve.h"
 
-#define KKT_VERSION_NUMBER 800  // 0.8.0
+#define KKT_VERSION_NUMBER 900  // 0.9.0
 
 namespace {
 
@@ -117,19 +117,65 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRawBufferFlags);
 }
 
-// The resource for k-step s (64 bytes of a key row) of a tile whose kernel
-// is built for K_T: the tile's own for s < k_steps, one of zero length beyond
-// (every load through it returns 0).  A kernel built for K_T serves every K
-// that is a multiple of 32 in (K_T / 2, K_T] (K_T = 64: also K = 32), so the
-// steps of K_T / 2 + 32 elements are always present and need no select; the
-// others take a scalar select (k_steps is wave-uniform).
+// Key pieces of a kernel built for K_T.  A call takes the smallest K_T >= K,
+// and the key bytes beyond the row's K * element size must enter the Gram as
+// zeros.  A kernel built for K_T serves the K in (K_T / 2, K_T] (K_T = 64:
+// every K up to 64) whose rows are whole 16-byte pieces.
+//   - k-step s (64 bytes of a row: a 16-byte piece per lane group q) is read
+//     through the tile's resource when it starts inside the row, and through
+//     one of zero length (every load returns 0) when it starts at or beyond
+//     the row's end: a scalar select per step (K is uniform).  The steps
+//     below the smallest K this kernel serves with whole steps, K_T / 2 plus
+//     one step, take no select.
+//   - A row that ends inside a k-step (`ragged`: 16-bit K not a multiple of
+//     32, fp32 K not a multiple of 16) reads that step whole, into the next
+//     key row or past the resource's end (zeros); once the loads have
+//     arrived, the lane groups whose piece lies past the row's end are
+//     zeroed (mask_key_tail, a uniform branch taken only for such K).
+// (Selecting per-lane offsets before the loads instead cost 0.3-0.4 us of
+// 7.7 on (1,8192,8,128), with or without a branch around them: the compiler
+// then scheduled the tile's loads worse, or waited for g and beta first.)
 template <int K_T, int ELT_BYTES>
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t k_step_rsrc(__amdgpu_buffer_rsrc_t r, int s, int k_steps)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t k_step_rsrc(__amdgpu_buffer_rsrc_t r, int s, uint32_t k_head_bytes)
 {
-    constexpr int kMinK = (K_T == 64) ? 32 : K_T / 2 + 32;
-    constexpr int kAlways = kMinK * ELT_BYTES / 64;
+    constexpr int kAlways = (K_T == 64) ? 1 : K_T * ELT_BYTES / 128 + 1;
     if (s < kAlways) return r;
-    return (s < k_steps) ? r : __builtin_amdgcn_make_buffer_rsrc(nullptr, 0, 0, kRawBufferFlags);
+    return ((uint32_t)s * 64u < k_head_bytes) ? r : __builtin_amdgcn_make_buffer_rsrc(nullptr, 0, 0, kRawBufferFlags);
+}
+
+// Key fragments f[b][s]: 16 bytes of the row at byte offset voff[b] (the
+// lane's piece in k-step 0) at k-step s0 + s, issued block by block.
+template <int K_T, int ELT_BYTES, int NB, int NS>
+__device__ __forceinline__ void load_key_frags(u32x4 (&f)[NB][NS], __amdgpu_buffer_rsrc_t r, const uint32_t (&voff)[NB],
+                                               int s0, uint32_t k_head_bytes)
+{
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            f[b][s] = __builtin_amdgcn_raw_buffer_load_b128(k_step_rsrc<K_T, ELT_BYTES>(r, s0 + s, k_head_bytes),
+                                                            voff[b] + (s0 + s) * 64, 0, 0);
+        }
+    }
+}
+
+// Zero the pieces of f (k-steps s0 ..) that lie past the row's end, when the
+// row ends inside a k-step.  Waits for the fragments.
+template <int K_T, int ELT_BYTES, int NB, int NS>
+__device__ __forceinline__ void mask_key_tail(u32x4 (&f)[NB][NS], int s0, int q, uint32_t k_head_bytes)
+{
+    if ((k_head_bytes & 63u) == 0) return;
+    constexpr int kFirst = (K_T == 64) ? 0 : (K_T / 2) * ELT_BYTES / 64;  // earliest step a row can end in
+    const int sp = (int)(k_head_bytes >> 6);                              // the step it ends in
+    const bool keep = (uint32_t)(q * 16) < (k_head_bytes & 63u);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        if (s0 + s < kFirst || s0 + s != sp) continue;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            if (!keep) f[b][s] = u32x4{0u, 0u, 0u, 0u};
+        }
+    }
 }
 
 // ---------------------------------------------------------------- element types
@@ -293,9 +339,8 @@ struct KernelArgs {
     float* g_out;               // gate-sum kernel: where the summed gate goes, or nullptr
     int32_t split_tiles;        // host only: launch the fused op's two-wave-per-tile form
     int32_t tile_waves;         // one-wave-per-tile kernels: waves (tiles) per workgroup, 1 or 4
-    int32_t k_steps;            // 64-byte k-steps of one key row (K * element size / 64); the
-                                // kernel's template K may be larger: its further steps read as 0
-    uint32_t k_head_bytes;      // bytes of one key row of one head (K * element size)
+    uint32_t k_head_bytes;      // bytes of one key row of one head (K * element size, a multiple of
+                                // 16); the kernel's template K may be larger: further pieces read as 0
     FastDiv div_H;              // division by H (tile -> chunk, head)
     FastDiv div_chunks;         // division by chunks_per_row (chunk -> batch row, chunk in row)
 };
@@ -395,7 +440,7 @@ __device__ __forceinline__ uint32_t workgroup_order(const KernelArgs& args)
     // loads it gates)
     asm volatile("" ::"s"(args.k), "s"(args.out), "s"(args.g), "s"(args.beta), "s"(args.cu_seqlens));
     asm volatile("" ::"s"(args.T), "s"(args.num_seqs), "s"(args.H), "s"(args.chunks_per_row), "s"(args.n_tiles),
-                 "s"(args.k_row_bytes), "s"(args.o_row_bytes), "s"(args.tile_waves), "s"(args.k_steps),
+                 "s"(args.k_row_bytes), "s"(args.o_row_bytes), "s"(args.tile_waves),
                  "s"(args.k_head_bytes), "s"(args.div_H.magic), "s"(args.div_H.shift), "s"(args.div_chunks.magic),
                  "s"(args.div_chunks.shift));
     const uint32_t n_groups = args.n_groups;
@@ -568,6 +613,18 @@ __device__ __forceinline__ void chunk_rows(const KernelArgs& args, WaveLds& lds,
             static_cast<const char*>(args.k) + tok * (int64_t)args.k_head_bytes,
             (uint32_t)(L - 1) * args.k_row_bytes + args.k_head_bytes);
 
+        // Byte offsets of this lane's key pieces in k-step 0 of each 16-row
+        // block, fixed here, before any load is in flight: formed later, one
+        // 32-bit multiply-add became a 64-bit one whose unused upper addend
+        // was allotted a register a g or beta load was still filling, and the
+        // wave then waited for that load before issuing its key loads.
+        uint32_t key_voff[4];
+#pragma unroll
+        for (int bi = 0; bi < 4; ++bi) {
+            key_voff[bi] = (row_base + (uint32_t)(16 * bi + m)) * args.k_row_bytes + q * 16;
+            asm volatile("" : "+v"(key_voff[bi]));
+        }
+
         // ---- a3: g and beta, one row per lane (rows >= L read as 0).  Issued
         // before the K tile: loads complete in order, so waiting for these two
         // does not wait for the whole tile.
@@ -594,17 +651,9 @@ __device__ __forceinline__ void chunk_rows(const KernelArgs& args, WaveLds& lds,
         // marked streaming (the lines must survive in L2 until then).  The
         // scheduling barrier keeps every load ahead of the first MFMA, so the
         // whole tile is in flight at once.
-        // (k-steps at or beyond args.k_steps, when K is below the template's
-        // K, are read through a zero-length resource: they return zeros,
-        // which add exact zeros to the Gram)
-#pragma unroll
-        for (int bi = 0; bi < 4; ++bi) {
-            const uint32_t voff = (row_base + (uint32_t)(16 * bi + m)) * args.k_row_bytes + q * 16;
-#pragma unroll
-            for (int s = 0; s < kSteps; ++s) {
-                frag[bi][s] = __builtin_amdgcn_raw_buffer_load_b128(k_step_rsrc<K, kInBytes>(k_rsrc, s, args.k_steps), voff + s * 64, 0, 0);
-            }
-        }
+        // (the bytes beyond K, when K is below the template's K, read as zeros
+        // or are zeroed before the Gram: load_key_frags, mask_key_tail)
+        load_key_frags<K, kInBytes>(frag, k_rsrc, key_voff, 0, args.k_head_bytes);
         __builtin_amdgcn_sched_barrier(0);
 
         // ---- gate from per-token log-decays (kkt_solve_gate_cumsum): the
@@ -653,6 +702,7 @@ __device__ __forceinline__ void chunk_rows(const KernelArgs& args, WaveLds& lds,
         }
         wave_lds_sync();
 
+        mask_key_tail<K, kInBytes>(frag, 0, q, args.k_head_bytes);
         // ---- a4: Gram blocks.  Block (i, j): lane (q, n=m) holds rows 16i + 4q + r, column 16j + n.
         f32x4 S[4][4];
         if constexpr (IN == Elt::F32) {
@@ -1260,25 +1310,16 @@ __device__ __forceinline__ void cross_block_rows(const KernelArgs& args, GateLds
 #pragma unroll
     for (int p0 = 0; p0 < kSteps; p0 += kPass) {
         u32x4 fr[2][kPass], fc[4][kPass];
+        uint32_t vr[2], vc[4];
 #pragma unroll
-        for (int bi = 0; bi < 2; ++bi) {
-            const uint32_t voff = (uint32_t)(64 + 32 * w2 + 16 * bi + m) * args.k_row_bytes + q * 16;
+        for (int bi = 0; bi < 2; ++bi) vr[bi] = (uint32_t)(64 + 32 * w2 + 16 * bi + m) * args.k_row_bytes + q * 16;
 #pragma unroll
-            for (int s = 0; s < kPass; ++s) {
-                fr[bi][s] = __builtin_amdgcn_raw_buffer_load_b128(k_step_rsrc<K, kInBytes>(k_rsrc, p0 + s, args.k_steps),
-                                                                  voff + (p0 + s) * 64, 0, 0);
-            }
-        }
-#pragma unroll
-        for (int bj = 0; bj < 4; ++bj) {
-            const uint32_t voff = (uint32_t)(16 * bj + m) * args.k_row_bytes + q * 16;
-#pragma unroll
-            for (int s = 0; s < kPass; ++s) {
-                fc[bj][s] = __builtin_amdgcn_raw_buffer_load_b128(k_step_rsrc<K, kInBytes>(k_rsrc, p0 + s, args.k_steps),
-                                                                  voff + (p0 + s) * 64, 0, 0);
-            }
-        }
+        for (int bj = 0; bj < 4; ++bj) vc[bj] = (uint32_t)(16 * bj + m) * args.k_row_bytes + q * 16;
+        load_key_frags<K, kInBytes>(fr, k_rsrc, vr, p0, args.k_head_bytes);
+        load_key_frags<K, kInBytes>(fc, k_rsrc, vc, p0, args.k_head_bytes);
         __builtin_amdgcn_sched_barrier(0);
+        mask_key_tail<K, kInBytes>(fr, p0, q, args.k_head_bytes);
+        mask_key_tail<K, kInBytes>(fc, p0, q, args.k_head_bytes);
         cross_gram<IN, kPass>(fr, fc, acc);
         __builtin_amdgcn_sched_barrier(0);
     }
@@ -1424,15 +1465,11 @@ void kkt_solve128_kernel(const KernelArgs args)
             }
             __syncthreads();  // the first half's key fragments are in LDS
             u32x4 fr[2][kSteps];
+            uint32_t vr[2];
 #pragma unroll
-            for (int bi = 0; bi < 2; ++bi) {
-                const uint32_t voff = (uint32_t)(64 + 32 * w2 + 16 * bi + m) * args.k_row_bytes + q * 16;
-#pragma unroll
-                for (int s = 0; s < kSteps; ++s) {
-                    fr[bi][s] = __builtin_amdgcn_raw_buffer_load_b128(k_step_rsrc<K, kInBytes>(k_rsrc, s, args.k_steps),
-                                                                      voff + s * 64, 0, 0);
-                }
-            }
+            for (int bi = 0; bi < 2; ++bi) vr[bi] = (uint32_t)(64 + 32 * w2 + 16 * bi + m) * args.k_row_bytes + q * 16;
+            load_key_frags<K, kInBytes>(fr, k_rsrc, vr, 0, args.k_head_bytes);
+            mask_key_tail<K, kInBytes>(fr, 0, q, args.k_head_bytes);
             constexpr int kPer = (IN == Elt::F32) ? 2 : 1;  // fragments per Gram step
 #pragma unroll
             for (int s = 0; s < kSteps; s += kPer) {
@@ -1591,8 +1628,8 @@ kkt_status_t validate_cu_seqlens(const int32_t* cu, int64_t num_seqs, int64_t T,
     return KKT_OK;
 }
 
-// The kernels are built for K = 64, 128 and 256; a smaller K that is a
-// multiple of 32 runs in the next one up, with its missing k-steps read as 0.
+// The kernels are built for K = 64, 128 and 256; any other K runs in the
+// next one up, with the key pieces beyond it read as 0 (k_piece_off).
 int64_t k_bucket(int64_t K) { return K <= 64 ? 64 : (K <= 128 ? 128 : 256); }
 
 // waves: the workgroup size in waves; the one-wave-per-tile kernels take
@@ -1820,17 +1857,21 @@ kkt_status_t setup(KernelArgs& a, const void* in, const float* g, const float* b
     a.split_tiles = split ? 1 : 0;
     a.tile_waves = (int32_t)tiles_per_group;
     a.k_head_bytes = (uint32_t)(in_row_bytes / H);
-    a.k_steps = (int32_t)(a.k_head_bytes / 64);
     a.div_H = make_fastdiv((uint32_t)H);
     a.div_chunks = make_fastdiv((uint32_t)(chunks_per_row > 0 ? chunks_per_row : 1));
     return KKT_OK;
 }
 
 // Size checks of the entry points that take k.
-kkt_status_t check_k_sizes(int64_t B, int64_t T, int64_t H, int64_t K, int64_t num_seqs, const int32_t* cu_seqlens)
+// K: up to 256, with key rows of whole 16-byte pieces (fp32: a multiple of
+// 4; bf16 / f16: a multiple of 8).
+kkt_status_t check_k_sizes(int64_t B, int64_t T, int64_t H, int64_t K, int64_t num_seqs, const int32_t* cu_seqlens,
+                           int64_t k_elt_bytes)
 {
     if (B < 1 || H < 1 || K < 1 || T < 0) return fail(KKT_ERR_INVALID_ARGUMENT, "B, H, K must be >= 1 and T >= 0");
-    if (K % 32 != 0 || K > 256) return fail(KKT_ERR_UNSUPPORTED, "K must be a multiple of 32 up to 256");
+    if (K > 256 || (K * k_elt_bytes) % 16 != 0) {
+        return fail(KKT_ERR_UNSUPPORTED, "K must be at most 256 and a multiple of 4 (fp32 keys) or 8 (bf16/f16 keys)");
+    }
     if (cu_seqlens != nullptr && (B != 1 || num_seqs < 1)) {
         return fail(KKT_ERR_INVALID_ARGUMENT, "cu_seqlens needs B == 1 and num_seqs >= 1");
     }
@@ -1853,7 +1894,7 @@ extern "C" kkt_status_t kkt_solve(const void* k, const float* g, const float* be
     }
     const kkt_dtype_t in_dtype = (kkt_dtype_t)enum_code(in_dtype_arg);
     const kkt_dtype_t out_dtype = (kkt_dtype_t)enum_code(out_dtype_arg);
-    kkt_status_t st = check_k_sizes(B, T, H, K, num_seqs, cu_seqlens);
+    kkt_status_t st = check_k_sizes(B, T, H, K, num_seqs, cu_seqlens, dtype_bytes(in_dtype));
     if (st != KKT_OK) return st;
     if (T == 0) return KKT_OK;
     KernelArgs a;
@@ -1884,7 +1925,7 @@ extern "C" kkt_status_t kkt_solve_gate_cumsum(const void* k, const float* g_deca
     }
     const kkt_dtype_t in_dtype = (kkt_dtype_t)enum_code(in_dtype_arg);
     const kkt_dtype_t out_dtype = (kkt_dtype_t)enum_code(out_dtype_arg);
-    kkt_status_t st = check_k_sizes(B, T, H, K, num_seqs, cu_seqlens);
+    kkt_status_t st = check_k_sizes(B, T, H, K, num_seqs, cu_seqlens, dtype_bytes(in_dtype));
     if (st != KKT_OK) return st;
     if (T == 0) return KKT_OK;
     if (g_decay == nullptr) return fail(KKT_ERR_INVALID_ARGUMENT, "g_decay must not be NULL");
@@ -1914,7 +1955,7 @@ extern "C" kkt_status_t kkt_scaled_dot(const void* k, const float* g, const floa
     if (chunk_size != kChunk) return fail(KKT_ERR_UNSUPPORTED, "chunk_size must be 64");
     if (!valid_dtype(enum_code(in_dtype_arg))) return fail(KKT_ERR_INVALID_ARGUMENT, "unknown dtype");
     const kkt_dtype_t in_dtype = (kkt_dtype_t)enum_code(in_dtype_arg);
-    kkt_status_t st = check_k_sizes(B, T, H, K, num_seqs, cu_seqlens);
+    kkt_status_t st = check_k_sizes(B, T, H, K, num_seqs, cu_seqlens, dtype_bytes(in_dtype));
     if (st != KKT_OK) return st;
     if (T == 0) return KKT_OK;
     KernelArgs a;

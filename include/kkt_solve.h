@@ -75,9 +75,10 @@ typedef enum {
  *              first.
  *   num_seqs   number of sequences; ignored when cu_seqlens is NULL.
  *   B, T, H, K sizes.  T may be 0 (nothing is launched).
- *              K must be a multiple of 32 from 32 to 256 (any key dtype); the
- *              PR #135 page shows K = 128 only, the rest is this library's
- *              range (KKT_ERR_UNSUPPORTED otherwise).
+ *              K is at most 256 and each key row a whole number of 16-byte
+ *              pieces: a multiple of 4 for fp32 keys, of 8 for bf16 / f16
+ *              keys.  The PR #135 page shows K = 128 only; the rest is this
+ *              library's range (KKT_ERR_UNSUPPORTED otherwise).
  *   chunk_size 64 or 128 (the chunk length; also the width of an output row).
  *   in_dtype   element type of k.
  *   out_dtype  element type of out.  bf16 / f16 results are rounded to nearest

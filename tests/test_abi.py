@@ -48,7 +48,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version(lib):
-    assert lib.kkt_version() == 800
+    assert lib.kkt_version() == 900
 
 
 def _call(lib, **over):
@@ -69,7 +69,10 @@ def _call(lib, **over):
     (dict(H=0), 1, ">= 1"),
     (dict(T=-1), 1, ">= 1"),
     (dict(K=100), 2, "K must be"),
-    (dict(K=16), 2, "K must be"),
+    (dict(K=20), 2, "K must be"),
+    (dict(K=6, in_dtype=0), 2, "K must be"),
+    (dict(K=258, in_dtype=0), 2, "K must be"),
+    (dict(K=264), 2, "K must be"),
     (dict(K=288), 2, "K must be"),
     (dict(K=512), 2, "K must be"),
     (dict(K=0), 1, ">= 1"),
@@ -89,16 +92,20 @@ def test_invalid_arguments_rejected_on_host(lib, over, status, msg):
     assert msg in kkt.last_error()
 
 
-@pytest.mark.parametrize("K", [32, 64, 96, 128, 160, 192, 224, 256])
 @pytest.mark.parametrize("in_dtype", [0, 1, 2])
-def test_every_multiple_of_32_up_to_256_passes_the_k_check(lib, K, in_dtype):
-    """Every key dtype takes K = 32, 64, ..., 256: with T = 0 the call passes
-    every argument check and returns KKT_OK without launching anything (so
-    this never touches a GPU, even where one is present)."""
+def test_k_check_takes_rows_of_whole_16_byte_pieces(lib, in_dtype):
+    """Every K from 1 to 300: the call passes the argument checks exactly when
+    K <= 256 and K * element size is a multiple of 16 bytes (fp32 keys: K a
+    multiple of 4; bf16 / f16: of 8).  With T = 0 a passing call returns
+    KKT_OK without launching anything (so this never touches a GPU, even
+    where one is present)."""
     from chunked_gated_delta_token_amd import kkt
-    for chunk in (64, 128):
-        assert _call(lib, K=K, in_dtype=in_dtype, T=0, chunk_size=chunk) == kkt.KKT_OK, kkt.last_error()
-    assert _call_scaled_dot(lib, K=K, in_dtype=in_dtype, T=0) == kkt.KKT_OK, kkt.last_error()
+    size = 4 if in_dtype == 0 else 2
+    for K in range(1, 301):
+        want = kkt.KKT_OK if (K <= 256 and (K * size) % 16 == 0) else kkt.KKT_ERR_UNSUPPORTED
+        for chunk in (64, 128):
+            assert _call(lib, K=K, in_dtype=in_dtype, T=0, chunk_size=chunk) == want, (K, kkt.last_error())
+        assert _call_scaled_dot(lib, K=K, in_dtype=in_dtype, T=0) == want, (K, kkt.last_error())
 
 
 def test_options_round_trip_and_reject_bad_values(lib):
@@ -154,7 +161,7 @@ def _call_scaled_dot(lib, **over):
     (dict(chunk_size=128), 2, "chunk_size"),
     (dict(in_dtype=5), 1, "dtype"),
     (dict(H=0), 1, ">= 1"),
-    (dict(K=80), 2, "K must be"),
+    (dict(K=84), 2, "K must be"),
     (dict(cu=16, num_seqs=1, B=3), 1, "cu_seqlens"),
     (dict(k=None), 1, "NULL"),
     (dict(A=None), 1, "NULL"),
@@ -191,7 +198,7 @@ def _call_gate_cumsum(lib, **over):
     (dict(chunk_size=32), 2, "chunk_size"),
     (dict(chunk_size=256), 2, "chunk_size"),
     (dict(out_dtype=9), 1, "dtype"),
-    (dict(K=48), 2, "K must be"),
+    (dict(K=52), 2, "K must be"),
     (dict(T=-1), 1, ">= 1"),
     (dict(g=None), 1, "g_decay"),
     (dict(k=None), 1, "NULL"),

@@ -73,7 +73,8 @@ def test_chunk128_lengths(kkt, T):
 # lane (16-bit K <= 128, fp32 K = 64); the others load keys per wave
 @pytest.mark.parametrize("K,in_dtype", [(64, "bf16"), (256, "bf16"), (64, "f32"), (128, "f32"), (256, "f32"),
                                         (64, "f16"), (32, "bf16"), (96, "bf16"), (192, "f16"), (224, "bf16"),
-                                        (32, "f32"), (96, "f32"), (160, "f32")])
+                                        (32, "f32"), (96, "f32"), (160, "f32"), (36, "f32"), (100, "f32"),
+                                        (252, "f32"), (40, "bf16"), (200, "f16")])
 def test_chunk128_head_dims(kkt, K, in_dtype):
     inp = W.generate("T256_H8_bf16_f32", T=260, H=2, K=K, in_dtype=in_dtype, seed=3200 + K)
     check(kkt, inp, "f32", f"K={K} {in_dtype}")

@@ -112,7 +112,8 @@ def test_gate_cumsum_dtypes(kkt, in_dtype, out_dtype):
     check(kkt, inp, out_dtype, f"{in_dtype}->{out_dtype}")
 
 
-@pytest.mark.parametrize("K,in_dtype,chunk", [(96, "bf16", 64), (160, "f32", 64), (32, "f16", 128), (192, "bf16", 128)])
+@pytest.mark.parametrize("K,in_dtype,chunk", [(96, "bf16", 64), (160, "f32", 64), (32, "f16", 128), (192, "bf16", 128),
+                                              (44, "f32", 64), (104, "bf16", 128)])
 def test_gate_cumsum_head_dims(kkt, K, in_dtype, chunk):
     inp = W.generate("T256_H8_bf16_f32", B=2, T=300, H=3, K=K, in_dtype=in_dtype, seed=2310 + K)
     check(kkt, inp, "f32", f"K={K} {in_dtype}", chunk=chunk)

@@ -92,13 +92,7 @@ def test_gate_beta_variants(kkt, gate, beta):
     check(kkt, inp, "bf16", f"gate={gate} beta={beta} bf16 out")
 
 
-@pytest.mark.parametrize("K", [32, 64, 96, 160, 192, 224, 256])
-@pytest.mark.parametrize("in_dtype", ["bf16", "f16", "f32"])
-def test_other_head_dims(kkt, K, in_dtype):
-    """Every multiple of 32 up to 256 (K = 128 is every workload's): the
-    kernels are built for 64, 128 and 256 and read the k-steps beyond a
-    smaller K as zeros.  The grid (6 tiles) takes the two-wave tiles; the
-    one-wave form is forced on the same inputs and must give the same bits."""
+def _head_dim_case(kkt, K, in_dtype):
     inp = W.generate("T256_H8_bf16_f32", T=130, H=2, K=K, in_dtype=in_dtype, seed=400 + K)
     two = check_bits(kkt, inp, "f32", f"K={K} {in_dtype}")
     with kkt.option(kkt.KKT_OPTION_SPLIT_MAX_TILES, 0):
@@ -106,7 +100,27 @@ def test_other_head_dims(kkt, K, in_dtype):
     assert np.array_equal(one.view(np.uint32), two.view(np.uint32))
 
 
-@pytest.mark.parametrize("K", [96, 160])
+@pytest.mark.parametrize("K", [32, 64, 96, 160, 192, 224, 256])
+@pytest.mark.parametrize("in_dtype", ["bf16", "f16", "f32"])
+def test_other_head_dims(kkt, K, in_dtype):
+    """Every multiple of 32 up to 256 (K = 128 is every workload's): the
+    kernels are built for 64, 128 and 256 and read the key pieces beyond a
+    smaller K as zeros.  The grid (6 tiles) takes the two-wave tiles; the
+    one-wave form is forced on the same inputs and must give the same bits."""
+    _head_dim_case(kkt, K, in_dtype)
+
+
+@pytest.mark.parametrize("K,in_dtype", [(4, "f32"), (36, "f32"), (68, "f32"), (100, "f32"), (132, "f32"),
+                                        (252, "f32"), (8, "bf16"), (40, "bf16"), (72, "bf16"), (136, "bf16"),
+                                        (248, "bf16"), (24, "f16"), (200, "f16")])
+def test_head_dims_ending_inside_a_k_step(kkt, K, in_dtype):
+    """K whose key rows end inside a 64-byte k-step (fp32: multiples of 4,
+    bf16 / f16: multiples of 8): the lane groups whose 16-byte piece lies
+    beyond K read zeros, the others their keys.  Both launch forms, same bits."""
+    _head_dim_case(kkt, K, in_dtype)
+
+
+@pytest.mark.parametrize("K", [96, 160, 40, 248])
 def test_other_head_dims_one_wave_grid(kkt, K):
     """A K below its kernel's on a grid of one-wave tiles with bf16 output and
     packed sequences (the last key row of the last head ends the tensor, so

@@ -139,7 +139,7 @@ def tril(**o):
                               a["do"], P(a["out"]), None)
 
 bad = [dict(ch=32), dict(ch=256), dict(di=3), dict(do=-1), dict(B=0), dict(H=0), dict(T=-1), dict(K=100),
-       dict(K=16), dict(K=288), dict(K=0), dict(cu=16, ns=2, B=2), dict(cu=16, ns=0), dict(k=None), dict(out=None),
+       dict(K=20), dict(K=6, di=0), dict(K=288), dict(K=0), dict(cu=16, ns=2, B=2), dict(cu=16, ns=0), dict(k=None), dict(out=None),
        dict(k=18), dict(out=72), dict(g=18), dict(beta=17), dict(cu=18, ns=1), dict(B=1 << 40, T=1 << 20)]
 # the arguments each entry point reads: an override of any other argument
 # would leave the call valid (and so launching), so it is not applied
@@ -153,8 +153,8 @@ for fn in (solve, gsum, sdot, tril):
             raise SystemExit(f"{fn.__name__}{o} passed its checks")
         assert lib.kkt_last_error()
 assert gsum(g=None) == 1 and gsum(gout=18) == 1
-for K in range(32, 257, 32):
-    for di in (0, 1, 2):
+for K in list(range(8, 257, 8)) + [4, 12, 36, 100, 252]:
+    for di in ((0,) if K % 8 else (0, 1, 2)):
         for ch in (64, 128):
             assert solve(K=K, di=di, ch=ch, T=0) == 0, lib.kkt_last_error()
             assert gsum(K=K, di=di, ch=ch, T=0) == 0, lib.kkt_last_error()
@@ -179,7 +179,7 @@ threads = [threading.Thread(target=worker, args=(i,)) for i in range(8)]
 [t.start() for t in threads]
 [t.join() for t in threads]
 assert not errors, errors[:3]
-assert lib.kkt_version() == 800
+assert lib.kkt_version() == 900
 print("abi exercise ok")
 '''
 
