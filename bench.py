@@ -280,8 +280,8 @@ def summarize_traffic(dirs, copy_bytes: int, op: str, workload: str, chunk: int 
     lines = [
         f"# HBM traffic of {kname}, workload {workload}",
         "# commands (from /tmp, repository at $R; each --pmc pass alone, the last command wrote this file):",
-        f"#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d <op_fetch> -o p -- python -u $R/bench.py {sel} --timing eager --steps 20 --warmup 2 --no-cpu-baseline",
-        f"#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d <op_write> -o p -- python -u $R/bench.py {sel} --timing eager --steps 20 --warmup 2 --no-cpu-baseline",
+        f"#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d <op_fetch> -o p -- python -u $R/bench.py {sel} --timing eager --steps 20 --warmup 2 --no-cpu-baseline --no-second-target --no-floor",
+        f"#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d <op_write> -o p -- python -u $R/bench.py {sel} --timing eager --steps 20 --warmup 2 --no-cpu-baseline --no-second-target --no-floor",
         f"#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d <copy_fetch> -o p -- python -u $R/bench.py --copy-calibration {copy_bytes} --steps 20",
         f"#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d <copy_write> -o p -- python -u $R/bench.py --copy-calibration {copy_bytes} --steps 20",
         f"#   python $R/bench.py --summarize-traffic <op_fetch> <op_write> <copy_fetch> <copy_write> --copy-bytes {copy_bytes} {sel}",
@@ -327,7 +327,7 @@ def summarize_mfma(directory: str, op: str, workload: str, chunk: int = 64):
         f"# MFMA counters of {kname}, workload {workload} (medians per launch)",
         "# commands (from /tmp, repository at $R; the last one wrote this file):",
         f"#   rocprofv3 --pmc {' '.join(MFMA_COUNTERS)} --output-format csv -d <dir> -o p -- python -u $R/bench.py "
-        f"{sel} --timing eager --steps 10 --warmup 2 --no-cpu-baseline",
+        f"{sel} --timing eager --steps 10 --warmup 2 --no-cpu-baseline --no-second-target --no-floor",
         f"#   python $R/bench.py --summarize-mfma <dir> {sel}",
         "# busy cycles are summed over the SIMDs; one MFMA operation (MOPS) is 512 flop",
         f"kernel_source_sha256_16: {source_digest(op)}",
@@ -408,8 +408,8 @@ def summarize_trace(directory: str, op: str, workload: str, run_log: str = None,
         f"{w.in_dtype} -> {w.out_dtype}; {nbytes} algorithmic bytes per launch",
         "# commands (from /tmp, repository at $R; the last one wrote this file):",
         f"#   rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o kt -- python -u $R/bench.py {sel} "
-        "--steps 200 --warmup 20 --no-cpu-baseline > <run_log>",
-        f"#   python -u $R/bench.py {sel} --no-cpu-baseline > <plain_log>",
+        "--steps 200 --warmup 20 --no-cpu-baseline --no-second-target --no-floor > <run_log>",
+        f"#   python -u $R/bench.py {sel} --no-cpu-baseline --no-second-target --no-floor > <plain_log>",
         f"#   python $R/bench.py --summarize-trace <dir> {sel} --run-log <run_log> --plain-log <plain_log>",
         f"kernel_source_sha256_16: {source_digest(op)}",
         f"kernel: {st['Name']}",

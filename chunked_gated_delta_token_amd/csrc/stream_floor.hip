@@ -1,8 +1,15 @@
 // Memory-traffic reference for the fused chunk-local KKT + solve (64-token
 // chunks, sequences of whole chunks).  It moves exactly the bytes one fused
 // step moves, in the fused kernel's pattern, and does no arithmetic:
-//   - one 64-row tile (one chunk of one head) per wave, four waves per
-//     workgroup, tiles in the fused kernel's order (head fastest);
+//   - one 64-row tile (one chunk of one head) per wave, four waves (four
+//     heads of a chunk) per workgroup, in the fused kernel's XCD order: grids
+//     of up to 1024 workgroups spread in contiguous ranges over the 8 XCDs,
+//     larger ones keep all the workgroups of a chunk on one XCD with the
+//     chunks round-robin over the XCDs (the heads of a token share the cache
+//     lines of g and beta, so each line is fetched by one L2).  (The fused
+//     kernel runs grids of up to 1024 tiles in one-wave workgroups; for this
+//     kernel that form is slower, 7.3 vs 6.7 us at (1,8192,8,128), so the
+//     reference keeps four waves);
 //   - g and beta of the tile's rows first (one row per lane), then every key
 //     row in 16-byte loads, all issued before any store;
 //   - the tile's output rows written in whole-row 16-byte pieces with
@@ -25,6 +32,7 @@ namespace {
 constexpr int kWave = 64;
 constexpr int kRows = 64;        // rows of one tile
 constexpr int kWavesPerGroup = 4;
+constexpr uint32_t kContiguousMaxGroups = 1024;  // grids of up to this many workgroups: contiguous XCD ranges
 constexpr int kNonTemporal = 2;  // cache-policy bit "nt", as on the fused kernel's output stores
 
 using u32x4 = uint32_t __attribute__((ext_vector_type(4)));
@@ -44,18 +52,36 @@ struct FloorArgs {
     int32_t chunks_per_row;
     uint32_t n_tiles;
     int64_t T;
+    uint32_t n_groups;         // workgroups of the grid
+    int32_t contiguous;        // 1: each XCD takes one contiguous range of workgroups' tiles
+    int32_t log2_run;          // otherwise: runs of 2^log2_run workgroups stay on one XCD
+    uint32_t remap_groups;     // workgroups in whole rounds of runs (the rest keep their order)
 };
 
+// Workgroup w runs on XCD w % 8 (the hardware's round-robin); the tile group
+// it takes, as described at the top.
+__device__ __forceinline__ uint32_t tile_group(const FloorArgs& a)
+{
+    const uint32_t w = blockIdx.x, xcd = w % 8, slot = w / 8;
+    if (a.contiguous) {
+        const uint32_t per = a.n_groups / 8, extra = a.n_groups % 8;
+        return (xcd < extra) ? xcd * (per + 1) + slot : extra * (per + 1) + (xcd - extra) * per + slot;
+    }
+    if (w >= a.remap_groups) return w;
+    const uint32_t lg = (uint32_t)a.log2_run;
+    return ((((slot >> lg) << 3) + xcd) << lg) | (slot & ((1u << lg) - 1u));
+}
+
 // KRB: key row bytes (128, 256 or 512); ORB: output row bytes (128 or 256).
-template <int KRB, int ORB>
-__global__ __launch_bounds__(kWave * kWavesPerGroup) void stream_floor_kernel(const FloorArgs a)
+template <int KRB, int ORB, int WAVES>
+__global__ __launch_bounds__(kWave * WAVES) void stream_floor_kernel(const FloorArgs a)
 {
     constexpr int kPieces = KRB / 16;                   // 16-byte pieces of a key row
     constexpr int kPasses = kPieces > 16 ? kPieces / 16 : 1;
     constexpr int kOutPieces = ORB / 16;
     static_assert(kOutPieces <= 16, "one pass of 16 lanes per output row");
     const int lane = threadIdx.x % kWave;
-    const uint32_t tile = blockIdx.x * kWavesPerGroup + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const uint32_t tile = tile_group(a) * WAVES + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     if (tile >= a.n_tiles) return;  // wave-uniform
     const uint32_t H = (uint32_t)a.H;
     const uint32_t chunk = tile / H;
@@ -112,10 +138,18 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup) void stream_floor_kernel(co
 }
 
 template <int KRB, int ORB>
-hipError_t launch(const FloorArgs& a, hipStream_t stream)
+hipError_t launch(FloorArgs a, hipStream_t stream)
 {
-    const uint32_t groups = (a.n_tiles + kWavesPerGroup - 1) / kWavesPerGroup;
-    hipLaunchKernelGGL((stream_floor_kernel<KRB, ORB>), dim3(groups), dim3(kWave * kWavesPerGroup), 0, stream, a);
+    const uint32_t waves = kWavesPerGroup;
+    a.n_groups = (a.n_tiles + waves - 1) / waves;
+    a.contiguous = a.n_groups <= kContiguousMaxGroups ? 1 : 0;
+    const uint32_t per_chunk = ((uint32_t)a.H + waves - 1) / waves;  // workgroups per chunk
+    int lg = 0;
+    while ((2u << lg) <= per_chunk && lg < 16) ++lg;
+    a.log2_run = lg;
+    a.remap_groups = (a.n_groups >> (lg + 3)) << (lg + 3);
+    hipLaunchKernelGGL((stream_floor_kernel<KRB, ORB, kWavesPerGroup>), dim3(a.n_groups), dim3(kWave * kWavesPerGroup),
+                       0, stream, a);
     return hipGetLastError();
 }
 
