@@ -614,15 +614,22 @@ __device__ __forceinline__ void chunk_rows(const KernelArgs& args, WaveLds& lds,
             (uint32_t)(L - 1) * args.k_row_bytes + args.k_head_bytes);
 
         // Byte offsets of this lane's key pieces in k-step 0 of each 16-row
-        // block, fixed here, before any load is in flight: formed later, one
-        // 32-bit multiply-add became a 64-bit one whose unused upper addend
-        // was allotted a register a g or beta load was still filling, and the
-        // wave then waited for that load before issuing its key loads.
+        // block.  One tile per wave: fixed here, before any load is in
+        // flight (formed later, one 32-bit multiply-add became a 64-bit one
+        // whose unused upper addend was allotted a register a g or beta load
+        // was still filling, and the wave then waited for that load before
+        // issuing its key loads; (1,8192,8,128) 7.8 -> 7.5 us).  Two-wave
+        // tiles form them at the loads: hoisted, their small grids took
+        // 0.58 us longer (4.38 -> 4.96 us on 32 tiles).
         uint32_t key_voff[4];
+        auto key_offsets = [&] {
 #pragma unroll
-        for (int bi = 0; bi < 4; ++bi) {
-            key_voff[bi] = (row_base + (uint32_t)(16 * bi + m)) * args.k_row_bytes + q * 16;
-            asm volatile("" : "+v"(key_voff[bi]));
+            for (int bi = 0; bi < 4; ++bi) key_voff[bi] = (row_base + (uint32_t)(16 * bi + m)) * args.k_row_bytes + q * 16;
+        };
+        if constexpr (SPLIT == 0) {
+            key_offsets();
+#pragma unroll
+            for (int bi = 0; bi < 4; ++bi) asm volatile("" : "+v"(key_voff[bi]));
         }
 
         // ---- a3: g and beta, one row per lane (rows >= L read as 0).  Issued
@@ -653,6 +660,7 @@ __device__ __forceinline__ void chunk_rows(const KernelArgs& args, WaveLds& lds,
         // whole tile is in flight at once.
         // (the bytes beyond K, when K is below the template's K, read as zeros
         // or are zeroed before the Gram: load_key_frags, mask_key_tail)
+        if constexpr (SPLIT != 0) key_offsets();
         load_key_frags<K, kInBytes>(frag, k_rsrc, key_voff, 0, args.k_head_bytes);
         __builtin_amdgcn_sched_barrier(0);
 
@@ -1765,8 +1773,12 @@ constexpr int64_t kSplitMaxTiles = 256;
 // 8.34-8.37, its gate-sum form 8.70-8.74 vs 8.70-8.71, the solve of a given A
 // 6.49-6.51 vs 6.44-6.46, the first step of the chain 7.33-7.36 vs
 // 6.82-6.87; beyond, four-wave workgroups are faster (16384 tiles: 75.0 vs
-// 80.2; 1876: 20.0 vs 21.0-21.4).
-constexpr int64_t kWave1GroupTilesFused = 1024;  // kkt_solve
+// 80.2; 1876: 20.0 vs 21.0-21.4).  Since the key offsets are fixed before
+// the g/beta loads, the fused op on 1024 tiles is faster in four-wave
+// workgroups (7.43-7.54 vs 7.55-7.66 us, same box), while one-wave ones
+// still win on 768 tiles (6.80-6.91 vs 6.85-6.97) and 512 (6.16-6.22 vs
+// 6.82-6.86).
+constexpr int64_t kWave1GroupTilesFused = 768;   // kkt_solve
 constexpr int64_t kWave1GroupTiles = 512;        // the other entry points
 
 // Process-wide options (kkt_set_option).  Their start values come from the
