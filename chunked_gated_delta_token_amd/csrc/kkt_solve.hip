@@ -600,7 +600,7 @@ __device__ __forceinline__ void chunk_rows(const KernelArgs& args, WaveLds& lds,
                     uint32_t voff = (uint32_t)(16 * i + 4 * q + r) * args.k_row_bytes + (16 * j + m) * 4;
                     if (j == i && r == 0 && q == 0) voff = 0x80000000u;
                     const float a = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(a_rsrc, voff, 0, 0));
-                    A[i][j][r] = (j < i) ? -a : a;  // off-diagonal blocks negated, as the fused op forms them
+                    A[i][j][r] = a;
                 }
             }
         }
@@ -984,21 +984,26 @@ __device__ __forceinline__ void chunk_rows(const KernelArgs& args, WaveLds& lds,
     // X_dd in both operand layouts (blk[d][col][row] = X_dd[row][col]):
     //   xa[d]: lane (q, m) holds X_dd[m][4q .. 4q+3]   (left operand)
     //   xd[d]: lane (q, n) holds X_dd[4q .. 4q+3][n]   (right operand / result layout)
+    // (the solve of a given A negates xa instead of its loaded A blocks: see
+    // below)
+    constexpr float kXaSign = (MODE == Mode::SolveTril) ? -1.0f : 1.0f;
     f32x4 xa[4], xd[4];
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
         xd[d] = *reinterpret_cast<const f32x4*>(&blk[d][m][4 * q]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) xa[d][r] = blk[d][4 * q + r][m];
+        for (int r = 0; r < 4; ++r) xa[d][r] = kXaSign * blk[d][4 * q + r][m];
     }
 
-    // ---- a7: merge.  The off-diagonal blocks of A arrive negated (the
-    // epilogue's column factor, or the solve's load, carries the sign), so
-    // wt_ik = -(X_ii A_ik)^T, whose result layout is the left-operand layout
-    // of -W_ik, and every X_ij = -sum_k W_ik X_kj is a plain accumulation
-    // (the same value, bit for bit, as 0 - sum: negating every product
-    // negates the rounded sum, and an all-zero sum stays +0.0 from the +0.0
-    // start).
+    // ---- a7: merge.  wt_ik = -(X_ii A_ik)^T: the off-diagonal blocks of A
+    // arrive negated from the epilogue (its column factor carries the sign),
+    // and the solve of a given A negates xa (negating it as each element of
+    // A loads cost that kernel 0.5 us of 6.3 on (1,8192,8,128)); a negated
+    // factor negates each product exactly, so both give the same bits.  The
+    // result layout of wt is the left-operand layout of -W_ik, and every
+    // X_ij = -sum_k W_ik X_kj is a plain accumulation (the same value, bit
+    // for bit, as 0 - sum: negating every product negates the rounded sum,
+    // and an all-zero sum stays +0.0 from the +0.0 start).
     if constexpr (SPLIT == 1) {
         // block rows 0..2; X10 and X21 go to the other wave before the
         // second barrier, X20 before the third
