@@ -1642,7 +1642,8 @@ kkt_status_t validate_cu_seqlens(const int32_t* cu, int64_t num_seqs, int64_t T,
 }
 
 // The kernels are built for K = 64, 128 and 256; any other K runs in the
-// next one up, with the key pieces beyond it read as 0 (k_piece_off).
+// next one up, with the key bytes beyond it read or zeroed as 0 (k_step_rsrc,
+// mask_key_tail).
 int64_t k_bucket(int64_t K) { return K <= 64 ? 64 : (K <= 128 ? 128 : 256); }
 
 // waves: the workgroup size in waves; the one-wave-per-tile kernels take
