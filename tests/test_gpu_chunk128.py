@@ -14,7 +14,7 @@ import pytest
 
 import oracle
 from chunked_gated_delta_token_amd import workloads as W
-from tests._compare import compare
+from tests._compare import compare, fused_bound
 from tests._gpu_util import TORCH_DT, from_device, load_kkt, say, to_device
 
 torch = pytest.importorskip("torch")
@@ -44,7 +44,7 @@ def check(kkt, inp: W.Inputs, out_dtype: str, label: str) -> dict:
         f"seqs={0 if inp.cu_seqlens is None else len(inp.cu_seqlens) - 1}")
     got = run(kkt, inp, out_dtype)
     ref = oracle.kkt_solve_ref(inp.k64(), inp.g, inp.beta, inp.cu_seqlens, chunk_size=CH)
-    stats = compare(got, ref, out_dtype, inp.cu_seqlens, label)
+    stats = compare(got, ref, out_dtype, inp.cu_seqlens, label, fused_bound(inp, ref, CH))
     say("[ok] " + json.dumps(stats))
     return stats
 

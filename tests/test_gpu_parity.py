@@ -15,7 +15,7 @@ import pytest
 
 import oracle
 from chunked_gated_delta_token_amd import workloads as W
-from tests._compare import compare
+from tests._compare import compare, fused_bound
 from tests._gpu_util import TORCH_DT, from_device, load_kkt, say, to_device
 
 torch = pytest.importorskip("torch")
@@ -45,7 +45,8 @@ def check_bits(kkt, inp: W.Inputs, out_dtype: str, label: str) -> np.ndarray:
     w = inp.workload
     say(f"[case] {label}: B={w.B} T={w.T} H={w.H} K={w.K} in={w.in_dtype} out={out_dtype}")
     got = run_gpu(kkt, inp, out_dtype)
-    say("[ok] " + json.dumps(compare(got, reference(inp), out_dtype, inp.cu_seqlens, label)))
+    ref = reference(inp)
+    say("[ok] " + json.dumps(compare(got, ref, out_dtype, inp.cu_seqlens, label, fused_bound(inp, ref))))
     return got
 
 
@@ -55,7 +56,8 @@ def check(kkt, inp: W.Inputs, out_dtype: str, label: str) -> dict:
         f"g={inp.g is not None} beta={inp.beta is not None} "
         f"seqs={0 if inp.cu_seqlens is None else len(inp.cu_seqlens) - 1}")
     got = run_gpu(kkt, inp, out_dtype)
-    stats = compare(got, reference(inp), out_dtype, inp.cu_seqlens, label)
+    ref = reference(inp)
+    stats = compare(got, ref, out_dtype, inp.cu_seqlens, label, fused_bound(inp, ref))
     say("[ok] " + json.dumps(stats))
     return stats
 

@@ -2,9 +2,11 @@
 
 Sizes, head counts and dimensions, key and output dtypes, gate and beta
 presence, packed sequences (empty ones among them), chunk sizes and entry
-points are drawn from one fixed seed, so every run checks the same 96 cases;
-each is small enough for the oracle to finish at once.  The criteria are
-those of the targeted tests (their check functions are reused).
+points are drawn from fixed seeds, so every run checks the same cases: 96
+with K in {64, 128, 256}, then 48 with any K the library serves (up to 256,
+fp32 keys a multiple of 4, 16-bit keys a multiple of 8).  Each is small
+enough for the oracle to finish at once.  The criteria are those of the
+targeted tests (their check functions are reused).
 """
 from __future__ import annotations
 
@@ -25,7 +27,7 @@ ENTRIES = ("fused", "fused128", "gate_cumsum", "chain")
 DTYPES = ("bf16", "f16", "f32")
 
 
-def _draw_cases(n=96, seed=9000):
+def _draw_cases(n=96, seed=9000, any_k=False, first=0):
     rng = np.random.default_rng(seed)
     cases = []
     for i in range(n):
@@ -33,7 +35,11 @@ def _draw_cases(n=96, seed=9000):
         c = dict(entry=entry, H=int(rng.integers(1, 10)), K=int(rng.choice([64, 128, 256])),
                  in_dtype=str(rng.choice(DTYPES)), out_dtype=str(rng.choice(DTYPES)),
                  gate=bool(rng.random() < 0.75) or entry == "gate_cumsum", beta=bool(rng.random() < 0.75),
-                 seed=9100 + i)
+                 seed=9100 + first + i)
+        if any_k:
+            # rows of whole 16-byte pieces: multiples of 4 (fp32) or 8 (16-bit)
+            step = 4 if c["in_dtype"] == "f32" else 8
+            c["K"] = int(rng.integers(1, 256 // step + 1)) * step
         if rng.random() < 0.4:
             n_seqs = int(rng.integers(1, 90))
             lens = rng.integers(0, 300, size=n_seqs)
@@ -48,7 +54,7 @@ def _draw_cases(n=96, seed=9000):
     return cases
 
 
-CASES = _draw_cases()
+CASES = _draw_cases() + _draw_cases(n=48, seed=9500, any_k=True, first=96)
 
 
 @pytest.fixture(scope="module")

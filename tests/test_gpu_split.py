@@ -16,7 +16,7 @@ import pytest
 
 import oracle
 from chunked_gated_delta_token_amd import workloads as W
-from tests._compare import a_scale, compare, compare_A, structural_masks
+from tests._compare import a_scale, compare, compare_A, structural_masks, tril_bound
 from tests._gpu_util import TORCH_DT, from_device, load_kkt, say, to_device
 
 torch = pytest.importorskip("torch")
@@ -87,7 +87,7 @@ def check_solve_tril(kkt, inp: W.Inputs, out_dtype: str, label: str) -> dict:
     cu = None if inp.cu_seqlens is None else torch.from_numpy(inp.cu_seqlens).to("cuda:0")
     got = gpu_solve_tril(kkt, torch.from_numpy(A).to("cuda:0"), cu, out_dtype)
     ref = oracle.solve_tril_ref(A.astype(np.float64), inp.cu_seqlens)
-    stats = compare(got, ref, out_dtype, inp.cu_seqlens, label)
+    stats = compare(got, ref, out_dtype, inp.cu_seqlens, label, tril_bound(A, ref, inp.cu_seqlens))
     say("[ok] " + json.dumps(stats))
     return stats
 

@@ -17,7 +17,7 @@ import pytest
 
 import oracle
 from chunked_gated_delta_token_amd import workloads as W
-from tests._compare import compare
+from tests._compare import compare, fused_bound
 from tests._gpu_util import TORCH_DT, from_device, load_kkt, say, to_device
 
 torch = pytest.importorskip("torch")
@@ -52,7 +52,7 @@ def both_forms(kkt, inp: W.Inputs, out_dtype: str, label: str):
     view = np.uint32 if out_dtype == "f32" else np.uint16
     assert np.array_equal(one.view(view), two.view(view)), label
     ref = oracle.kkt_solve_ref(inp.k64(), inp.g, inp.beta, inp.cu_seqlens)
-    stats = compare(two, ref, out_dtype, inp.cu_seqlens, label)
+    stats = compare(two, ref, out_dtype, inp.cu_seqlens, label, fused_bound(inp, ref))
     say("[ok] " + json.dumps(stats))
 
 
@@ -184,5 +184,5 @@ def test_split_tiles_solve_tril(kkt, shape, out_dtype):
     fused = run_form(kkt, (k, g, b, cu), out_dtype, split=True)
     assert np.array_equal(res[1].view(view), fused.view(view))
     ref = oracle.kkt_solve_ref(inp.k64(), inp.g, inp.beta, inp.cu_seqlens)
-    compare(res[1], ref, out_dtype, inp.cu_seqlens, f"solve_tril split {shape}")
+    compare(res[1], ref, out_dtype, inp.cu_seqlens, f"solve_tril split {shape}", fused_bound(inp, ref))
     say("[ok]")
