@@ -68,7 +68,7 @@
 
 #include "kkt_solve.h"
 
-#define KKT_VERSION_NUMBER 900  // 0.9.0
+#define KKT_VERSION_NUMBER 901  // 0.9.1
 
 namespace {
 
@@ -343,6 +343,8 @@ struct KernelArgs {
                                 // 16); the kernel's template K may be larger: further pieces read as 0
     FastDiv div_H;              // division by H (tile -> chunk, head)
     FastDiv div_chunks;         // division by chunks_per_row (chunk -> batch row, chunk in row)
+    int32_t gate_gather;        // gate-sum kernel: the four tiles of a workgroup (four heads of one
+                                // chunk) write their summed gates together (run_tile)
 };
 
 // ---------------------------------------------------------------- tile map (a1)
@@ -678,12 +680,8 @@ __device__ __forceinline__ void chunk_rows(const KernelArgs& args, WaveLds& lds,
                     const float total = __shfl(wave_prefix_sum(g_first, lane), kWave - 1, kWave);
                     gv = total + gv;
                 }
-            } else if (args.g_out != nullptr && SPLIT == 0) {
-                const uint32_t span = (uint32_t)(L - 1) * (uint32_t)H * 4u + 4u;
-                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, gv), make_rsrc(args.g_out + tok, span),
-                                                      (uint32_t)lane * (uint32_t)H * 4u, 0, 0);
             }
-            g_sum = gv;
+            g_sum = gv;  // written to g_out after the tile's rows (below)
         }
 
         // ---- a5, first part: the row and column scales of the epilogue.
@@ -1080,6 +1078,27 @@ __device__ __forceinline__ void chunk_rows(const KernelArgs& args, WaveLds& lds,
         const f32x4 x30 = mm16(wt32, x20, p30);
         store_block_row(3, x30, x31, x32, xd[3]);
 
+        if constexpr (GATE_SUM && CH == 64) {
+            // The summed gate goes last.  Each of these stores writes one
+            // 4-byte word per lane into 64 cache lines that the tiles of the
+            // other heads write too.  Issued right after the scan, while the
+            // key tile was still arriving, they cost 0.9 us of 8.5 on
+            // (1,8192,8,128); here nothing measurable.
+            if (args.g != nullptr && args.g_out != nullptr) {
+                if (args.gate_gather) {
+                    // to the workgroup's store (run_tile); row_scale is no
+                    // longer read
+                    wave_lds_sync();
+                    lds.row_scale[lane] = g_sum;
+                } else {
+                    const uint32_t span = (uint32_t)(L - 1) * (uint32_t)H * 4u + 4u;
+                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, g_sum),
+                                                          make_rsrc(args.g_out + tok, span),
+                                                          (uint32_t)lane * (uint32_t)H * 4u, 0, 0);
+                }
+            }
+        }
+
         if constexpr (CH == 128) {
             __syncthreads();  // end of the first phase: the exchange area overlaps its areas
             // hand the block to the workgroup: X11 as result-layout register
@@ -1120,6 +1139,27 @@ __device__ __forceinline__ void run_tile(const KernelArgs& args, WaveLds* lds_al
     if (tile.len <= 0) return;  // wave-uniform
     chunk_rows<MODE, IN, OUT, K, GATE_SUM, kChunk>(args, lds_all[wave], lds_all[wave].blk, nullptr, lane,
                                                    tile.row0 * H + h, tile.len, 0, nullptr);
+    if constexpr (GATE_SUM && MODE == Mode::Fused) {
+        // Large grids of fixed-length rows with H a multiple of 4: the four
+        // tiles of this workgroup are heads h - wave .. h - wave + 3 of one
+        // chunk (every one valid), and their summed gates of a token are 16
+        // contiguous bytes, written by one lane: a quarter of the strided
+        // write requests.  (2,16384,32,128): 80.9 -> 77.8 us; on
+        // (1,8192,8,128), one tile per SIMD, the barrier cost 0.2 us, so
+        // there each wave writes its own words.
+        if (args.gate_gather) {
+            __syncthreads();  // every wave's row_scale holds its summed gate
+            const int t = 16 * wave + lane;
+            if (lane < 16 && t < tile.len) {
+                const f32x4 v = {lds_all[0].row_scale[t], lds_all[1].row_scale[t], lds_all[2].row_scale[t],
+                                 lds_all[3].row_scale[t]};
+                const uint32_t span = (uint32_t)(tile.len - 1) * (uint32_t)H * 4u + 16u;
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v),
+                                                       make_rsrc(args.g_out + tile.row0 * H + (h - wave), span),
+                                                       (uint32_t)t * (uint32_t)H * 4u, 0, 0);
+            }
+        }
+    }
 }
 
 // LDS of a 64-token tile split over two waves: their own gate arrays and
@@ -1454,6 +1494,9 @@ void kkt_solve128_kernel(const KernelArgs args)
     constexpr int kInBytes = EltInfo<IN>::bytes;
     constexpr int kSteps = K / (4 * (16 / kInBytes));
     static_assert(STAGE == kKeysGlobal || kSteps <= 4, "the LDS key image holds at most 4 k-steps");
+    float gsum_lo = 0.0f, gsum_hi = 0.0f;  // GATE_SUM: wave 2's summed gate, stored last
+    (void)gsum_lo;
+    (void)gsum_hi;
     if (wave < 2) {
         chunk_rows<Mode::Fused, IN, OUT, K, GATE_SUM, 2 * kChunk, STAGE == kKeysShared>(
             args, ex.half[wave], ex.half[wave].blk, nullptr, lane, tok, L, wave, &ex);
@@ -1503,15 +1546,8 @@ void kkt_solve128_kernel(const KernelArgs args)
         __syncthreads();  // end of the first phase: the exchange area overlaps its areas
         cross_store(ex, lane, w2, acc);
         if constexpr (GATE_SUM) {
-            // every wave has read its decays by now, so g_out may alias them
-            if (w2 == 0 && args.g != nullptr && args.g_out != nullptr) {
-                const uint32_t span = (uint32_t)(L - 1) * (uint32_t)H * 4u + 4u;
-                const __amdgpu_buffer_rsrc_t go = make_rsrc(args.g_out + tok, span);
-                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, cin.g_lo), go,
-                                                      (uint32_t)lane * (uint32_t)H * 4u, 0, 0);
-                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, cin.g_hi), go,
-                                                      (64u + (uint32_t)lane) * (uint32_t)H * 4u, 0, 0);
-            }
+            gsum_lo = cin.g_lo;
+            gsum_hi = cin.g_hi;
         }
     }
     __syncthreads();
@@ -1589,6 +1625,19 @@ void kkt_solve128_kernel(const KernelArgs args)
             p[3] = pack2<OUT>(v1[2], v1[3]);
             __builtin_amdgcn_raw_buffer_store_b128(p, o_rsrc, (uint32_t)(64 + rr) * args.o_row_bytes + c8 * 2, 0,
                                                    kNonTemporal);
+        }
+    }
+    if constexpr (GATE_SUM) {
+        // the summed gate of both halves, after the rows (strided 4-byte
+        // words: see the 64-token tile; every wave has read its decays long
+        // before, so g_out may alias them)
+        if (wave == 2 && args.g != nullptr && args.g_out != nullptr) {
+            const uint32_t span = (uint32_t)(L - 1) * (uint32_t)H * 4u + 4u;
+            const __amdgpu_buffer_rsrc_t go = make_rsrc(args.g_out + tok, span);
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, gsum_lo), go,
+                                                  (uint32_t)lane * (uint32_t)H * 4u, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, gsum_hi), go,
+                                                  (64u + (uint32_t)lane) * (uint32_t)H * 4u, 0, 0);
         }
     }
 }
@@ -1756,6 +1805,9 @@ int64_t dtype_bytes(kkt_dtype_t d) { return d == KKT_DTYPE_F32 ? 4 : 2; }
 // ones keep chunks in round-robin order over the XCDs (each XCD's concurrent
 // accesses spread over the whole tensor), with all heads of a chunk on one XCD.
 constexpr int64_t kRemapMaxGroups = 1024;
+// Gate-sum grids of more four-wave workgroups than this gather the summed
+// gates of a workgroup's four heads (run_tile).
+constexpr int64_t kGateGatherMinGroups = 1024;
 #ifndef KKT_LARGE_GRID_ORDER
 #define KKT_LARGE_GRID_ORDER kChunkRoundRobin
 #endif
@@ -1872,6 +1924,7 @@ kkt_status_t setup(KernelArgs& a, const void* in, const float* g, const float* b
     a.log2_group_run = lg;
     a.remap_groups = (uint32_t)((groups >> (lg + 3)) << (lg + 3));
     a.g_out = nullptr;
+    a.gate_gather = 0;
     a.split_tiles = split ? 1 : 0;
     a.tile_waves = (int32_t)tiles_per_group;
     a.k_head_bytes = (uint32_t)(in_row_bytes / H);
@@ -1953,6 +2006,13 @@ extern "C" kkt_status_t kkt_solve_gate_cumsum(const void* k, const float* g_deca
                H * chunk_size * dtype_bytes(out_dtype), out, stream, chunk_size, true, kWave1GroupTiles);
     if (st != KKT_OK) return st;
     a.g_out = g_out;
+    // four heads' summed gates per 16-byte store (run_tile): only where every
+    // four-wave workgroup holds four valid tiles of one chunk, and on grids
+    // of more workgroups than run at once on the chip (below that, the
+    // barrier it needs lengthens the tiles' tail)
+    a.gate_gather = (cu_seqlens == nullptr && chunk_size == kChunk && !a.split_tiles && a.tile_waves == 4 &&
+                     H % 4 == 0 && a.n_groups > kGateGatherMinGroups && g_out != nullptr &&
+                     (reinterpret_cast<uintptr_t>(g_out) & 15u) == 0) ? 1 : 0;
 
     hipError_t e;
     switch (in_dtype) {

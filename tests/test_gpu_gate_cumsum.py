@@ -133,6 +133,39 @@ def test_gate_cumsum_in_place_and_without_gate_output(kkt):
     assert np.array_equal(X_none.view(np.uint32), ref_X.view(np.uint32))
 
 
+def _run_g_out_at(kkt, inp: W.Inputs, offset: int):
+    """The gate-sum op with g_out a view ``offset`` words into a larger
+    buffer (offset 1: not 16-byte aligned)."""
+    k, _g, b, cu = to_device(inp)
+    a = torch.from_numpy(inp.g_raw).to(k.device)
+    B, T, H, _ = k.shape
+    out = torch.full((B, T, H, 64), float("nan"), dtype=torch.float32, device=k.device)
+    buf = torch.full((B * T * H + 4,), float("nan"), dtype=torch.float32, device=k.device)
+    g_out = buf[offset:offset + B * T * H].view(B, T, H)
+    kkt.kkt_solve_gate_cumsum(k, a, b, cu, output_dtype=torch.float32, out=out, g_out=g_out)
+    torch.cuda.synchronize()
+    return from_device(out, "f32"), g_out.cpu().numpy()
+
+
+@pytest.mark.parametrize("B,T,H", [(1, 65536 + 37, 4), (3, 22000, 8)])
+def test_gate_cumsum_gathered_gate_stores(kkt, B, T, H):
+    """Grids of more than 1024 four-wave workgroups, fixed-length rows, H a
+    multiple of 4: each workgroup writes its four heads' summed gates
+    together.  Against the oracle (a partial last chunk included), in place
+    too, and bit-equal to the per-wave stores taken when g_out is not
+    16-byte aligned."""
+    inp = W.generate("T256_H8_bf16_f32", B=B, T=T, H=H, K=64, seed=2450 + H)
+    assert B * -(-T // 64) * H > 4 * 1024
+    check(kkt, inp, "f32", f"gathered B={B} T={T} H={H}")
+    say(f"[case] gathered gate stores, in place and unaligned: B={B} T={T} H={H}")
+    X_al, g_al = run(kkt, inp, "f32")
+    X_in, g_in = run(kkt, inp, "f32", in_place=True)
+    X_un, g_un = _run_g_out_at(kkt, inp, 1)
+    for X, g in ((X_in, g_in), (X_un, g_un)):
+        assert np.array_equal(X.view(np.uint32), X_al.view(np.uint32))
+        assert np.array_equal(g.view(np.uint32), g_al.view(np.uint32))
+
+
 # ---------------------------------------------------------------- 128-token chunks
 @pytest.mark.parametrize("name", GATED)
 def test_gate_cumsum128_full_parity(kkt, name):
