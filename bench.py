@@ -524,6 +524,8 @@ def measure(name: str, op: str, chunk: int, steps: int, warmup: int, timing: str
     del k0, g0, b0
     if op == "solve_tril":
         del A0
+    # the copies above ran on the current stream; the launches go to `stream`
+    torch.cuda.synchronize()
 
     def ptr(t):
         return None if t is None else ctypes.c_void_p(t.data_ptr())

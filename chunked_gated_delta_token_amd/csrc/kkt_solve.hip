@@ -849,6 +849,29 @@ __device__ __forceinline__ void chunk_rows(const KernelArgs& args, WaveLds& lds,
         }
     };
 
+    // One 128-byte line of each of the 16 rows of block row i of a 64-token
+    // chunk with fp32 output: columns 32 hl .. 32 hl + 31 from the blocks b0
+    // and b1 (8 lanes per line, 8 rows per pass).
+    // (called only where OUT is F32 and CH is 64)
+    auto store_row_line = [&](int i, int hl, f32x4 b0, f32x4 b1) {
+        wave_lds_sync();  // earlier reads of the area are done
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            lds.stage[4 * q + r][0 + m] = b0[r];
+            lds.stage[4 * q + r][16 + m] = b1[r];
+        }
+        wave_lds_sync();
+        const int rsub = lane / 8, c4 = (lane % 8) * 4;
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+            const int rr = 8 * it + rsub;
+            const f32x4 v = *reinterpret_cast<const f32x4*>(&lds.stage[rr][c4]);
+            const uint32_t voff = (row_base + (uint32_t)(16 * i + rr)) * args.o_row_bytes + (col_base + 32 * hl + c4) * 4;
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), o_rsrc, voff, 0, kNonTemporal);
+        }
+    };
+    (void)store_row_line;
+
     if constexpr (MODE == Mode::ScaledDot) {
         // ---- A itself: strict lower triangle of every chunk, zeros elsewhere
 #pragma unroll
@@ -1058,25 +1081,56 @@ __device__ __forceinline__ void chunk_rows(const KernelArgs& args, WaveLds& lds,
         // times slower overall on the (2,16384,32,128) workload.  With
         // 128-token chunks this half's blocks also go to the rest of the
         // workgroup.
-        store_block_row(0, xd[0], zero4, zero4, zero4);
         // The partial products that do not wait on this level's results are
-        // issued before each block-row store, so the MFMA pipe works through
-        // them while the store's LDS and memory instructions execute.
-        const f32x4 x10 = mm16(wt10, xd[0], zero4);
-        const f32x4 x21 = mm16(wt21, xd[1], zero4);
-        const f32x4 x32 = mm16(wt32, xd[2], zero4);
-        const f32x4 p20 = mm16(wt20, xd[0], zero4);
-        const f32x4 p31 = mm16(wt31, xd[1], zero4);
-        f32x4 p30 = mm16(wt30, xd[0], zero4);
-        store_block_row(1, x10, xd[1], zero4, zero4);
+        // issued before each store, so the MFMA pipe works through them while
+        // the store's LDS and memory instructions execute.
+        f32x4 x10, x21, x32, x20, x31, x30;
+        if constexpr (OUT == Elt::F32 && CH == 64) {
+            // fp32 rows of 64-token chunks are two 128-byte lines (columns
+            // 0..31, 32..63), and each line goes out once its two blocks are
+            // final: the right half of block row 2 (X22, zeros) right after
+            // the diagonal inverses, that of block row 3 (X32, X33) after the
+            // first merge level, the left halves after the second and third.
+            // After the last product 2 KB of the tile's 16 remain to be
+            // written instead of 8.  Same box, µs: (1,8192,8,128) 7.47-7.53
+            // -> 7.32-7.38, 512 tiles 6.25-6.36 -> 5.99-6.12, 4096 tiles
+            // 24.64-24.76 -> 24.28-24.35; fp32 keys unchanged.
+            store_block_row(0, xd[0], zero4, zero4, zero4);
+            store_row_line(2, 1, xd[2], zero4);
+            x10 = mm16(wt10, xd[0], zero4);
+            x21 = mm16(wt21, xd[1], zero4);
+            x32 = mm16(wt32, xd[2], zero4);
+            const f32x4 p20 = mm16(wt20, xd[0], zero4);
+            const f32x4 p31 = mm16(wt31, xd[1], zero4);
+            f32x4 p30 = mm16(wt30, xd[0], zero4);
+            store_block_row(1, x10, xd[1], zero4, zero4);
+            store_row_line(3, 1, x32, xd[3]);
 
-        const f32x4 x20 = mm16(wt21, x10, p20);
-        const f32x4 x31 = mm16(wt32, x21, p31);
-        p30 = mm16(wt31, x10, p30);
-        store_block_row(2, x20, x21, xd[2], zero4);
+            x20 = mm16(wt21, x10, p20);
+            x31 = mm16(wt32, x21, p31);
+            p30 = mm16(wt31, x10, p30);
+            store_row_line(2, 0, x20, x21);
 
-        const f32x4 x30 = mm16(wt32, x20, p30);
-        store_block_row(3, x30, x31, x32, xd[3]);
+            x30 = mm16(wt32, x20, p30);
+            store_row_line(3, 0, x30, x31);
+        } else {
+            store_block_row(0, xd[0], zero4, zero4, zero4);
+            x10 = mm16(wt10, xd[0], zero4);
+            x21 = mm16(wt21, xd[1], zero4);
+            x32 = mm16(wt32, xd[2], zero4);
+            const f32x4 p20 = mm16(wt20, xd[0], zero4);
+            const f32x4 p31 = mm16(wt31, xd[1], zero4);
+            f32x4 p30 = mm16(wt30, xd[0], zero4);
+            store_block_row(1, x10, xd[1], zero4, zero4);
+
+            x20 = mm16(wt21, x10, p20);
+            x31 = mm16(wt32, x21, p31);
+            p30 = mm16(wt31, x10, p30);
+            store_block_row(2, x20, x21, xd[2], zero4);
+
+            x30 = mm16(wt32, x20, p30);
+            store_block_row(3, x30, x31, x32, xd[3]);
+        }
 
         if constexpr (GATE_SUM && CH == 64) {
             // The summed gate goes last.  Each of these stores writes one
