@@ -871,6 +871,18 @@ __device__ __forceinline__ void chunk_rows(const KernelArgs& args, WaveLds& lds,
         }
     };
     (void)store_row_line;
+    // Columns 32..63 of block row i (0 or 1) of a 64-token chunk with fp32
+    // output: all zeros, stored straight from registers.
+    auto store_zero_lines = [&](int i) {
+        const int rsub = lane / 8, c4 = (lane % 8) * 4;
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+            const int rr = 8 * it + rsub;
+            const uint32_t voff = (row_base + (uint32_t)(16 * i + rr)) * args.o_row_bytes + (col_base + 32 + c4) * 4;
+            __builtin_amdgcn_raw_buffer_store_b128(u32x4{0u, 0u, 0u, 0u}, o_rsrc, voff, 0, kNonTemporal);
+        }
+    };
+    (void)store_zero_lines;
 
     if constexpr (MODE == Mode::ScaledDot) {
         // ---- A itself: strict lower triangle of every chunk, zeros elsewhere
@@ -1094,8 +1106,15 @@ __device__ __forceinline__ void chunk_rows(const KernelArgs& args, WaveLds& lds,
             // After the last product 2 KB of the tile's 16 remain to be
             // written instead of 8.  Same box, µs: (1,8192,8,128) 7.47-7.53
             // -> 7.32-7.38, 512 tiles 6.25-6.36 -> 5.99-6.12, 4096 tiles
-            // 24.64-24.76 -> 24.28-24.35; fp32 keys unchanged.
-            store_block_row(0, xd[0], zero4, zero4, zero4);
+            // 24.64-24.76 -> 24.28-24.35; fp32 keys unchanged.  The all-zero
+            // right halves of block rows 0 and 1 skip the LDS staging
+            // (another box: 7.12-7.20 -> 7.03-7.06, 4096 tiles 19.94-20.04 ->
+            // 19.75-19.81; stored right after the key loads instead, they
+            // cost 0.1-0.2 us).  In the two-wave tiles of small grids the
+            // same line stores took longer: 32 tiles 4.38 -> 4.70 us, 250
+            // tiles with fp32 output 4.85 -> 5.07 us.
+            store_row_line(0, 0, xd[0], zero4);
+            store_zero_lines(0);
             store_row_line(2, 1, xd[2], zero4);
             x10 = mm16(wt10, xd[0], zero4);
             x21 = mm16(wt21, xd[1], zero4);
@@ -1103,7 +1122,8 @@ __device__ __forceinline__ void chunk_rows(const KernelArgs& args, WaveLds& lds,
             const f32x4 p20 = mm16(wt20, xd[0], zero4);
             const f32x4 p31 = mm16(wt31, xd[1], zero4);
             f32x4 p30 = mm16(wt30, xd[0], zero4);
-            store_block_row(1, x10, xd[1], zero4, zero4);
+            store_row_line(1, 0, x10, xd[1]);
+            store_zero_lines(1);
             store_row_line(3, 1, x32, xd[3]);
 
             x20 = mm16(wt21, x10, p20);
