@@ -1084,9 +1084,9 @@ __device__ __forceinline__ void chunk_rows(const KernelArgs& args, WaveLds& lds,
     const f32x4 wt32 = mm16(A[3][2], xa[3], zero4);
 
     {
-        // The blocks are formed in the result layout and each block row is
-        // staged through LDS, so that every store instruction writes whole
-        // output rows (4 rows of 256 bytes, or 8 of 128).  Stored straight
+        // The blocks are formed in the result layout and staged through LDS,
+        // so that every store instruction writes whole 128-byte lines (4 rows
+        // of 256 bytes, or 8 of 128; fp32 line by line below).  Stored straight
         // from registers, each instruction writes a 64- or 32-byte piece of
         // 16 rows, twice or four times the cache lines per instruction: that
         // measured slower in the store phase on the bench workload and 1.6
@@ -1104,7 +1104,7 @@ __device__ __forceinline__ void chunk_rows(const KernelArgs& args, WaveLds& lds,
             // the diagonal inverses, that of block row 3 (X32, X33) after the
             // first merge level, the left halves after the second and third.
             // After the last product 2 KB of the tile's 16 remain to be
-            // written instead of 8.  Same box, µs: (1,8192,8,128) 7.47-7.53
+            // written instead of 8.  Same box, us: (1,8192,8,128) 7.47-7.53
             // -> 7.32-7.38, 512 tiles 6.25-6.36 -> 5.99-6.12, 4096 tiles
             // 24.64-24.76 -> 24.28-24.35; fp32 keys unchanged.  The all-zero
             // right halves of block rows 0 and 1 skip the LDS staging
@@ -1898,7 +1898,7 @@ constexpr int64_t kSplitMaxTiles = 256;
 // Grids that run one tile per wave use workgroups of one wave up to a bound
 // (the hardware spreads them over every CU; four-wave workgroups put a small
 // grid on a quarter or half of the CUs), of four waves beyond it.  Measured
-// one-wave against four-wave workgroups (µs, bf16 keys, K = 128): the fused
+// one-wave against four-wave workgroups (us, bf16 keys, K = 128): the fused
 // op on 512 tiles 6.11-6.14 vs 6.74, on 448 tiles with fp32 keys 9.17-9.19 vs
 // 10.34-10.36; the first step of the chain on 256 and 32 tiles 4.15-4.16 vs
 // 5.46-5.48 and 3.47-3.48 vs 4.93; at 1024 tiles the fused op 8.22-8.24 vs
