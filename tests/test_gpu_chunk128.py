@@ -14,6 +14,7 @@ import pytest
 
 import oracle
 from chunked_gated_delta_token_amd import workloads as W
+from tests import _edge
 from tests._compare import compare, fused_bound
 from tests._gpu_util import TORCH_DT, from_device, load_kkt, say, to_device
 
@@ -170,3 +171,17 @@ def test_chunk128_repeatable(kkt, case):
         kkt.kkt_solve(k, g, b, cu, chunk_size=CH, output_dtype=TORCH_DT[out_dtype], out=out)
         assert torch.equal(out.view(bits), first.view(bits)), rep
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("out_dtype", ["f32", "f16"])
+@pytest.mark.parametrize("T,H", [(300, 3), (2400, 8)])
+@pytest.mark.parametrize("kind", _edge.KINDS)
+def test_chunk128_edge_inputs(kkt, kind, T, H, out_dtype):
+    """The edge inputs of the 64-token tests at 128-token chunks (gates
+    restarted every 128 tokens).  fp32 and f16
+    output: the one-bf16-ulp rule is the one stated for decaying gates; with
+    gates that rise, an element that nearly cancels in a chunk with |X| ~ 13
+    measured 1.3e-7 off (fp32 arithmetic, fast exp), past that rule's
+    2^-23 floor, and f16 output carries the fp32 error bound."""
+    inp = _edge.edge_inputs(kind, T, H, seed=590 + T % 7, chunk=CH)
+    check(kkt, inp, out_dtype, f"{kind} T={T} H={H}")

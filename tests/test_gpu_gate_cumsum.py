@@ -166,6 +166,19 @@ def test_gate_cumsum_gathered_gate_stores(kkt, B, T, H):
         assert np.array_equal(g.view(np.uint32), g_al.view(np.uint32))
 
 
+@pytest.mark.parametrize("chunk", [64, 128])
+def test_gate_cumsum_rising_and_wandering_decays(kkt, chunk):
+    """Per-token log-decays of both signs (the summed gate rises and falls)
+    and signed beta with zeros."""
+    inp = W.generate("T256_H8_bf16_f32", B=2, T=700, H=4, seed=2460 + chunk)
+    rng = np.random.default_rng(2461 + chunk)
+    inp.g_raw = rng.uniform(-0.3, 0.3 if chunk == 64 else 0.2, inp.g_raw.shape).astype(np.float32)
+    b = rng.uniform(-1.5, 1.5, inp.beta.shape)
+    b[rng.random(b.shape) < 0.1] = 0.0
+    inp.beta = b.astype(np.float32)
+    check(kkt, inp, "f32", f"signed decays chunk={chunk}", chunk=chunk)
+
+
 # ---------------------------------------------------------------- 128-token chunks
 @pytest.mark.parametrize("name", GATED)
 def test_gate_cumsum128_full_parity(kkt, name):

@@ -15,6 +15,7 @@ import pytest
 
 import oracle
 from chunked_gated_delta_token_amd import workloads as W
+from tests import _edge
 from tests._compare import compare, fused_bound
 from tests._gpu_util import TORCH_DT, from_device, load_kkt, say, to_device
 
@@ -141,6 +142,20 @@ def test_large_gate_spread(kkt):
         g[:, t0:t0 + 64] = np.cumsum(inc[:, t0:t0 + 64], axis=1)
     inp.g = g.astype(np.float32)
     check(kkt, inp, "f32", "gate spread ~ -96")
+
+
+@pytest.mark.parametrize("out_dtype", ["f32", "f16"])
+@pytest.mark.parametrize("T,H", [(300, 3), (2400, 8)])
+@pytest.mark.parametrize("kind", _edge.KINDS)
+def test_edge_inputs(kkt, kind, T, H, out_dtype):
+    """Signed and zero beta, rising or wandering gates, zero key rows and a
+    zero chunk, on a two-wave grid (15 tiles) and a one-wave grid (304).  fp32 and f16
+    output: the one-bf16-ulp rule is the one stated for decaying gates; with
+    gates that rise, an element that nearly cancels in a chunk with |X| ~ 13
+    measured 1.3e-7 off (fp32 arithmetic, fast exp), past that rule's
+    2^-23 floor, and f16 output carries the fp32 error bound."""
+    inp = _edge.edge_inputs(kind, T, H, seed=490 + T % 7)
+    check(kkt, inp, out_dtype, f"{kind} T={T} H={H}")
 
 
 @pytest.mark.parametrize("T,H", [(38481, 8), (40000, 7)])

@@ -16,6 +16,7 @@ import pytest
 
 import oracle
 from chunked_gated_delta_token_amd import workloads as W
+from tests import _edge
 from tests._compare import a_scale, compare, compare_A, structural_masks, tril_bound
 from tests._gpu_util import TORCH_DT, from_device, load_kkt, say, to_device
 
@@ -258,3 +259,13 @@ def test_hand_worked_golden_split(kkt):
             exp = np.zeros(64)
             exp[:len(row)] = row
             assert np.all(np.abs(got[0, i, 0] - exp) <= 1e-6 * np.maximum(np.abs(exp), 1.0)), (c["name"], i)
+
+
+@pytest.mark.parametrize("kind", _edge.KINDS)
+def test_edge_inputs_unfused_chain(kkt, kind):
+    """The edge inputs through the two unfused steps: A against the oracle,
+    the solve of the oracle's A, and the chain bit-equal to the fused op."""
+    inp = _edge.edge_inputs(kind, 2400, 8, seed=690)
+    check_scaled_dot(kkt, inp, kind)
+    check_solve_tril(kkt, inp, "f32", kind)
+    check_chain_equals_fused(kkt, inp, "f32", kind)
