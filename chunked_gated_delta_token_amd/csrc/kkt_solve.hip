@@ -68,7 +68,7 @@
 
 #include "kkt_solve.h"
 
-#define KKT_VERSION_NUMBER 901  // 0.9.1
+#define KKT_VERSION_NUMBER 902  // 0.9.2
 
 namespace {
 
@@ -711,6 +711,7 @@ __device__ __forceinline__ void chunk_rows(const KernelArgs& args, WaveLds& lds,
         mask_key_tail<K, kInBytes>(frag, 0, q, args.k_head_bytes);
         // ---- a4: Gram blocks.  Block (i, j): lane (q, n=m) holds rows 16i + 4q + r, column 16j + n.
         f32x4 S[4][4];
+        bool epilogue_done = false;  // a5 already applied, block row by block row
         if constexpr (IN == Elt::F32) {
             // fp32 keys: k-outer, each pair of fragments split once for all
             // ten blocks (the split parts of one pair are all that is live)
@@ -738,10 +739,38 @@ __device__ __forceinline__ void chunk_rows(const KernelArgs& args, WaveLds& lds,
                 for (int s = 0; s < kSteps; ++s) acc = gram_step<IN>(frag[i][s], frag[j][s], acc);
                 return acc;
             };
+            if constexpr (!SHARE && SPLIT == 0) {
+                // With a factored gate or none, each block row is scaled
+                // right after its Gram blocks (the same operations as a5
+                // below, bit for bit), so rows 0..2 are done while row 3's
+                // keys may still be arriving.  Same box, us:
+                // (2,16384,32,128) 75.1 -> 73.2, its gate-sum form 77.7 ->
+                // 75.0, kkt_scaled_dot 97.9 -> 97.0; (1,8192,8,128) 7.0-7.1
+                // -> 7.0.  Not in the two-wave tiles of small grids (32
+                // tiles 4.39 -> 4.73) nor with the shared key image, whose
+                // write and barrier come first.
+                if (!has_g || factored) {
+                    constexpr float kOff0 = (MODE == Mode::ScaledDot) ? 1.0f : -1.0f;
+                    float cc[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+                    for (int j = 0; j < 4; ++j) cc[j] = has_g ? lds.col_scale[16 * j + m] : 1.0f;
 #pragma unroll
-                for (int j = 0; j <= i; ++j) S[i][j] = gram(i, j);
+                    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+                        for (int j = 0; j <= i; ++j) S[i][j] = gram(i, j);
+                        const f32x4 rr = *reinterpret_cast<const f32x4*>(&lds.row_scale[16 * i + 4 * q]);
+#pragma unroll
+                        for (int j = 0; j <= i; ++j) A[i][j] = (rr * S[i][j]) * (j < i ? kOff0 * cc[j] : cc[j]);
+                    }
+                    epilogue_done = true;
+                }
+            }
+            if (!epilogue_done) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+#pragma unroll
+                    for (int j = 0; j <= i; ++j) S[i][j] = gram(i, j);
+                }
             }
         }
         if constexpr (SHARE) {
@@ -761,7 +790,9 @@ __device__ __forceinline__ void chunk_rows(const KernelArgs& args, WaveLds& lds,
         // negated factor negates the rounded product exactly; A itself, for
         // kkt_scaled_dot, keeps its sign)
         constexpr float kOff = (MODE == Mode::ScaledDot) ? 1.0f : -1.0f;
-        if (!has_g) {
+        if (epilogue_done) {
+            // (16-bit keys without the shared image: done with the Gram)
+        } else if (!has_g) {
             // A = beta_i S (rows >= L have beta 0 and zero keys)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {

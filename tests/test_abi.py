@@ -48,7 +48,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version(lib):
-    assert lib.kkt_version() == 901
+    assert lib.kkt_version() == 902
 
 
 def _call(lib, **over):
