@@ -579,6 +579,7 @@ __device__ __forceinline__ void chunk_rows(const KernelArgs& args, WaveLds& lds,
     float g_sum = 0.0f;
     (void)g_sum;
 
+    bool diag_in_lds = false;  // the diagonal blocks already written to blk
     // The 10 lower 16x16 blocks of A, result layout: A[i][j] lane (q, n)
     // holds A_ij[4q .. 4q+3][n] (rows 16i + 4q + r, column 16j + n).  The
     // diagonal blocks still hold their upper part here; it is masked below.
@@ -761,8 +762,17 @@ __device__ __forceinline__ void chunk_rows(const KernelArgs& args, WaveLds& lds,
                         const f32x4 rr = *reinterpret_cast<const f32x4*>(&lds.row_scale[16 * i + 4 * q]);
 #pragma unroll
                         for (int j = 0; j <= i; ++j) A[i][j] = (rr * S[i][j]) * (j < i ? kOff0 * cc[j] : cc[j]);
+                        if constexpr (MODE == Mode::Fused) {
+                            // the diagonal block to LDS for the solve, as below
+                            // (4096 tiles 19.83 -> 19.63 us)
+                            f32x4 v;
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) v[r] = (4 * q + r > m) ? -A[i][i][r] : 0.0f;
+                            *reinterpret_cast<f32x4*>(&blk[i][m][4 * q]) = v;
+                        }
                     }
                     epilogue_done = true;
+                    diag_in_lds = (MODE == Mode::Fused);
                 }
             }
             if (!epilogue_done) {
@@ -935,7 +945,7 @@ __device__ __forceinline__ void chunk_rows(const KernelArgs& args, WaveLds& lds,
     // column as one contiguous row
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        if (!owns(i)) continue;
+        if (!owns(i) || diag_in_lds) continue;
         f32x4 v;
 #pragma unroll
         for (int r = 0; r < 4; ++r) v[r] = (4 * q + r > m) ? -A[i][i][r] : 0.0f;
