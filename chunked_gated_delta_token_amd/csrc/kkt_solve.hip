@@ -1117,6 +1117,18 @@ __device__ __forceinline__ void chunk_rows(const KernelArgs& args, WaveLds& lds,
         return;
     }
 
+    if constexpr (OUT == Elt::F32 && CH == 64) {
+        // fp32 lines that need only the diagonal inverses (below): issued
+        // before the six W products, whose MFMAs then run while these
+        // stores drain (the LDS barriers of a staged store bound the
+        // compiler's scheduling).  Same box, us: (1,8192,8,128) 6.93-7.03
+        // -> 6.84-6.93, its gate-sum form 7.29-7.38 -> 7.17-7.21, 512 tiles
+        // 5.65-5.69 -> 5.60-5.62; 2048 and 4096 tiles about 1% slower,
+        // 16384 tiles unchanged.
+        store_row_line(0, 0, xd[0], zero4);
+        store_zero_lines(0);
+        store_row_line(2, 1, xd[2], zero4);
+    }
     const f32x4 wt10 = mm16(A[1][0], xa[1], zero4);
     const f32x4 wt20 = mm16(A[2][0], xa[2], zero4);
     const f32x4 wt21 = mm16(A[2][1], xa[2], zero4);
@@ -1154,9 +1166,8 @@ __device__ __forceinline__ void chunk_rows(const KernelArgs& args, WaveLds& lds,
             // cost 0.1-0.2 us).  In the two-wave tiles of small grids the
             // same line stores took longer: 32 tiles 4.38 -> 4.70 us, 250
             // tiles with fp32 output 4.85 -> 5.07 us.
-            store_row_line(0, 0, xd[0], zero4);
-            store_zero_lines(0);
-            store_row_line(2, 1, xd[2], zero4);
+            // (block row 0 and the right half of block row 2 went out
+            // before the W products, above)
             x10 = mm16(wt10, xd[0], zero4);
             x21 = mm16(wt21, xd[1], zero4);
             x32 = mm16(wt32, xd[2], zero4);
