@@ -37,6 +37,9 @@ def build(verbose: bool = False, extra_flags=(), out: str = None, src: str = Non
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
            # MFMA results in ordinary VGPRs: no accumulator-register copies
            "-mllvm", "-amdgpu-mfma-vgpr-form=1",
+           # the leading scalar kernel arguments arrive in SGPRs at wave launch
+           # (9 arguments, 14 dwords: the most the user SGPRs hold here)
+           "-mllvm", "-amdgpu-kernarg-preload-count=9",
            "-Wall", "-I", INCLUDE, "-o", lib + ".tmp", src or SRC, *extra_flags]
     if verbose:
         print(" ".join(cmd), flush=True)

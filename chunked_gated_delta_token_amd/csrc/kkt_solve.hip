@@ -68,7 +68,7 @@
 
 #include "kkt_solve.h"
 
-#define KKT_VERSION_NUMBER 902  // 0.9.2
+#define KKT_VERSION_NUMBER 903  // 0.9.3
 
 namespace {
 
@@ -328,7 +328,6 @@ struct KernelArgs {
     int64_t T;                  // tokens per batch row (total packed tokens for varlen)
     int32_t num_seqs;
     int32_t H;
-    int32_t chunks_per_row;
     int32_t n_tiles;            // tiles in the grid (an upper bound for varlen)
     uint32_t n_groups;          // workgroups in the grid
     uint32_t k_row_bytes;       // bytes between consecutive tokens of one head in k
@@ -345,7 +344,69 @@ struct KernelArgs {
     FastDiv div_chunks;         // division by chunks_per_row (chunk -> batch row, chunk in row)
     int32_t gate_gather;        // gate-sum kernel: the four tiles of a workgroup (four heads of one
                                 // chunk) write their summed gates together (run_tile)
+    int32_t packed;             // cu_seqlens != nullptr, preloaded: the tile map tests this flag,
+                                // not the pointer, so fixed-length rows never wait for the pointer
 };
+
+// Kernel arguments, preloaded.  Every tile needs the fields below before it
+// can issue its first load (workgroup order, tile map, the key, g, beta and
+// output addresses) or during its compute (the gate-sum output).  Passed as
+// the leading 9 scalar kernel arguments (14 dwords), they are preloaded into
+// SGPRs when the wave launches (the library is built with
+// -amdgpu-kernarg-preload-count=9); read from the kernel argument segment,
+// they would cost a tile one scalar-load round trip, about 0.5 us at the
+// start of a launch, before its loads or in the middle of its compute (the
+// next LDS wait waits for it too).  The other fields (packed sequences,
+// options) come from the KernelArgs copy behind them.
+// The five addresses are below 2^48 (setup() checks it; buffer resources
+// hold 48-bit bases); their top 16 bits carry the small fields:
+//   k:    xcd_order (bits 0-1), log2_group_run (2-6), tile_waves (7-9,
+//         1 or 4), div_H.shift (10-14), packed (15);
+//   g:    div_chunks.magic, low half;  beta: its high half;
+//   out:  div_chunks.shift (0-4), log2 of the output bytes of one head's
+//         row minus 7 (5-6), k_head_bytes / 16 (7-13), gate_gather (14).
+// n_groups, remap_groups, k_row_bytes and o_row_bytes follow from the
+// others (launch() checks the n_groups they give).
+#define KKT_KERNEL_PARAMS                                                                                      \
+    uint64_t pre_k, uint64_t pre_g, uint64_t pre_beta, uint64_t pre_out, uint64_t pre_g_out, uint32_t pre_n_tiles, \
+        uint32_t pre_H, uint32_t pre_div_H, uint32_t pre_T, const KernelArgs args_in
+#define KKT_KERNEL_ARGS                                                                                        \
+    const KernelArgs args = with_preloaded(args_in, pre_k, pre_g, pre_beta, pre_out, pre_g_out, pre_n_tiles,  \
+                                           pre_H, pre_div_H, pre_T)
+
+constexpr uint64_t kAddrMask = (1ull << 48) - 1;
+
+__device__ __forceinline__ KernelArgs with_preloaded(KernelArgs a, uint64_t k, uint64_t g, uint64_t beta,
+                                                     uint64_t out, uint64_t g_out, uint32_t n_tiles, uint32_t H,
+                                                     uint32_t div_H, uint32_t T)
+{
+    const uint32_t fk = (uint32_t)(k >> 48), fg = (uint32_t)(g >> 48), fb = (uint32_t)(beta >> 48),
+                   fo = (uint32_t)(out >> 48);
+    a.k = reinterpret_cast<const void*>(k & kAddrMask);
+    a.g = reinterpret_cast<const float*>(g & kAddrMask);
+    a.beta = reinterpret_cast<const float*>(beta & kAddrMask);
+    a.out = reinterpret_cast<void*>(out & kAddrMask);
+    a.g_out = reinterpret_cast<float*>(g_out & kAddrMask);
+    a.xcd_order = (int32_t)(fk & 3u);
+    a.log2_group_run = (int32_t)((fk >> 2) & 31u);
+    a.tile_waves = (int32_t)((fk >> 7) & 7u);
+    a.div_H = FastDiv{div_H, (fk >> 10) & 31u};
+    a.packed = (int32_t)((fk >> 15) & 1u);
+    a.div_chunks = FastDiv{fg | (fb << 16), fo & 31u};
+    a.o_row_bytes = H << (7u + ((fo >> 5) & 3u));
+    a.k_head_bytes = ((fo >> 7) & 127u) * 16u;
+    a.gate_gather = (int32_t)((fo >> 14) & 1u);
+    a.n_tiles = (int32_t)n_tiles;
+    a.H = (int32_t)H;
+    a.T = (int64_t)T;
+    a.k_row_bytes = H * a.k_head_bytes;
+    // tile_waves is 1 or 4 (the shift by tile_waves / 2 divides by it)
+    const uint32_t tw = (uint32_t)a.tile_waves;
+    a.n_groups = (n_tiles + tw - 1u) >> (tw >> 1);
+    const uint32_t lg = (uint32_t)a.log2_group_run;
+    a.remap_groups = (a.n_groups >> (lg + 3u)) << (lg + 3u);
+    return a;
+}
 
 // ---------------------------------------------------------------- tile map (a1)
 struct Tile {
@@ -431,20 +492,11 @@ __device__ Tile varlen_tile(const int32_t* __restrict__ cu, int32_t num_seqs, in
 }
 
 // Workgroup order (see XcdOrder); both remaps are permutations of
-// [0, n_groups).  Computed without branches from kernel arguments only, so the
-// argument loads are issued together.
+// [0, n_groups).  Computed without branches from preloaded kernel arguments
+// only (KKT_KERNEL_PARAMS), so no memory round trip comes before the tile's
+// first loads.
 __device__ __forceinline__ uint32_t workgroup_order(const KernelArgs& args)
 {
-    // (the empty statements make every argument the tile's path reads live
-    // here, so that all of them are loaded with the ones the order needs, in
-    // one round trip: a kernel-argument load issued later waits behind the
-    // whole chip's memory traffic, up to microseconds, right before the key
-    // loads it gates)
-    asm volatile("" ::"s"(args.k), "s"(args.out), "s"(args.g), "s"(args.beta), "s"(args.cu_seqlens));
-    asm volatile("" ::"s"(args.T), "s"(args.num_seqs), "s"(args.H), "s"(args.chunks_per_row), "s"(args.n_tiles),
-                 "s"(args.k_row_bytes), "s"(args.o_row_bytes), "s"(args.tile_waves),
-                 "s"(args.k_head_bytes), "s"(args.div_H.magic), "s"(args.div_H.shift), "s"(args.div_chunks.magic),
-                 "s"(args.div_chunks.shift));
     const uint32_t n_groups = args.n_groups;
     const uint32_t hw = blockIdx.x;
     const uint32_t xcd = hw % 8, slot = hw / 8;
@@ -464,9 +516,10 @@ template <int CH>
 __device__ __forceinline__ Tile chunk_tile(const KernelArgs& args, uint32_t chunk, int lane)
 {
     Tile tile;
-    if (args.cu_seqlens == nullptr) {
+    if (!args.packed) {
+        const uint32_t chunks_per_row = (uint32_t)((args.T + (CH - 1)) / CH);
         const uint32_t b = fast_div(chunk, args.div_chunks);
-        const uint32_t c = chunk - b * (uint32_t)args.chunks_per_row;
+        const uint32_t c = chunk - b * chunks_per_row;
         const int64_t t0 = (int64_t)c * CH;
         tile.row0 = (int64_t)b * args.T + t0;
         tile.len = (int)((args.T - t0) < CH ? (args.T - t0) : CH);
@@ -568,11 +621,6 @@ __device__ __forceinline__ void chunk_rows(const KernelArgs& args, WaveLds& lds,
     // first row and first output column of this wave's 64 rows
     const uint32_t row_base = (CH == 128) ? 64u * (uint32_t)half : 0u;
     const uint32_t col_base = row_base;
-
-    // Buffer resources spanning exactly rows 0 .. L-1 of the chunk.
-    const __amdgpu_buffer_rsrc_t o_rsrc = make_rsrc(
-        static_cast<char*>(args.out) + tok * (int64_t)(CH * kOutBytes),
-        (uint32_t)(L - 1) * args.o_row_bytes + CH * kOutBytes);
 
     // split tile, GATE_SUM: the summed gate of row `lane`, written to g_out by
     // the first wave once the second has read the decays (g_out may be g)
@@ -842,6 +890,13 @@ __device__ __forceinline__ void chunk_rows(const KernelArgs& args, WaveLds& lds,
             }
         }
     }  // A from k, g, beta
+    // The output's buffer resource, spanning exactly rows 0 .. L-1 of the
+    // chunk.  Formed here, after the loads: out and o_row_bytes are not
+    // preloaded, and their scalar load must not hold up the tile's loads.
+    const __amdgpu_buffer_rsrc_t o_rsrc = make_rsrc(
+        static_cast<char*>(args.out) + tok * (int64_t)(CH * kOutBytes),
+        (uint32_t)(L - 1) * args.o_row_bytes + CH * kOutBytes);
+
     // ---- a8 helper: stage one 16-row block row and write full output rows
     // (rows >= L fall outside o_rsrc and are dropped)
     const f32x4 zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -1516,8 +1571,9 @@ __device__ __forceinline__ WaveLds* tile_lds()
 // One kernel per entry point, so that profiles name the operation.
 template <Elt IN, Elt OUT, int K>
 __global__ __launch_bounds__(kWave * kWavesPerGroup)
-void kkt_solve_kernel(const KernelArgs args)
+void kkt_solve_kernel(KKT_KERNEL_PARAMS)
 {
+    KKT_KERNEL_ARGS;
     WaveLds* lds_all = tile_lds();
     run_tile<Mode::Fused, IN, OUT, K>(args, lds_all);
 }
@@ -1525,32 +1581,36 @@ void kkt_solve_kernel(const KernelArgs args)
 // The fused op with each 64-token tile split over a two-wave workgroup.
 template <Elt IN, Elt OUT, int K>
 __global__ __launch_bounds__(kWave * 2)
-void kkt_solve_split_kernel(const KernelArgs args)
+void kkt_solve_split_kernel(KKT_KERNEL_PARAMS)
 {
+    KKT_KERNEL_ARGS;
     __shared__ SplitLds lds;
     run_split_tile<Mode::Fused, IN, OUT, K>(args, lds);
 }
 
 template <Elt IN, Elt OUT, int K>
 __global__ __launch_bounds__(kWave * kWavesPerGroup)
-void kkt_solve_gate_cumsum_kernel(const KernelArgs args)
+void kkt_solve_gate_cumsum_kernel(KKT_KERNEL_PARAMS)
 {
+    KKT_KERNEL_ARGS;
     WaveLds* lds_all = tile_lds();
     run_tile<Mode::Fused, IN, OUT, K, true>(args, lds_all);
 }
 
 template <Elt IN, Elt OUT, int K>
 __global__ __launch_bounds__(kWave * 2)
-void kkt_solve_gate_cumsum_split_kernel(const KernelArgs args)
+void kkt_solve_gate_cumsum_split_kernel(KKT_KERNEL_PARAMS)
 {
+    KKT_KERNEL_ARGS;
     __shared__ SplitLds lds;
     run_split_tile<Mode::Fused, IN, OUT, K, true>(args, lds);
 }
 
 template <Elt IN, int K>
 __global__ __launch_bounds__(kWave * kWavesPerGroup)
-void kkt_scaled_dot_kernel(const KernelArgs args)
+void kkt_scaled_dot_kernel(KKT_KERNEL_PARAMS)
 {
+    KKT_KERNEL_ARGS;
     WaveLds* lds_all = tile_lds();
     run_tile<Mode::ScaledDot, IN, Elt::F32, K>(args, lds_all);
 }
@@ -1558,16 +1618,18 @@ void kkt_scaled_dot_kernel(const KernelArgs args)
 // (the input-type and K arguments of run_tile are unused in this mode)
 template <Elt OUT>
 __global__ __launch_bounds__(kWave * kWavesPerGroup)
-void kkt_solve_tril_kernel(const KernelArgs args)
+void kkt_solve_tril_kernel(KKT_KERNEL_PARAMS)
 {
+    KKT_KERNEL_ARGS;
     WaveLds* lds_all = tile_lds();
     run_tile<Mode::SolveTril, Elt::F32, OUT, 64>(args, lds_all);
 }
 
 template <Elt OUT>
 __global__ __launch_bounds__(kWave * 2)
-void kkt_solve_tril_split_kernel(const KernelArgs args)
+void kkt_solve_tril_split_kernel(KKT_KERNEL_PARAMS)
 {
+    KKT_KERNEL_ARGS;
     __shared__ SplitLds lds;
     run_split_tile<Mode::SolveTril, Elt::F32, OUT, 64>(args, lds);
 }
@@ -1599,8 +1661,9 @@ __global__ __launch_bounds__(kWave * kWavesPerGroup)
 // (shared 16-bit keys: at most 128 VGPRs, so that registers, like the 39 KB
 // of LDS, leave room for four workgroups per CU; split fp32 keys need more)
 __attribute__((amdgpu_waves_per_eu(STAGE == kKeysShared && IN != Elt::F32 ? 4 : 1)))
-void kkt_solve128_kernel(const KernelArgs args)
+void kkt_solve128_kernel(KKT_KERNEL_PARAMS)
 {
+    KKT_KERNEL_ARGS;
     constexpr int kOutBytes = EltInfo<OUT>::bytes;
     __shared__ Chunk128Lds ex;
     const int lane = threadIdx.x % kWave;
@@ -1823,11 +1886,42 @@ int64_t k_bucket(int64_t K) { return K <= 64 ? 64 : (K <= 128 ? 128 : 256); }
 
 // waves: the workgroup size in waves; the one-wave-per-tile kernels take
 // a.tile_waves (their default), the others name theirs
-hipError_t launch(void (*kernel)(KernelArgs), const KernelArgs& a, hipStream_t stream, int waves = 0)
+using KernelFn = void (*)(uint64_t, uint64_t, uint64_t, uint64_t, uint64_t, uint32_t, uint32_t, uint32_t, uint32_t,
+                          KernelArgs);
+
+// The log2 of a power of two v >= 1.
+uint32_t log2_exact(uint32_t v)
+{
+    uint32_t l = 0;
+    while ((1u << l) < v) ++l;
+    return l;
+}
+
+// An address with a field in its top 16 bits (KKT_KERNEL_PARAMS).
+uint64_t with_field(const void* p, uint32_t field)
+{
+    return reinterpret_cast<uint64_t>(p) | ((uint64_t)(field & 0xffffu) << 48);
+}
+
+hipError_t launch(KernelFn kernel, const KernelArgs& a, hipStream_t stream, int waves = 0)
 {
     // (the one-wave-per-tile kernels take one WaveLds per wave as dynamic LDS)
     const size_t lds_bytes = (waves > 0) ? 0 : (size_t)a.tile_waves * sizeof(WaveLds);
-    hipLaunchKernelGGL(kernel, dim3(a.n_groups), dim3(kWave * (waves > 0 ? waves : a.tile_waves)), lds_bytes, stream, a);
+    // the preloaded fields (see KKT_KERNEL_PARAMS); setup() checks that they fit
+    const uint32_t tw = (uint32_t)a.tile_waves;
+    const uint32_t o_head_bytes = a.o_row_bytes / (uint32_t)a.H;
+    if ((tw != 1 && tw != 4) || a.n_groups != (((uint32_t)a.n_tiles + tw - 1u) >> (tw >> 1)) ||
+        a.k_head_bytes % 16u != 0 || a.k_head_bytes / 16u > 127u || o_head_bytes < 128u || o_head_bytes > 512u) {
+        return hipErrorInvalidConfiguration;  // not reached: setup() makes them so
+    }
+    const uint32_t fk = (uint32_t)a.xcd_order | ((uint32_t)a.log2_group_run << 2) | (tw << 7) |
+                        (a.div_H.shift << 10) | ((uint32_t)a.packed << 15);
+    const uint32_t fo = a.div_chunks.shift | ((log2_exact(o_head_bytes) - 7u) << 5) | ((a.k_head_bytes / 16u) << 7) |
+                        ((uint32_t)a.gate_gather << 14);
+    hipLaunchKernelGGL(kernel, dim3(a.n_groups), dim3(kWave * (waves > 0 ? waves : a.tile_waves)), lds_bytes, stream,
+                       with_field(a.k, fk), with_field(a.g, a.div_chunks.magic & 0xffffu),
+                       with_field(a.beta, a.div_chunks.magic >> 16), with_field(a.out, fo), with_field(a.g_out, 0),
+                       (uint32_t)a.n_tiles, (uint32_t)a.H, a.div_H.magic, (uint32_t)a.T, a);
     return hipGetLastError();
 }
 
@@ -1990,6 +2084,9 @@ FastDiv make_fastdiv(uint32_t d)
 // and out_row_bytes are the strides between consecutive tokens of one head;
 // chunk is 64 (one tile per wave) or 128 (one tile per workgroup).
 // Returns KKT_OK with a filled in; makes no HIP call unless the arguments pass.
+// Device addresses travel with fields in their top 16 bits (KKT_KERNEL_PARAMS).
+bool below_2_48(const void* p) { return (reinterpret_cast<uint64_t>(p) >> 48) == 0; }
+
 kkt_status_t setup(KernelArgs& a, const void* in, const float* g, const float* beta,
                    const int32_t* cu_seqlens, int64_t num_seqs, int64_t B, int64_t T, int64_t H,
                    int64_t in_row_bytes, int64_t out_row_bytes, void* out, hipStream_t stream,
@@ -2020,6 +2117,18 @@ kkt_status_t setup(KernelArgs& a, const void* in, const float* g, const float* b
     if (n_tiles >= (1LL << 31) - kWavesPerGroup || num_seqs >= (1LL << 31) - 1) {
         return fail(KKT_ERR_UNSUPPORTED, "problem too large for one launch");
     }
+    // T and the bytes of one head's row travel in 32-bit and narrower fields
+    // of the preloaded kernel arguments (KKT_KERNEL_PARAMS): a key row of up to
+    // 1 KiB, an output row of 128, 256 or 512 bytes
+    const int64_t o_head_bytes = out_row_bytes / H;
+    if (in_row_bytes % H != 0 || in_row_bytes / H >= 2048 || out_row_bytes % H != 0 ||
+        (o_head_bytes != 128 && o_head_bytes != 256 && o_head_bytes != 512)) {
+        return fail(KKT_ERR_UNSUPPORTED, "row sizes outside the kernels' range");
+    }
+    if (T > (int64_t)UINT32_MAX) return fail(KKT_ERR_UNSUPPORTED, "T must be below 2^32 tokens");
+    if (!below_2_48(in) || !below_2_48(g) || !below_2_48(beta) || !below_2_48(out)) {
+        return fail(KKT_ERR_UNSUPPORTED, "device addresses must lie below 2^48");
+    }
 
     kkt_status_t st = check_device();
     if (st != KKT_OK) return st;
@@ -2036,7 +2145,7 @@ kkt_status_t setup(KernelArgs& a, const void* in, const float* g, const float* b
     a.T = T;
     a.num_seqs = (int32_t)num_seqs;
     a.H = (int32_t)H;
-    a.chunks_per_row = (int32_t)chunks_per_row;
+    a.div_chunks = make_fastdiv((uint32_t)(chunks_per_row > 0 ? chunks_per_row : 1));
     a.n_tiles = (int32_t)n_tiles;
     a.k_row_bytes = (uint32_t)in_row_bytes;
     a.o_row_bytes = (uint32_t)out_row_bytes;
@@ -2051,11 +2160,11 @@ kkt_status_t setup(KernelArgs& a, const void* in, const float* g, const float* b
     a.remap_groups = (uint32_t)((groups >> (lg + 3)) << (lg + 3));
     a.g_out = nullptr;
     a.gate_gather = 0;
+    a.packed = (cu_seqlens != nullptr) ? 1 : 0;
     a.split_tiles = split ? 1 : 0;
     a.tile_waves = (int32_t)tiles_per_group;
     a.k_head_bytes = (uint32_t)(in_row_bytes / H);
     a.div_H = make_fastdiv((uint32_t)H);
-    a.div_chunks = make_fastdiv((uint32_t)(chunks_per_row > 0 ? chunks_per_row : 1));
     return KKT_OK;
 }
 
@@ -2127,6 +2236,7 @@ extern "C" kkt_status_t kkt_solve_gate_cumsum(const void* k, const float* g_deca
     if (T == 0) return KKT_OK;
     if (g_decay == nullptr) return fail(KKT_ERR_INVALID_ARGUMENT, "g_decay must not be NULL");
     if ((reinterpret_cast<uintptr_t>(g_out) & 3u) != 0) return fail(KKT_ERR_INVALID_ARGUMENT, "g_out must be 4-byte aligned");
+    if (!below_2_48(g_out)) return fail(KKT_ERR_UNSUPPORTED, "device addresses must lie below 2^48");
     KernelArgs a;
     st = setup(a, k, g_decay, beta, cu_seqlens, num_seqs, B, T, H, H * K * dtype_bytes(in_dtype),
                H * chunk_size * dtype_bytes(out_dtype), out, stream, chunk_size, true, kWave1GroupTiles);

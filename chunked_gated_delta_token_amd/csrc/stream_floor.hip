@@ -73,9 +73,30 @@ __device__ __forceinline__ uint32_t tile_group(const FloorArgs& a)
 }
 
 // KRB: key row bytes (128, 256 or 512); ORB: output row bytes (128 or 256).
+// The arguments are scalars, preloaded into SGPRs at wave launch (the
+// library is built with -amdgpu-kernarg-preload-count=9), as the fused
+// kernels' are: no kernel-argument load precedes a tile's first loads.
+// p_bits: contiguous (bit 0), log2_run (bits 1-5); n_groups and
+// remap_groups follow from the others.
 template <int KRB, int ORB, int WAVES>
-__global__ __launch_bounds__(kWave * WAVES) void stream_floor_kernel(const FloorArgs a)
+__global__ __launch_bounds__(kWave * WAVES) void stream_floor_kernel(const char* p_k, const float* p_g,
+                                                                     const float* p_beta, char* p_out, uint32_t p_H,
+                                                                     uint32_t p_cpr, uint32_t p_n_tiles, uint32_t p_T,
+                                                                     uint32_t p_bits)
 {
+    FloorArgs a;
+    a.k = p_k;
+    a.g = p_g;
+    a.beta = p_beta;
+    a.out = p_out;
+    a.H = (int32_t)p_H;
+    a.chunks_per_row = (int32_t)p_cpr;
+    a.n_tiles = p_n_tiles;
+    a.T = (int64_t)p_T;
+    a.n_groups = (p_n_tiles + WAVES - 1) / WAVES;
+    a.contiguous = (int32_t)(p_bits & 1u);
+    a.log2_run = (int32_t)((p_bits >> 1) & 31u);
+    a.remap_groups = (a.n_groups >> (a.log2_run + 3)) << (a.log2_run + 3);
     constexpr int kPieces = KRB / 16;                   // 16-byte pieces of a key row
     constexpr int kPasses = kPieces > 16 ? kPieces / 16 : 1;
     constexpr int kOutPieces = ORB / 16;
@@ -149,7 +170,8 @@ hipError_t launch(FloorArgs a, hipStream_t stream)
     a.log2_run = lg;
     a.remap_groups = (a.n_groups >> (lg + 3)) << (lg + 3);
     hipLaunchKernelGGL((stream_floor_kernel<KRB, ORB, kWavesPerGroup>), dim3(a.n_groups), dim3(kWave * kWavesPerGroup),
-                       0, stream, a);
+                       0, stream, a.k, a.g, a.beta, a.out, (uint32_t)a.H, (uint32_t)a.chunks_per_row, a.n_tiles,
+                       (uint32_t)a.T, (uint32_t)a.contiguous | ((uint32_t)a.log2_run << 1));
     return hipGetLastError();
 }
 

@@ -74,7 +74,8 @@ typedef enum {
  *              offsets are copied to the host (synchronously) and checked
  *              first.
  *   num_seqs   number of sequences; ignored when cu_seqlens is NULL.
- *   B, T, H, K sizes.  T may be 0 (nothing is launched).
+ *   B, T, H, K sizes.  T may be 0 (nothing is launched) and is below 2^32
+ *              (KKT_ERR_UNSUPPORTED otherwise).
  *              K is at most 256 and each key row a whole number of 16-byte
  *              pieces: a multiple of 4 for fp32 keys, of 8 for bf16 / f16
  *              keys.  The PR #135 page shows K = 128 only; the rest is this
@@ -96,7 +97,9 @@ typedef enum {
  *              is the device checked to be gfx950.
  *
  * Alignment: k and out 16-byte aligned; g, beta and cu_seqlens 4-byte aligned
- * (KKT_ERR_INVALID_ARGUMENT otherwise).
+ * (KKT_ERR_INVALID_ARGUMENT otherwise).  Every device address lies below 2^48,
+ * as GPU virtual addresses do on ROCm (KKT_ERR_UNSUPPORTED otherwise): the
+ * kernels receive addresses in 48 bits.
  *
  * Launch form (chunk_size 64): grids of up to 256 chunk-head tiles run each
  * tile on two waves, larger grids one tile per wave; both give bit-identical

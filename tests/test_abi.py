@@ -48,7 +48,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version(lib):
-    assert lib.kkt_version() == 902
+    assert lib.kkt_version() == 903
 
 
 def _call(lib, **over):
@@ -85,6 +85,12 @@ def _call(lib, **over):
     (dict(g=16 + 2), 1, "4-byte aligned"),
     (dict(beta=16 + 1), 1, "4-byte aligned"),
     (dict(cu=16 + 2, num_seqs=1), 1, "4-byte aligned"),
+    # T and the addresses travel in the kernels' preloaded 32-bit and 48-bit fields
+    (dict(T=2 ** 32), 2, "below 2^32"),
+    (dict(k=1 << 48), 2, "below 2^48"),
+    (dict(out=(1 << 63) + 16), 2, "below 2^48"),
+    (dict(g=1 << 48), 2, "below 2^48"),
+    (dict(beta=(1 << 52) + 4), 2, "below 2^48"),
 ])
 def test_invalid_arguments_rejected_on_host(lib, over, status, msg):
     from chunked_gated_delta_token_amd import kkt
@@ -205,6 +211,8 @@ def _call_gate_cumsum(lib, **over):
     (dict(out=16 + 4), 1, "16-byte aligned"),
     (dict(g=32 + 2), 1, "4-byte aligned"),
     (dict(g_out=64 + 1), 1, "4-byte aligned"),
+    (dict(g_out=1 << 48), 2, "below 2^48"),
+    (dict(g=(1 << 49) + 4), 2, "below 2^48"),
 ])
 def test_gate_cumsum_invalid_arguments(lib, over, status, msg):
     from chunked_gated_delta_token_amd import kkt
@@ -229,6 +237,8 @@ def _call_solve_tril(lib, **over):
     (dict(out=None), 1, "NULL"),
     (dict(A=16 + 8), 1, "16-byte aligned"),
     (dict(cu=16 + 1, num_seqs=1), 1, "4-byte aligned"),
+    (dict(T=2 ** 32 + 64), 2, "below 2^32"),
+    (dict(out=1 << 48), 2, "below 2^48"),
 ])
 def test_solve_tril_invalid_arguments(lib, over, status, msg):
     from chunked_gated_delta_token_amd import kkt

@@ -179,7 +179,7 @@ threads = [threading.Thread(target=worker, args=(i,)) for i in range(8)]
 [t.start() for t in threads]
 [t.join() for t in threads]
 assert not errors, errors[:3]
-assert lib.kkt_version() == 902
+assert lib.kkt_version() == 903
 print("abi exercise ok")
 '''
 
