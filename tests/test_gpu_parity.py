@@ -175,6 +175,23 @@ def test_many_heads(kkt):
     check(kkt, inp, "bf16", "many heads H=96")
 
 
+@pytest.mark.parametrize("B,T,H,K,in_dtype,out_dtype", [
+    (1, 1100, 1024, 16, "bf16", "bf16"),
+    (1, 70, 4099, 8, "f16", "f32"),
+    (1, 4000, 12, 256, "f32", "f32"),
+])
+def test_launch_fields_at_their_limits(kkt, B, T, H, K, in_dtype, out_dtype):
+    """The launch fields the kernels receive packed into their first
+    arguments, near the ends of their ranges: H = 1024 (18 chunks of 256
+    four-wave workgroups, runs of 256 in the chunk-grouped order, whole
+    rounds and a remainder, a 12-row last chunk); H = 4099 (odd: workgroups
+    straddle chunks and the last one holds two tiles; a large magic number
+    for the division by H; 16-byte key rows); 1 KB fp32 key rows (K = 256),
+    the widest key row, on 756 one-wave tiles."""
+    inp = W.generate("T256_H8_bf16_f32", B=B, T=T, H=H, K=K, in_dtype=in_dtype, seed=475 + H)
+    check(kkt, inp, out_dtype, f"launch fields B={B} T={T} H={H} K={K}")
+
+
 # ---------------------------------------------------------------- varlen
 def _lengths(seed, n, lo, hi, empty_every=0):
     rng = np.random.default_rng(seed)
