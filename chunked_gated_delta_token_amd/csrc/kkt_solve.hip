@@ -1172,6 +1172,21 @@ __device__ __forceinline__ void chunk_rows(const KernelArgs& args, WaveLds& lds,
         return;
     }
 
+    if constexpr (GATE_SUM && CH == 64) {
+        // The summed gate, one 4-byte word per lane into 64 cache lines that
+        // the tiles of the other heads write too, when each wave writes its
+        // own words: issued with the first output lines, before the W
+        // products, so that it drains during the merge.  Issued right after
+        // the scan, while the key tile was still arriving, these stores cost
+        // 0.9 us of 8.5 on (1,8192,8,128); after the last rows, bf16 output,
+        // 7.22 vs 7.13 us here (same box).
+        if (args.g != nullptr && args.g_out != nullptr && !args.gate_gather) {
+            const uint32_t span = (uint32_t)(L - 1) * (uint32_t)H * 4u + 4u;
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, g_sum),
+                                                  make_rsrc(args.g_out + tok, span),
+                                                  (uint32_t)lane * (uint32_t)H * 4u, 0, 0);
+        }
+    }
     if constexpr (OUT == Elt::F32 && CH == 64) {
         // fp32 lines that need only the diagonal inverses (below): issued
         // before the six W products, whose MFMAs then run while these
@@ -1260,23 +1275,11 @@ __device__ __forceinline__ void chunk_rows(const KernelArgs& args, WaveLds& lds,
         }
 
         if constexpr (GATE_SUM && CH == 64) {
-            // The summed gate goes last.  Each of these stores writes one
-            // 4-byte word per lane into 64 cache lines that the tiles of the
-            // other heads write too.  Issued right after the scan, while the
-            // key tile was still arriving, they cost 0.9 us of 8.5 on
-            // (1,8192,8,128); here nothing measurable.
-            if (args.g != nullptr && args.g_out != nullptr) {
-                if (args.gate_gather) {
-                    // to the workgroup's store (run_tile); row_scale is no
-                    // longer read
-                    wave_lds_sync();
-                    lds.row_scale[lane] = g_sum;
-                } else {
-                    const uint32_t span = (uint32_t)(L - 1) * (uint32_t)H * 4u + 4u;
-                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, g_sum),
-                                                          make_rsrc(args.g_out + tok, span),
-                                                          (uint32_t)lane * (uint32_t)H * 4u, 0, 0);
-                }
+            // The workgroup's gathered store of the summed gate (run_tile)
+            // takes this wave's sums from row_scale, no longer read here.
+            if (args.g != nullptr && args.g_out != nullptr && args.gate_gather) {
+                wave_lds_sync();
+                lds.row_scale[lane] = g_sum;
             }
         }
 
