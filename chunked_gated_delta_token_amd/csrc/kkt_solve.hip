@@ -891,8 +891,7 @@ __device__ __forceinline__ void chunk_rows(const KernelArgs& args, WaveLds& lds,
         }
     }  // A from k, g, beta
     // The output's buffer resource, spanning exactly rows 0 .. L-1 of the
-    // chunk.  Formed here, after the loads: out and o_row_bytes are not
-    // preloaded, and their scalar load must not hold up the tile's loads.
+    // chunk (first needed by the stores below).
     const __amdgpu_buffer_rsrc_t o_rsrc = make_rsrc(
         static_cast<char*>(args.out) + tok * (int64_t)(CH * kOutBytes),
         (uint32_t)(L - 1) * args.o_row_bytes + CH * kOutBytes);
