@@ -58,7 +58,7 @@ ENTRY = {"fused": "kkt_solve", "scaled_dot": "kkt_scaled_dot", "solve_tril": "kk
          "gate_cumsum128": "kkt_solve_gate_cumsum128", "floor": "stream_floor"}
 
 
-SPLIT_MAX_TILES = 256          # the library's bound for two-wave tiles of the fused op (KKT_SPLIT_TILES overrides it)
+SPLIT_MAX_TILES = 256          # the library's own bound for two-wave tiles (KKT_SPLIT_TILES >= 0 overrides it)
 
 
 def kernel_name(key: str, workload: str) -> str:
@@ -66,7 +66,9 @@ def kernel_name(key: str, workload: str) -> str:
     chunks (with or without the gate sum) and the solve of a given A take
     their two-wave-per-tile form on grids of up to SPLIT_MAX_TILES
     chunk-head tiles (the library's grid counts T/64 + num_seqs chunks for
-    packed sequences)."""
+    packed sequences), except the fused op with 16-bit keys and output,
+    which the library keeps at one wave per tile unless KKT_SPLIT_TILES
+    sets a bound."""
     from chunked_gated_delta_token_amd import workloads as W
     split_names = {"fused": "kkt_solve_split_kernel", "gate_cumsum": "kkt_solve_gate_cumsum_split_kernel",
                    "solve_tril": "kkt_solve_tril_split_kernel"}
@@ -74,7 +76,11 @@ def kernel_name(key: str, workload: str) -> str:
         w = W.WORKLOADS[workload]
         grid = w.H * ((w.T // 64 + w.n_seqs) if w.n_seqs else w.B * (-(-w.T // 64)))
         env = os.environ.get("KKT_SPLIT_TILES", "")
-        if grid <= (int(env) if env else SPLIT_MAX_TILES):
+        bound = int(env) if env else -1
+        if bound < 0:
+            sixteen_bit = w.in_dtype != "f32" and w.out_dtype != "f32"
+            bound = 0 if (key == "fused" and sixteen_bit) else SPLIT_MAX_TILES
+        if grid <= bound:
             return split_names[key]
     return KERNELS[key]
 

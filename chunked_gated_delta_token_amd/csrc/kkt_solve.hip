@@ -68,7 +68,7 @@
 
 #include "kkt_solve.h"
 
-#define KKT_VERSION_NUMBER 903  // 0.9.3
+#define KKT_VERSION_NUMBER 904  // 0.9.4
 
 namespace {
 
@@ -2042,6 +2042,7 @@ constexpr int64_t kGateGatherMinGroups = 1024;
 // cost as much as the shorter tail saves or more (1024 tiles: 13-25% more
 // time).  KKT_SPLIT_TILES overrides the bound (0: never split).
 constexpr int64_t kSplitMaxTiles = 256;
+constexpr int64_t kSplitAuto = -1;  // KKT_OPTION_SPLIT_MAX_TILES: the library chooses (split_max_tiles)
 
 // Grids that run one tile per wave use workgroups of one wave up to a bound
 // (the hardware spreads them over every CU; four-wave workgroups put a small
@@ -2069,9 +2070,19 @@ int64_t env_int(const char* name, int64_t fallback)
     const char* v = getenv(name);
     return (v != nullptr && v[0] != '\0') ? strtoll(v, nullptr, 10) : fallback;
 }
-std::atomic<int64_t> g_split_max_tiles{env_int("KKT_SPLIT_TILES", kSplitMaxTiles)};
+std::atomic<int64_t> g_split_max_tiles{env_int("KKT_SPLIT_TILES", kSplitAuto)};
 std::atomic<int64_t> g_validate_cu_seqlens{env_int("KKT_VALIDATE", 0) == 1 ? 1 : 0};
-int64_t split_max_tiles() { return g_split_max_tiles.load(std::memory_order_relaxed); }
+// The two-wave bound of a call: the option's value, or, by default
+// (kSplitAuto), kSplitMaxTiles, except for the fused op with 16-bit keys and
+// 16-bit output (one_wave_faster), whose one-wave tiles are faster on every
+// grid measured (32-256 tiles: 0.08-0.19 us; with an fp32 output or fp32
+// keys the two-wave tiles stay 0.12-0.25 us faster, and so do the gate-sum
+// op and the solve of a given A).
+int64_t split_max_tiles(bool one_wave_faster)
+{
+    const int64_t v = g_split_max_tiles.load(std::memory_order_relaxed);
+    return (v >= 0) ? v : (one_wave_faster ? 0 : kSplitMaxTiles);
+}
 
 FastDiv make_fastdiv(uint32_t d)
 {
@@ -2092,7 +2103,7 @@ bool below_2_48(const void* p) { return (reinterpret_cast<uint64_t>(p) >> 48) ==
 kkt_status_t setup(KernelArgs& a, const void* in, const float* g, const float* beta,
                    const int32_t* cu_seqlens, int64_t num_seqs, int64_t B, int64_t T, int64_t H,
                    int64_t in_row_bytes, int64_t out_row_bytes, void* out, hipStream_t stream,
-                   int64_t chunk = kChunk, bool allow_split = false, int64_t wave1_group_tiles = 0)
+                   int64_t chunk = kChunk, int64_t split_bound = 0, int64_t wave1_group_tiles = 0)
 {
     if (in == nullptr || out == nullptr) return fail(KKT_ERR_INVALID_ARGUMENT, "input and output must not be NULL");
     // the kernel moves the row tensors in 16-byte vectors, g / beta / cu_seqlens in 4-byte words
@@ -2111,7 +2122,7 @@ kkt_status_t setup(KernelArgs& a, const void* in, const float* g, const float* b
     // Packed sequences: at most floor(T/chunk) + num_seqs chunks; surplus tiles exit.
     const int64_t n_chunks = (cu_seqlens == nullptr) ? B * chunks_per_row : T / chunk + num_seqs;
     const int64_t n_tiles = n_chunks * H;
-    const bool split = allow_split && chunk == kChunk && n_tiles <= split_max_tiles();
+    const bool split = chunk == kChunk && n_tiles <= split_bound;  // two-wave tiles
     // one wave per tile: a workgroup of one wave on grids of up to
     // wave1_group_tiles tiles (spread over every CU), else of four
     const int64_t tiles_per_group =
@@ -2207,7 +2218,8 @@ extern "C" kkt_status_t kkt_solve(const void* k, const float* g, const float* be
     if (T == 0) return KKT_OK;
     KernelArgs a;
     st = setup(a, k, g, beta, cu_seqlens, num_seqs, B, T, H, H * K * dtype_bytes(in_dtype),
-               H * chunk_size * dtype_bytes(out_dtype), out, stream, chunk_size, true, kWave1GroupTilesFused);
+               H * chunk_size * dtype_bytes(out_dtype), out, stream, chunk_size,
+               split_max_tiles(in_dtype != KKT_DTYPE_F32 && out_dtype != KKT_DTYPE_F32), kWave1GroupTilesFused);
     if (st != KKT_OK) return st;
 
     hipError_t e;
@@ -2241,7 +2253,8 @@ extern "C" kkt_status_t kkt_solve_gate_cumsum(const void* k, const float* g_deca
     if (!below_2_48(g_out)) return fail(KKT_ERR_UNSUPPORTED, "device addresses must lie below 2^48");
     KernelArgs a;
     st = setup(a, k, g_decay, beta, cu_seqlens, num_seqs, B, T, H, H * K * dtype_bytes(in_dtype),
-               H * chunk_size * dtype_bytes(out_dtype), out, stream, chunk_size, true, kWave1GroupTiles);
+               H * chunk_size * dtype_bytes(out_dtype), out, stream, chunk_size, split_max_tiles(false),
+               kWave1GroupTiles);
     if (st != KKT_OK) return st;
     a.g_out = g_out;
     // four heads' summed gates per 16-byte store (run_tile): only where every
@@ -2276,7 +2289,7 @@ extern "C" kkt_status_t kkt_scaled_dot(const void* k, const float* g, const floa
     if (T == 0) return KKT_OK;
     KernelArgs a;
     st = setup(a, k, g, beta, cu_seqlens, num_seqs, B, T, H, H * K * dtype_bytes(in_dtype), H * kChunk * 4, A, stream,
-               kChunk, false, kWave1GroupTiles);
+               kChunk, 0, kWave1GroupTiles);
     if (st != KKT_OK) return st;
 
     hipError_t e;
@@ -2304,7 +2317,8 @@ extern "C" kkt_status_t kkt_solve_tril(const float* A, const int32_t* cu_seqlens
     if (T == 0) return KKT_OK;
     KernelArgs a;
     kkt_status_t st = setup(a, A, nullptr, nullptr, cu_seqlens, num_seqs, B, T, H, H * kChunk * 4,
-                            H * kChunk * dtype_bytes(out_dtype), out, stream, kChunk, true, kWave1GroupTiles);
+                            H * kChunk * dtype_bytes(out_dtype), out, stream, kChunk, split_max_tiles(false),
+                            kWave1GroupTiles);
     if (st != KKT_OK) return st;
 
     hipError_t e;
@@ -2331,7 +2345,9 @@ extern "C" kkt_status_t kkt_set_option(kkt_option_t option_arg, int64_t value)
     g_last_error.clear();
     switch (enum_code(option_arg)) {
     case KKT_OPTION_SPLIT_MAX_TILES:
-        if (value < 0) return fail(KKT_ERR_INVALID_ARGUMENT, "KKT_OPTION_SPLIT_MAX_TILES must be >= 0");
+        if (value < kSplitAuto) {
+            return fail(KKT_ERR_INVALID_ARGUMENT, "KKT_OPTION_SPLIT_MAX_TILES must be >= 0, or -1 (automatic)");
+        }
         g_split_max_tiles.store(value, std::memory_order_relaxed);
         return KKT_OK;
     case KKT_OPTION_VALIDATE_CU_SEQLENS:

@@ -103,8 +103,11 @@ typedef enum {
  *
  * Launch form (chunk_size 64): grids of up to 256 chunk-head tiles run each
  * tile on two waves, larger grids one tile per wave; both give bit-identical
- * results.  The option KKT_OPTION_SPLIT_MAX_TILES replaces the 256 (0: always
- * one wave per tile).
+ * results.  With 16-bit keys and a 16-bit output every grid takes one wave
+ * per tile (on small grids it is the faster form for those types; the
+ * gate-sum op and the solve of a given A keep the 256 whatever the types).
+ * The option KKT_OPTION_SPLIT_MAX_TILES sets one bound for every call
+ * instead (0: always one wave per tile).
  *
  * All pointers are owned by the caller; the library allocates nothing and
  * keeps no pointer after the call returns.  The call is asynchronous: it
@@ -203,8 +206,10 @@ kkt_status_t kkt_solve_tril(const float* A, const int32_t* cu_seqlens, int64_t n
  *
  *   KKT_OPTION_SPLIT_MAX_TILES      grids of up to this many 64-token
  *                                   chunk-head tiles run each tile on two
- *                                   waves (the launch form above); 0: never.
- *                                   Default 256 (env KKT_SPLIT_TILES).
+ *                                   waves (the launch form above); 0: never;
+ *                                   -1 (the default; env KKT_SPLIT_TILES):
+ *                                   the library's choice, 256 except for
+ *                                   kkt_solve with 16-bit keys and output.
  *   KKT_OPTION_VALIDATE_CU_SEQLENS  nonzero: every call with cu_seqlens first
  *                                   copies the offsets to the host
  *                                   (synchronously, on the call's stream) and
@@ -213,7 +218,7 @@ kkt_status_t kkt_solve_tril(const float* A, const int32_t* cu_seqlens, int64_t n
  *                                   at T.  Default 0 (env KKT_VALIDATE=1: on).
  *
  * kkt_set_option returns KKT_ERR_INVALID_ARGUMENT for an unknown option or a
- * negative KKT_OPTION_SPLIT_MAX_TILES; kkt_get_option returns the current
+ * KKT_OPTION_SPLIT_MAX_TILES below -1; kkt_get_option returns the current
  * value, or -1 for an unknown option.
  */
 typedef enum {

@@ -48,7 +48,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version(lib):
-    assert lib.kkt_version() == 903
+    assert lib.kkt_version() == 904
 
 
 def _call(lib, **over):
@@ -115,19 +115,22 @@ def test_k_check_takes_rows_of_whole_16_byte_pieces(lib, in_dtype):
 
 
 def test_options_round_trip_and_reject_bad_values(lib):
-    """kkt_set_option / kkt_get_option: values round-trip, an unknown option
-    or a negative two-wave bound is rejected and leaves the option as it was;
-    the Python context manager restores the previous value."""
+    """kkt_set_option / kkt_get_option: values round-trip (-1: the library's
+    own choice, the default), an unknown option or a two-wave bound below -1
+    is rejected and leaves the option as it was; the Python context manager
+    restores the previous value."""
     from chunked_gated_delta_token_amd import kkt
     split0 = kkt.get_option(kkt.KKT_OPTION_SPLIT_MAX_TILES)
     val0 = kkt.get_option(kkt.KKT_OPTION_VALIDATE_CU_SEQLENS)
-    assert split0 == int(os.environ.get("KKT_SPLIT_TILES") or 256)
+    assert split0 == int(os.environ.get("KKT_SPLIT_TILES") or -1)
     try:
         kkt.set_option(kkt.KKT_OPTION_SPLIT_MAX_TILES, 7)
         assert kkt.get_option(kkt.KKT_OPTION_SPLIT_MAX_TILES) == 7
         with pytest.raises(kkt.KKTInvalidArgument):
-            kkt.set_option(kkt.KKT_OPTION_SPLIT_MAX_TILES, -1)
+            kkt.set_option(kkt.KKT_OPTION_SPLIT_MAX_TILES, -2)
         assert kkt.get_option(kkt.KKT_OPTION_SPLIT_MAX_TILES) == 7
+        with kkt.option(kkt.KKT_OPTION_SPLIT_MAX_TILES, -1):
+            assert kkt.get_option(kkt.KKT_OPTION_SPLIT_MAX_TILES) == -1
         with kkt.option(kkt.KKT_OPTION_SPLIT_MAX_TILES, 0):
             assert kkt.get_option(kkt.KKT_OPTION_SPLIT_MAX_TILES) == 0
         assert kkt.get_option(kkt.KKT_OPTION_SPLIT_MAX_TILES) == 7
@@ -151,7 +154,7 @@ def test_options_start_from_the_environment(tmp_path):
     assert out.stdout.split() == ["33", "1"]
     env = {k: v for k, v in os.environ.items() if k not in ("KKT_SPLIT_TILES", "KKT_VALIDATE")}
     out = subprocess.run(["python3", "-c", code, LIB], capture_output=True, text=True, env=env, check=True)
-    assert out.stdout.split() == ["256", "0"]
+    assert out.stdout.split() == ["-1", "0"]
 
 
 def _call_scaled_dot(lib, **over):

@@ -91,11 +91,12 @@ def test_gpus_above_one_exit_with_a_message(monkeypatch, capsys):
 
 
 def test_kernel_name_follows_the_launch_form(monkeypatch):
-    """Small fused grids name the two-wave kernel, the rest one wave per tile;
-    KKT_SPLIT_TILES moves the bound as it does in the library."""
+    """Small fused grids name the two-wave kernel, the rest one wave per tile,
+    and so do the 16-bit-key, 16-bit-output fused grids; KKT_SPLIT_TILES
+    sets one bound for all, as it does in the library (-1: its own choice)."""
     monkeypatch.delenv("KKT_SPLIT_TILES", raising=False)
     assert bench.kernel_name("fused", "T256_H8_bf16_f32") == "kkt_solve_split_kernel"      # 32 tiles
-    assert bench.kernel_name("fused", "T2000_H8_bf16_bf16") == "kkt_solve_split_kernel"    # 256 tiles
+    assert bench.kernel_name("fused", "T2000_H8_bf16_bf16") == "kkt_solve_kernel"          # 256 tiles, 16-bit
     assert bench.kernel_name("fused", "T8192_H8_bf16_f32") == "kkt_solve_kernel"           # 1024 tiles
     assert bench.kernel_name("fused", "varlen12_T16384_H7_f32_f32") == "kkt_solve_kernel"  # 7 * (256 + 12)
     assert bench.kernel_name("fused128", "T256_H8_bf16_f32") == "kkt_solve128_kernel"
@@ -103,9 +104,15 @@ def test_kernel_name_follows_the_launch_form(monkeypatch):
     assert bench.kernel_name("gate_cumsum", "T8192_H8_bf16_f32") == "kkt_solve_gate_cumsum_kernel"
     assert bench.kernel_name("gate_cumsum128", "T256_H8_bf16_f32") == "kkt_solve128_kernel"
     assert bench.kernel_name("solve_tril", "T2000_H8_bf16_bf16") == "kkt_solve_tril_split_kernel"
+    assert bench.kernel_name("gate_cumsum", "T2000_H8_bf16_bf16") == "kkt_solve_gate_cumsum_split_kernel"
     assert bench.kernel_name("solve_tril", "T8192_H8_bf16_f32") == "kkt_solve_tril_kernel"
     assert bench.kernel_name("scaled_dot", "T256_H8_bf16_f32") == "kkt_scaled_dot_kernel"
     monkeypatch.setenv("KKT_SPLIT_TILES", "0")
     assert bench.kernel_name("fused", "T256_H8_bf16_f32") == "kkt_solve_kernel"
+    monkeypatch.setenv("KKT_SPLIT_TILES", "256")
+    assert bench.kernel_name("fused", "T2000_H8_bf16_bf16") == "kkt_solve_split_kernel"
+    monkeypatch.setenv("KKT_SPLIT_TILES", "-1")
+    assert bench.kernel_name("fused", "T2000_H8_bf16_bf16") == "kkt_solve_kernel"
+    assert bench.kernel_name("fused", "T256_H8_bf16_f32") == "kkt_solve_split_kernel"
     monkeypatch.setenv("KKT_SPLIT_TILES", "1024")
     assert bench.kernel_name("fused", "T8192_H8_bf16_f32") == "kkt_solve_split_kernel"

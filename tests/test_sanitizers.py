@@ -161,9 +161,9 @@ for K in list(range(8, 257, 8)) + [4, 12, 36, 100, 252]:
         assert sdot(K=K, di=di, T=0) == 0, lib.kkt_last_error()
 assert tril(T=0) == 0
 assert solve(T=0, k=None, out=None) == 0
-for v in (0, 1, 7, 1 << 40):
+for v in (0, 1, 7, 1 << 40, -1):
     assert lib.kkt_set_option(0, v) == 0 and lib.kkt_get_option(0) == v
-assert lib.kkt_set_option(0, -1) == 1 and lib.kkt_set_option(7, 0) == 1 and lib.kkt_get_option(7) == -1
+assert lib.kkt_set_option(0, -2) == 1 and lib.kkt_set_option(7, 0) == 1 and lib.kkt_get_option(7) == -1
 assert lib.kkt_set_option(1, 3) == 0 and lib.kkt_get_option(1) == 1
 
 errors = []
@@ -179,7 +179,7 @@ threads = [threading.Thread(target=worker, args=(i,)) for i in range(8)]
 [t.start() for t in threads]
 [t.join() for t in threads]
 assert not errors, errors[:3]
-assert lib.kkt_version() == 903
+assert lib.kkt_version() == 904
 print("abi exercise ok")
 '''
 
