@@ -4,7 +4,8 @@
  * of kkt_solve moves on sequences of whole 64-token chunks (the key rows, g
  * and beta in; the output rows out), in the fused kernel's access pattern
  * (one chunk of one head per wave, all of a wave's loads before its stores,
- * non-temporal whole-row stores), with no arithmetic.  Its time bounds from
+ * non-temporal whole-row stores, launch arguments preloaded into SGPRs),
+ * with no arithmetic.  Its time bounds from
  * below what a kernel with this data movement takes on the machine; the
  * benchmark reports it beside the fused op (bench.py --op floor).
  *
@@ -27,7 +28,7 @@ extern "C" {
  *   out:  [B, T, H] rows of out_row_bytes bytes, contiguous, device memory
  * Output: 16-byte piece c of output row (b, t, h) holds piece
  * c mod (key_row_bytes / 16) of key row (b, t, h).
- * Sizes: B, H >= 1; T a positive multiple of 64; key_row_bytes 128, 256 or
+ * Sizes: B, H >= 1; T a positive multiple of 64 below 2^31; key_row_bytes 128, 256 or
  * 512; out_row_bytes 128 or 256; 64 * H * key_row_bytes and
  * 64 * H * out_row_bytes below 2^31; B * (T / 64) * H below 2^31.
  * Returns 0 when the kernel was launched, 1 for invalid arguments (nothing
