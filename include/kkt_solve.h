@@ -219,7 +219,8 @@ kkt_status_t kkt_solve_tril(const float* A, const int32_t* cu_seqlens, int64_t n
  *
  * kkt_set_option returns KKT_ERR_INVALID_ARGUMENT for an unknown option or a
  * KKT_OPTION_SPLIT_MAX_TILES below -1; kkt_get_option returns the current
- * value, or -1 for an unknown option.
+ * value, or -1 for an unknown option (for KKT_OPTION_SPLIT_MAX_TILES, -1 is
+ * also the value that leaves the choice to the library).
  */
 typedef enum {
     KKT_OPTION_SPLIT_MAX_TILES = 0,
